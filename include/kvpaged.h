@@ -1,0 +1,241 @@
+/*
+ * kvpaged.h - C ABI of the paged-KV attention library for MI355X (gfx950).
+ *
+ * What it implements (pages cited by title and section):
+ *   - The KV cache of each sequence lives in fixed-size blocks of token
+ *     slots; blocks are taken as the sequence grows; a block table maps
+ *     logical blocks to physical ones; the attention kernel reads K/V
+ *     through that table; freed blocks are reused ["PagedAttention Nedir?"
+ *     (bitcanli.com), section "PagedAttention Nasıl Çalışır?", steps 1-5].
+ *   - A free block is taken from the pool when the current block is full;
+ *     empty slots exist only in a sequence's last block; parallel samples
+ *     share blocks by reference with copy-on-write ["Makale Bülteni —
+ *     PagedAttention ve vLLM", section "İddia ve Gerçeklik"].
+ *   - The contiguous variant keeps one contiguous K/V buffer per sequence,
+ *     reserved for the maximum context, so the kernel sees a plain tensor
+ *     ["Makale Bülteni — vAttention", section "İddia ve Gerçeklik"].
+ *
+ * Conventions:
+ *   - Every function returns a kv_status (or a documented value); no
+ *     exception or abort crosses the ABI. On an error return, host state
+ *     (pool, tables, lengths) is unchanged and kv_last_error() describes it.
+ *   - Host-side functions (kv_pool_*, kv_block_*, kv_seq_append,
+ *     kv_slot_mapping, kv_blocks_needed) touch no GPU.
+ *   - Device ops take device pointers owned by the caller, enqueue work on
+ *     `stream` (a hipStream_t; NULL = the default stream), return after the
+ *     launch, and allocate no device memory. Launch failures return KV_EHIP.
+ *   - Layouts (row-major, element type = `dtype`):
+ *       paged K/V pool        [num_blocks, block_size, Hkv, D]
+ *       contiguous K/V        [num_seqs, seq_stride, Hkv, D]
+ *       new K/V rows          [num_tokens, Hkv, D]
+ *       decode q / out        [num_seqs, Hq, D]
+ *       prefill q / out       [total_q, Hq, D]   (sequence s owns rows
+ *                                                 cu_q_lens[s]..cu_q_lens[s+1])
+ *       block table           int32 [num_seqs, bt_stride]
+ *     A slot numbers the token rows of a cache: slot = block * block_size +
+ *     offset for the paged pool, s * seq_stride + position for the
+ *     contiguous layout.
+ *   - Query head h reads KV head h / (Hq / Hkv). Attention is softmax of
+ *     scale * q.k over the visible keys, accumulated in fp32; out has the
+ *     dtype of q.
+ *   - The allocator is single-threaded: one host thread per pool.
+ */
+#ifndef KVPAGED_H
+#define KVPAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KV_OK = 0,
+  KV_EINVAL = -1,       /* bad argument (null pointer, out-of-range id, shape) */
+  KV_ENOMEM = -2,       /* the pool has too few free blocks                     */
+  KV_EREFCOUNT = -3,    /* free/share/cow of a block whose refcount is 0        */
+  KV_EHIP = -4,         /* a HIP runtime call or kernel launch failed           */
+  KV_EUNSUPPORTED = -5  /* valid, but no kernel covers this shape/dtype         */
+} kv_status;
+
+typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
+
+typedef struct kv_pool kv_pool; /* opaque host-side block metadata */
+
+/* Thread-local description of the last non-OK status on this thread. */
+const char* kv_last_error(void);
+
+/* ---------------------------------------------------------------------
+ * Block arithmetic ["PagedAttention Nasıl Çalışır?", worked example:
+ * 35 tokens in 16-slot blocks take 3 blocks].
+ * Returns ceil(num_tokens / block_size), or -1 if num_tokens < 0 or
+ * block_size <= 0. */
+int64_t kv_blocks_needed(int64_t num_tokens, int32_t block_size);
+
+/* ---------------------------------------------------------------------
+ * Block pool [steps 2 and 5 of "PagedAttention Nasıl Çalışır?";
+ * copy-on-write from "İddia ve Gerçeklik" of the PagedAttention newsletter].
+ * Policy: the free blocks form a FIFO queue, initially init_free_order
+ * (a permutation of 0..num_blocks-1; NULL means ascending). Allocation pops
+ * from the head; a block whose refcount drops to 0 is pushed at the tail,
+ * in argument order. The caller owns the returned pool. */
+kv_status kv_pool_create(int32_t num_blocks, int32_t block_size,
+                         const int32_t* init_free_order, kv_pool** out);
+void kv_pool_destroy(kv_pool* pool); /* NULL is a no-op */
+
+/* Take n blocks (refcount 1) into out_ids[0..n). All or nothing:
+ * KV_ENOMEM if fewer than n are free. */
+kv_status kv_block_alloc(kv_pool* pool, int32_t n, int32_t* out_ids);
+
+/* Drop one reference per listed id (ids may repeat). KV_EINVAL for an id
+ * outside the pool, KV_EREFCOUNT if an id would drop below 0. */
+kv_status kv_block_free(kv_pool* pool, int32_t n, const int32_t* ids);
+
+/* Add one reference per listed id (fork). KV_EREFCOUNT for a free block. */
+kv_status kv_block_share(kv_pool* pool, int32_t n, const int32_t* ids);
+
+/* Copy-on-write check before writing into block `id`. Refcount 1: *out_id
+ * = id, *need_copy = 0. Refcount > 1: a new block (refcount 1) is taken,
+ * id loses one reference, *out_id = new block, *need_copy = 1 (the caller
+ * copies the contents, e.g. with kv_copy_blocks). KV_ENOMEM if no block is
+ * free, KV_EREFCOUNT if id is free. */
+kv_status kv_block_cow(kv_pool* pool, int32_t id, int32_t* out_id,
+                       int32_t* need_copy);
+
+/* Refcount of id, or KV_EINVAL (< 0) for an id outside the pool. */
+int32_t kv_block_refcount(const kv_pool* pool, int32_t id);
+int32_t kv_pool_num_free(const kv_pool* pool);
+int32_t kv_pool_num_blocks(const kv_pool* pool);
+int32_t kv_pool_block_size(const kv_pool* pool);
+
+/* Copy the free queue, head first, into out[0..min(cap, num_free)).
+ * Returns the number of free blocks. */
+int32_t kv_pool_free_list(const kv_pool* pool, int32_t* out, int32_t cap);
+
+/* ---------------------------------------------------------------------
+ * Sequence growth (host; steps 2-3 of "PagedAttention Nasıl Çalışır?").
+ * Sequences s = 0..num_seqs-1, in order, each gain n_new[s] tokens (NULL:
+ * one token each). For the token at position p = seq_lens[s]:
+ *   - if p % block_size == 0, a new block is allocated and written to
+ *     block_tables[s * bt_stride + p / block_size];
+ *   - otherwise, if the block holding p is shared (refcount > 1), it is
+ *     copied on write: the table entry is replaced by the new block and
+ *     the pair (old, new) is appended to out_cow_pairs;
+ *   - its slot, table[p / block_size] * block_size + p % block_size, is
+ *     appended to out_slots (sequence order, then position order).
+ * seq_lens[s] grows by n_new[s]. block_tables and seq_lens are host
+ * arrays, read and written. out_slots needs sum(n_new) entries;
+ * out_cow_pairs holds [cow_capacity, 2] int32; *out_num_cow receives the
+ * number of pairs. All or nothing: KV_ENOMEM when the pool runs dry,
+ * KV_EINVAL when a table row or cow_capacity is too small. */
+kv_status kv_seq_append(kv_pool* pool, int32_t* block_tables,
+                        int32_t bt_stride, int32_t* seq_lens,
+                        const int32_t* n_new, int32_t num_seqs,
+                        int64_t* out_slots, int32_t* out_cow_pairs,
+                        int32_t cow_capacity, int32_t* out_num_cow);
+
+/* Slot of each (seq_ids[i], positions[i]) from a host block table:
+ * block_tables[seq * bt_stride + pos / block_size] * block_size +
+ * pos % block_size; a negative position gives -1 (padding). Host only. */
+kv_status kv_slot_mapping(const int32_t* block_tables, int32_t bt_stride,
+                          const int32_t* seq_ids, const int32_t* positions,
+                          int32_t n, int32_t block_size, int64_t* out_slots);
+
+/* ---------------------------------------------------------------------
+ * Cache write [step 2: a new token's K and V go into its slot].
+ * k, v: new rows [num_tokens, Hkv, D]; slots: device int64 [num_tokens].
+ * Row i is copied to cache row slots[i] of k_cache/v_cache, which hold
+ * num_slots token rows of Hkv*D elements (paged: num_blocks*block_size,
+ * contiguous: num_seqs*seq_stride). Slots < 0 (padding) and slots >=
+ * num_slots are skipped. Bit copy. */
+kv_status kv_reshape_and_cache(const void* k, const void* v,
+                               const int64_t* slots, int32_t num_tokens,
+                               void* k_cache, void* v_cache, int64_t num_slots,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               kv_dtype dtype, void* stream);
+
+/* Copy-on-write data move: for i < n, block src_dst[2i] -> src_dst[2i+1]
+ * of both caches (device int32 pairs). The pairs must be independent: no
+ * destination may be another pair's source or destination (the pairs
+ * kv_seq_append emits always are); they are copied in parallel. Pairs
+ * naming a block outside [0, num_blocks) are skipped. Bit copy. */
+kv_status kv_copy_blocks(void* k_cache, void* v_cache,
+                         const int32_t* src_dst, int32_t n, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, kv_dtype dtype, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Decode attention: one query per sequence against all context_lens[s]
+ * tokens of its context (the query's own K/V is written first)
+ * [step 4 of "PagedAttention Nasıl Çalışır?"; the kernel-side table read
+ * described in "İddia ve Gerçeklik" of the vAttention newsletter].
+ *
+ * Long contexts are split into partitions of kv_decode_partition() tokens
+ * whose partial softmax results are merged exactly; the workspace holds
+ * the partials. kv_decode_workspace_bytes() gives the size needed for the
+ * given shape (0 when no partition can be split); pass at least that.
+ * max_context bounds every context_lens[s] (larger values are clamped to
+ * it, and to bt_stride * block_size for the paged layout). Table entries
+ * outside [0, num_blocks) are clamped into range, which keeps memory
+ * accesses in bounds but makes that output meaningless. context_lens[s]
+ * == 0 gives a zero output row. */
+int32_t kv_decode_partition(int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t max_context);
+size_t kv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_context);
+
+kv_status paged_attn_decode(void* out, const void* q, const void* k_cache,
+                            const void* v_cache, int32_t num_blocks,
+                            const int32_t* block_tables, int32_t bt_stride,
+                            const int32_t* context_lens, int32_t max_context,
+                            int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, float scale, kv_dtype dtype,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Same on the contiguous layout [num_seqs, seq_stride, Hkv, D]. */
+kv_status contig_attn_decode(void* out, const void* q, const void* k,
+                             const void* v, int32_t seq_stride,
+                             const int32_t* context_lens, int32_t max_context,
+                             int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             float scale, kv_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Chunked prefill attention. Sequence s has cu_q_lens[s+1]-cu_q_lens[s]
+ * queries at absolute positions q_start_pos[s] + i and a context of
+ * context_lens[s] tokens already in the cache (including this chunk's
+ * own K/V). With causal != 0 a query at position p sees keys 0..p (and
+ * < context_lens[s]); otherwise all context keys. max_q_len bounds every
+ * sequence's query count. cu_q_lens, q_start_pos and context_lens are
+ * device int32 arrays. [The prefill kernels the vAttention newsletter
+ * compares in "İddia ve Gerçeklik".] */
+kv_status paged_attn_prefill(void* out, const void* q,
+                             const int32_t* cu_q_lens,
+                             const int32_t* q_start_pos, int32_t max_q_len,
+                             const void* k_cache, const void* v_cache,
+                             int32_t num_blocks, const int32_t* block_tables,
+                             int32_t bt_stride, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, float scale, int32_t causal,
+                             kv_dtype dtype, void* stream);
+
+kv_status contig_attn_prefill(void* out, const void* q,
+                              const int32_t* cu_q_lens,
+                              const int32_t* q_start_pos, int32_t max_q_len,
+                              const void* k, const void* v, int32_t seq_stride,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, float scale, int32_t causal,
+                              kv_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPAGED_H */

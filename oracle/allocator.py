@@ -143,7 +143,7 @@ def append_tokens(pool: ModelPool, tables, lens, n_new, table_capacity: int):
         return st, [], []
 
     for s in range(len(lens)):
-        if n_new[s] < 0:
+        if n_new[s] < 0 or lens[s] < 0:
             return fail(EINVAL)
         for _ in range(int(n_new[s])):
             p = lens[s]

@@ -180,13 +180,16 @@ def decode_logical(q: np.ndarray, ks, vs, scale: float) -> np.ndarray:
 
 
 def decode_paged(q, k_pool, v_pool, block_tables, context_lens,
-                 scale: float) -> np.ndarray:
-    """Decode reading K/V through the block table."""
-    ks = [gather_rows(k_pool, block_tables[s], int(context_lens[s]))
-          for s in range(q.shape[0])]
-    vs = [gather_rows(v_pool, block_tables[s], int(context_lens[s]))
-          for s in range(q.shape[0])]
-    return decode_logical(q, ks, vs, scale)
+                 scale: float, seqs=None) -> np.ndarray:
+    """Decode reading K/V through the block table (one sequence at a time;
+    ``seqs`` restricts the work to some sequences, the rest are NaN)."""
+    out = np.full(q.shape, np.nan, dtype=np.float64)
+    for s in (range(q.shape[0]) if seqs is None else seqs):
+        K = gather_rows(k_pool, block_tables[s], int(context_lens[s]))
+        V = gather_rows(v_pool, block_tables[s], int(context_lens[s]))
+        out[s] = attend_heads(np.asarray(q[s], dtype=np.float64), K, V,
+                              scale)
+    return out
 
 
 def decode_contig(q, k, v, context_lens, scale: float) -> np.ndarray:
@@ -236,13 +239,27 @@ def prefill_logical(q, cu_q_lens, q_start_pos, ks, vs, scale: float,
 def prefill_paged(q, cu_q_lens, q_start_pos, k_pool, v_pool, block_tables,
                   context_lens, scale: float, causal: bool, rows=None
                   ) -> np.ndarray:
+    """Chunked prefill reading K/V through the block table, one sequence at
+    a time (only sequences owning a requested row are gathered)."""
     S = len(cu_q_lens) - 1
-    ks = [gather_rows(k_pool, block_tables[s], int(context_lens[s]))
-          for s in range(S)]
-    vs = [gather_rows(v_pool, block_tables[s], int(context_lens[s]))
-          for s in range(S)]
-    return prefill_logical(q, cu_q_lens, q_start_pos, ks, vs, scale, causal,
-                           rows)
+    out = np.full(q.shape, np.nan, dtype=np.float64)
+    wanted = None if rows is None else np.asarray(rows)
+    empty = np.zeros((0,) + k_pool.shape[2:])
+    for s in range(S):
+        lo, hi = int(cu_q_lens[s]), int(cu_q_lens[s + 1])
+        if wanted is not None and not ((wanted >= lo) & (wanted < hi)).any():
+            continue
+        K = gather_rows(k_pool, block_tables[s], int(context_lens[s]))
+        V = gather_rows(v_pool, block_tables[s], int(context_lens[s]))
+        ks = [empty] * S
+        vs = [empty] * S
+        ks[s], vs[s] = K, V
+        sub = None if wanted is None else wanted[(wanted >= lo) & (wanted < hi)]
+        part = prefill_logical(q, cu_q_lens, q_start_pos, ks, vs, scale,
+                               causal, rows=sub if sub is not None else
+                               range(lo, hi))
+        out[lo:hi] = part[lo:hi]
+    return out
 
 
 def prefill_contig(q, cu_q_lens, q_start_pos, k, v, context_lens,

@@ -1,0 +1,147 @@
+// Cache writes: the slot-mapped row scatter of new K/V tokens and the
+// whole-block copies of copy-on-write.
+//
+// A new token's K and V rows go into the slot its block table assigns
+// ["PagedAttention Nedir?" (bitcanli.com), "PagedAttention Nasıl Çalışır?",
+// steps 2-3]; a shared block is copied before it is written
+// ["Makale Bülteni — PagedAttention ve vLLM", "İddia ve Gerçeklik"].
+// Both are plain byte moves bounded by HBM bandwidth: each row is moved in
+// 16-byte (or 4/2-byte) units, consecutive lanes on consecutive units.
+
+#include "device_common.h"
+
+namespace {
+
+using namespace kvp;
+
+template <typename U>
+__global__ __launch_bounds__(256) void scatter_rows_kernel(
+    const U* __restrict__ k, const U* __restrict__ v,
+    const int64_t* __restrict__ slots, int32_t num_tokens, U* k_cache,
+    U* v_cache, int64_t num_slots, int32_t units_per_row) {
+  // One work item = one unit of one row of K or V.
+  const int64_t per_tensor = (int64_t)num_tokens * units_per_row;
+  const int64_t total = 2 * per_tensor;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const bool is_v = i >= per_tensor;
+    const int64_t j = is_v ? i - per_tensor : i;
+    const int64_t t = j / units_per_row;
+    const int64_t u = j - t * units_per_row;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const U* src = is_v ? v : k;
+    U* dst = is_v ? v_cache : k_cache;
+    dst[slot * units_per_row + u] = src[t * units_per_row + u];
+  }
+}
+
+// Pairs are independent (no destination is read or written by another
+// pair), so they are copied in parallel: blockIdx.y walks the pairs,
+// blockIdx.x/threads walk the units of one block of K and of V.
+template <typename U>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    U* k_cache, U* v_cache, const int32_t* __restrict__ src_dst, int32_t n,
+    int32_t num_blocks, int64_t units_per_block) {
+  const int64_t total = 2 * units_per_block;
+  for (int32_t p = blockIdx.y; p < n; p += gridDim.y) {
+    const int32_t src = src_dst[2 * p], dst = src_dst[2 * p + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+      const bool is_v = i >= units_per_block;
+      const int64_t u = is_v ? i - units_per_block : i;
+      U* c = is_v ? v_cache : k_cache;
+      c[(int64_t)dst * units_per_block + u] =
+          c[(int64_t)src * units_per_block + u];
+    }
+  }
+}
+
+size_t elem_size(kv_dtype dt) { return dt == KV_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" kv_status kv_reshape_and_cache(const void* k, const void* v,
+                                          const int64_t* slots,
+                                          int32_t num_tokens, void* k_cache,
+                                          void* v_cache, int64_t num_slots,
+                                          int32_t num_kv_heads,
+                                          int32_t head_dim, kv_dtype dtype,
+                                          void* stream) {
+  if (dtype != KV_F32 && dtype != KV_BF16)
+    return kvp_fail(KV_EINVAL, "kv_reshape_and_cache: unknown dtype %d",
+                    (int)dtype);
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_slots < 0)
+    return kvp_fail(KV_EINVAL, "kv_reshape_and_cache: bad shape");
+  if (num_tokens == 0) return KV_OK;
+  if (!k || !v || !slots || !k_cache || !v_cache)
+    return kvp_fail(KV_EINVAL, "kv_reshape_and_cache: NULL pointer");
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_size(dtype);
+  hipStream_t st = (hipStream_t)stream;
+  const int threads = 256;
+  auto grid_for = [&](int64_t items) {
+    int64_t g = (items + threads - 1) / threads;
+    return (int)(g < 65536 ? g : 65536);
+  };
+  if (row_bytes % 16 == 0) {
+    const int32_t upr = (int32_t)(row_bytes / 16);
+    scatter_rows_kernel<u32x4><<<grid_for(2LL * num_tokens * upr), threads, 0, st>>>(
+        (const u32x4*)k, (const u32x4*)v, slots, num_tokens, (u32x4*)k_cache,
+        (u32x4*)v_cache, num_slots, upr);
+  } else if (row_bytes % 4 == 0) {
+    const int32_t upr = (int32_t)(row_bytes / 4);
+    scatter_rows_kernel<uint32_t><<<grid_for(2LL * num_tokens * upr), threads, 0, st>>>(
+        (const uint32_t*)k, (const uint32_t*)v, slots, num_tokens,
+        (uint32_t*)k_cache, (uint32_t*)v_cache, num_slots, upr);
+  } else {
+    const int32_t upr = (int32_t)(row_bytes / 2);
+    scatter_rows_kernel<uint16_t><<<grid_for(2LL * num_tokens * upr), threads, 0, st>>>(
+        (const uint16_t*)k, (const uint16_t*)v, slots, num_tokens,
+        (uint16_t*)k_cache, (uint16_t*)v_cache, num_slots, upr);
+  }
+  KVP_LAUNCH_CHECK("kv_reshape_and_cache");
+  return KV_OK;
+}
+
+namespace {
+template <typename U>
+void launch_copy(void* k_cache, void* v_cache, const int32_t* src_dst,
+                 int32_t n, int32_t num_blocks, int64_t units, hipStream_t st) {
+  const int threads = 256;
+  const int64_t per_pair = (2 * units + threads - 1) / threads;
+  dim3 grid((unsigned)(per_pair < 1024 ? per_pair : 1024),
+            (unsigned)(n < 65535 ? n : 65535));
+  copy_blocks_kernel<U><<<grid, threads, 0, st>>>(
+      (U*)k_cache, (U*)v_cache, src_dst, n, num_blocks, units);
+}
+}  // namespace
+
+extern "C" kv_status kv_copy_blocks(void* k_cache, void* v_cache,
+                                    const int32_t* src_dst, int32_t n,
+                                    int32_t num_blocks, int32_t block_size,
+                                    int32_t num_kv_heads, int32_t head_dim,
+                                    kv_dtype dtype, void* stream) {
+  if (dtype != KV_F32 && dtype != KV_BF16)
+    return kvp_fail(KV_EINVAL, "kv_copy_blocks: unknown dtype %d", (int)dtype);
+  if (n < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0)
+    return kvp_fail(KV_EINVAL, "kv_copy_blocks: bad shape");
+  if (n == 0) return KV_OK;
+  if (!k_cache || !v_cache || !src_dst)
+    return kvp_fail(KV_EINVAL, "kv_copy_blocks: NULL pointer");
+  const int64_t block_bytes =
+      (int64_t)block_size * num_kv_heads * head_dim * elem_size(dtype);
+  hipStream_t st = (hipStream_t)stream;
+  if (block_bytes % 16 == 0)
+    launch_copy<u32x4>(k_cache, v_cache, src_dst, n, num_blocks,
+                       block_bytes / 16, st);
+  else if (block_bytes % 4 == 0)
+    launch_copy<uint32_t>(k_cache, v_cache, src_dst, n, num_blocks,
+                          block_bytes / 4, st);
+  else
+    launch_copy<uint16_t>(k_cache, v_cache, src_dst, n, num_blocks,
+                          block_bytes / 2, st);
+  KVP_LAUNCH_CHECK("kv_copy_blocks");
+  return KV_OK;
+}

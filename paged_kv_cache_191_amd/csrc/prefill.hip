@@ -1,0 +1,468 @@
+// Chunked-prefill attention over a paged or contiguous KV cache.
+//
+// Every query of a chunk attends, causally, to the keys at or before its
+// absolute position, reading K/V through the block table. The vAttention
+// newsletter ("İddia ve Gerçeklik") reports paged FlashAttention-2 and
+// FlashInfer prefill kernels running 37-42% slower than contiguous ones on
+// A100; the paged and contiguous variants here share one kernel body, with
+// only the tile loader's row addressing different.
+//
+// Fast path (bf16, head_dim 128, group % 4 == 0, block_size % 16 == 0):
+//   * A workgroup of 4 waves owns 32 query rows of one sequence and 4 query
+//     heads of one KV head (grouped-query packing: the K/V tile in LDS serves
+//     all four heads). Each wave owns one head.
+//   * Keys advance in tiles of 64. The whole workgroup loads a tile with
+//     16-byte loads (16 lanes per 256-byte token row), gathering rows through
+//     the block table (4 consecutive keys share a block), into a double
+//     buffer in LDS: K row-major, V transposed (V^T) with a column order that
+//     matches the order in which S^T leaves P in registers. The next tile's
+//     global loads are in flight while the current tile is computed.
+//   * Per tile a wave computes S^T = K Q^T (keys x queries) with
+//     v_mfma_f32_32x32x16_bf16, an online softmax in the log2 domain (one
+//     query per lane column), and O^T += V^T P^T with the same MFMA; P stays
+//     in the lanes that computed it.
+//   * Causal and context masks are selects (-inf scores, zero V rows), only
+//     in the tiles that need them.
+// Generic path (other dtypes/shapes): one wave per (query row, head).
+
+#include "device_common.h"
+
+namespace {
+
+using namespace kvp;
+
+constexpr int kD = 128;
+constexpr int kBM = 32;            // query rows per workgroup
+constexpr int kBN = 64;            // keys per tile
+constexpr int kWaves = 4;          // = query heads per workgroup
+constexpr int kKStride = kD + 8;   // LDS row stride of the K tile (elements)
+constexpr int kVStride = kBN + 8;  // LDS row stride of the V^T tile
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const int32_t* cu_q;
+  const int32_t* q_start;
+  int32_t max_q_len;
+  const void* k;
+  const void* v;
+  const int32_t* bt;
+  int32_t bt_stride;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t seq_stride;
+  const int32_t* ctx;
+  int32_t num_seqs;
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;
+  int32_t head_dim;
+  float scale_log2;
+  int32_t causal;
+};
+
+__device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int s,
+                                         bool paged) {
+  int c = a.ctx[s];
+  c = c < 0 ? 0 : c;
+  if (paged) {
+    const int64_t cap = (int64_t)a.bt_stride * a.block_size;
+    if (c > cap) c = (int)cap;
+  } else if (c > a.seq_stride) {
+    c = a.seq_stride;
+  }
+  return c;
+}
+
+// Column of key k (0..63) in the V^T tile: within each 16-key group, bits 2
+// and 3 of the key index swap, so that the 8 keys a lane feeds to one PV
+// MFMA are contiguous.
+__device__ __forceinline__ int vt_col(int k) {
+  const int k16 = k & 15;
+  return (k & ~15) | (((k16 >> 2) & 1) << 3) | ((k16 >> 3) << 2) | (k16 & 3);
+}
+// Row of head-dim index d in the V^T tile: inside each 32-row block, row
+// 8a + 4g + b holds d = 16g + 4a + b, so that the O^T accumulator of a lane
+// covers 16 contiguous d.
+__device__ __forceinline__ int vt_row(int d) {
+  const int dd = d & 31;
+  return (d & ~31) | (((dd >> 2) & 3) << 3) | ((dd >> 4) << 2) | (dd & 3);
+}
+
+__device__ __forceinline__ uint32_t pick16(u32x4 a, u32x4 b, int m) {
+  const uint32_t x = a[m >> 1], y = b[m >> 1];
+  return (m & 1) ? pick_hi(x, y) : pick_lo(x, y);
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(
+    PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 sk[2][kBN * kKStride];
+  __shared__ __attribute__((aligned(16))) bf16 svt[2][kD * kVStride];
+
+  const int s = blockIdx.z;
+  const int qbeg = a.cu_q[s];
+  const int nq = a.cu_q[s + 1] - qbeg;
+  // Heaviest (latest) query blocks first.
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * kBM;
+  if (q0 >= nq) return;
+  const int ctx = clamp_ctx(a, s, PAGED);
+  const int nrows = min(kBM, nq - q0);
+  const int pos_first = a.q_start[s] + q0;
+  const int pos_last = pos_first + nrows - 1;
+  int kv_end = a.causal ? min(ctx, pos_last + 1) : ctx;
+  kv_end = kv_end < 0 ? 0 : kv_end;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;
+  const int h = blockIdx.y * kWaves + w;
+  const int kvh = (blockIdx.y * kWaves) / a.group;
+
+  // Q^T as the B operand of S^T = K Q^T: lane holds query l32,
+  // d = 16 ks + 8 g2 + e.
+  bf16x8 qop[8];
+  {
+    const int qr = qbeg + q0 + min(l32, nrows - 1);
+    const bf16* qp = (const bf16*)a.q + ((int64_t)qr * a.hq + h) * kD + 8 * g2;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(ld16(qp + 16 * ks));
+  }
+  const int my_pos = pos_first + l32;
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;
+
+  // Tile loader: thread tid moves keys 4n..4n+3, d-chunk 8c..8c+7.
+  const int ln = tid >> 4;
+  const int lc = tid & 15;
+  const int64_t row_elems = (int64_t)a.hkv * kD;
+  const bf16* kg = (const bf16*)a.k + (int64_t)kvh * kD + 8 * lc;
+  const bf16* vg = (const bf16*)a.v + (int64_t)kvh * kD + 8 * lc;
+  u32x4 kreg[4], vreg[4];
+
+  auto load_tile = [&](int j) {
+    const int key0 = j * kBN + 4 * ln;
+    if (PAGED) {
+      // Four consecutive keys share a block; past the context, re-read the
+      // last valid group of four (in bounds, masked later).
+      const int kb = min(key0, ((kv_end - 1) >> 2) << 2);
+      int b = a.bt[(int64_t)s * a.bt_stride + kb / a.block_size];
+      b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+      const int64_t row0 = (int64_t)b * a.block_size + kb % a.block_size;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        kreg[jj] = ld16(kg + (row0 + jj) * row_elems);
+        vreg[jj] = ld16(vg + (row0 + jj) * row_elems);
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t row = (int64_t)s * a.seq_stride + min(key0 + jj, kv_end - 1);
+        kreg[jj] = ld16(kg + row * row_elems);
+        vreg[jj] = ld16(vg + row * row_elems);
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf, int j) {
+    const int key0 = j * kBN + 4 * ln;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      st16(&sk[buf][(4 * ln + jj) * kKStride + 8 * lc], kreg[jj]);
+      if (key0 + jj >= kv_end) vreg[jj] = u32x4{0, 0, 0, 0};
+    }
+    const int col = vt_col(4 * ln);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      u32x2 val;
+      val[0] = pick16(vreg[0], vreg[1], m);
+      val[1] = pick16(vreg[2], vreg[3], m);
+      *reinterpret_cast<u32x2*>(&svt[buf][vt_row(8 * lc + m) * kVStride + col]) =
+          val;
+    }
+  };
+
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  if (n_tiles > 0) load_tile(0);
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    store_tile(buf, j);
+    __syncthreads();
+    if (j + 1 < n_tiles) load_tile(j + 1);
+
+    const bf16* K_ = sk[buf];
+    const bf16* VT = svt[buf];
+    // S^T = K Q^T for the two 32-key halves of the tile.
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 ka = as_bf16x8(
+            ld16(&K_[(32 * kb + l32) * kKStride + 16 * ks + 8 * g2]));
+        sacc[kb] = mfma32(ka, qop[ks], sacc[kb]);
+      }
+    }
+    // Scores (log2 domain) with the causal/context mask where needed.
+    const int tile0 = j * kBN;
+    const bool need_mask = (tile0 + kBN > kv_end) ||
+                           (a.causal && tile0 + kBN - 1 > pos_first);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = sacc[kb][r] * a.scale_log2;
+        if (need_mask) {
+          const int key = tile0 + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+          const bool dead = key >= kv_end || (a.causal && key > my_pos);
+          x = dead ? -INFINITY : x;
+        }
+        sacc[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    // A query row whose keys are all masked so far keeps m = -inf; use 0 as
+    // the reference so that exp2 stays finite (its p are all 0).
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(sacc[kb][r] - m_ref);
+        sacc[kb][r] = p;
+        psum += p;
+      }
+    l_part = l_part * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T, 16 keys per MFMA.
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int kb = kk >> 1;
+      const int rb = 8 * (kk & 1);
+      u32x4 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pb[e] = pack_bf16(sacc[kb][rb + 2 * e], sacc[kb][rb + 2 * e + 1]);
+      const bf16x8 pop = as_bf16x8(pb);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 va = as_bf16x8(
+            ld16(&VT[(32 * db + l32) * kVStride + 16 * kk + 8 * g2]));
+        oacc[db] = mfma32(va, pop, oacc[db]);
+      }
+    }
+  }
+
+  l_part += __shfl_xor(l_part, 32);
+  if (l32 < nrows) {
+    const float inv = l_part > 0.f ? 1.f / l_part : 0.f;
+    bf16* op = (bf16*)a.out + ((int64_t)(qbeg + q0 + l32) * a.hq + h) * kD +
+               16 * g2;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      u32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = pack_bf16(oacc[db][2 * e] * inv, oacc[db][2 * e + 1] * inv);
+        hi[e] = pack_bf16(oacc[db][8 + 2 * e] * inv,
+                          oacc[db][8 + 2 * e + 1] * inv);
+      }
+      st16(op + 32 * db, lo);
+      st16(op + 32 * db + 8, hi);
+    }
+  }
+}
+
+// Generic path: one wave per (query head, query row, sequence).
+template <typename T, bool PAGED>
+__global__ __launch_bounds__(kWave) void prefill_generic_kernel(PrefillArgs a) {
+  const int h = blockIdx.x;
+  const int i = blockIdx.y;
+  const int s = blockIdx.z;
+  const int qbeg = a.cu_q[s];
+  const int nq = a.cu_q[s + 1] - qbeg;
+  if (i >= nq) return;
+  const int lane = threadIdx.x;
+  const int D = a.head_dim;
+  const int g = h / a.group;
+  const int ctx = clamp_ctx(a, s, PAGED);
+  const int pos = a.q_start[s] + i;
+  int nvis = a.causal ? min(ctx, pos + 1) : ctx;
+  nvis = nvis < 0 ? 0 : nvis;
+  float qv[4], acc[4];
+  const T* qp = (const T*)a.q + ((int64_t)(qbeg + i) * a.hq + h) * D;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = lane + kWave * k;
+    qv[k] = d < D ? to_f32<T>(qp[d]) : 0.f;
+    acc[k] = 0.f;
+  }
+  const int64_t row_elems = (int64_t)a.hkv * D;
+  float m_run = -INFINITY, l = 0.f;
+  for (int p = 0; p < nvis; ++p) {
+    int64_t row;
+    if (PAGED) {
+      int b = a.bt[(int64_t)s * a.bt_stride + p / a.block_size];
+      b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+      row = (int64_t)b * a.block_size + p % a.block_size;
+    } else {
+      row = (int64_t)s * a.seq_stride + p;
+    }
+    const T* kp = (const T*)a.k + row * row_elems + (int64_t)g * D;
+    const T* vp = (const T*)a.v + row * row_elems + (int64_t)g * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = lane + kWave * k;
+      if (d < D) dot += qv[k] * to_f32<T>(kp[d]);
+    }
+    dot = wave_sum(dot);
+    const float x = dot * a.scale_log2;
+    const float m_new = fmaxf(m_run, x);
+    const float alpha = fast_exp2(m_run - m_new);
+    const float pr = fast_exp2(x - m_new);
+    l = l * alpha + pr;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = lane + kWave * k;
+      const float vv = d < D ? to_f32<T>(vp[d]) : 0.f;
+      acc[k] = acc[k] * alpha + pr * vv;
+    }
+    m_run = m_new;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  T* op = (T*)a.out + ((int64_t)(qbeg + i) * a.hq + h) * D;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = lane + kWave * k;
+    if (d < D) op[d] = from_f32<T>(acc[k] * inv);
+  }
+}
+
+kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
+                      kv_dtype dtype, hipStream_t st) {
+  if (dtype != KV_F32 && dtype != KV_BF16)
+    return kvp_fail(KV_EINVAL, "%s: unknown dtype %d", name, (int)dtype);
+  if (a.num_seqs < 0 || a.hq <= 0 || a.hkv <= 0 || a.hq % a.hkv != 0 ||
+      a.head_dim <= 0 || a.max_q_len < 0)
+    return kvp_fail(KV_EINVAL, "%s: bad shape (S=%d Hq=%d Hkv=%d D=%d)", name,
+                    a.num_seqs, a.hq, a.hkv, a.head_dim);
+  if (paged && (a.block_size <= 0 || a.bt_stride <= 0 || a.num_blocks <= 0))
+    return kvp_fail(KV_EINVAL, "%s: bad paging arguments", name);
+  if (paged && (int64_t)a.num_blocks * a.block_size > INT32_MAX)
+    return kvp_fail(KV_EUNSUPPORTED, "%s: pool of more than 2^31 slots", name);
+  if (!paged && a.seq_stride <= 0)
+    return kvp_fail(KV_EINVAL, "%s: seq_stride must be > 0", name);
+  if (a.num_seqs == 0 || a.max_q_len == 0) return KV_OK;
+  if (!a.out || !a.q || !a.cu_q || !a.q_start || !a.k || !a.v || !a.ctx ||
+      (paged && !a.bt))
+    return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
+  a.group = a.hq / a.hkv;
+  const bool fast = dtype == KV_BF16 && a.head_dim == kD &&
+                    a.group % kWaves == 0 && (!paged || a.block_size % 16 == 0);
+  if (fast) {
+    dim3 grid((a.max_q_len + kBM - 1) / kBM, a.hq / kWaves, a.num_seqs);
+    if (paged)
+      prefill_mfma_kernel<true><<<grid, kWaves * kWave, 0, st>>>(a);
+    else
+      prefill_mfma_kernel<false><<<grid, kWaves * kWave, 0, st>>>(a);
+    KVP_LAUNCH_CHECK(name);
+    return KV_OK;
+  }
+  if (a.head_dim > 4 * kWave)
+    return kvp_fail(KV_EUNSUPPORTED, "%s: head_dim %d > 256", name,
+                    a.head_dim);
+  if (a.max_q_len > 65535)
+    return kvp_fail(KV_EUNSUPPORTED, "%s: generic path takes <= 65535 queries "
+                    "per sequence", name);
+  dim3 grid(a.hq, a.max_q_len, a.num_seqs);
+  if (dtype == KV_F32) {
+    if (paged)
+      prefill_generic_kernel<float, true><<<grid, kWave, 0, st>>>(a);
+    else
+      prefill_generic_kernel<float, false><<<grid, kWave, 0, st>>>(a);
+  } else {
+    if (paged)
+      prefill_generic_kernel<bf16, true><<<grid, kWave, 0, st>>>(a);
+    else
+      prefill_generic_kernel<bf16, false><<<grid, kWave, 0, st>>>(a);
+  }
+  KVP_LAUNCH_CHECK(name);
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" kv_status paged_attn_prefill(
+    void* out, const void* q, const int32_t* cu_q_lens,
+    const int32_t* q_start_pos, int32_t max_q_len, const void* k_cache,
+    const void* v_cache, int32_t num_blocks, const int32_t* block_tables,
+    int32_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, int32_t causal, kv_dtype dtype,
+    void* stream) {
+  PrefillArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.cu_q = cu_q_lens;
+  a.q_start = q_start_pos;
+  a.max_q_len = max_q_len;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.ctx = context_lens;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal ? 1 : 0;
+  return run_prefill("paged_attn_prefill", true, a, dtype, (hipStream_t)stream);
+}
+
+extern "C" kv_status contig_attn_prefill(
+    void* out, const void* q, const int32_t* cu_q_lens,
+    const int32_t* q_start_pos, int32_t max_q_len, const void* k,
+    const void* v, int32_t seq_stride, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, float scale, int32_t causal, kv_dtype dtype,
+    void* stream) {
+  PrefillArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.cu_q = cu_q_lens;
+  a.q_start = q_start_pos;
+  a.max_q_len = max_q_len;
+  a.k = k;
+  a.v = v;
+  a.seq_stride = seq_stride;
+  a.block_size = 16;
+  a.ctx = context_lens;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal ? 1 : 0;
+  return run_prefill("contig_attn_prefill", false, a, dtype,
+                     (hipStream_t)stream);
+}

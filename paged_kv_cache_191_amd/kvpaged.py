@@ -1,0 +1,406 @@
+"""Python binding of libkvpaged.so (include/kvpaged.h).
+
+Argument marshalling only: every step runs in the native library (host
+allocator in C++, device ops in HIP kernels). Device tensors are torch CUDA
+tensors, passed as raw pointers on torch's current stream. If the library
+is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvpaged.so")
+
+KV_OK = 0
+KV_EINVAL = -1
+KV_ENOMEM = -2
+KV_EREFCOUNT = -3
+KV_EHIP = -4
+KV_EUNSUPPORTED = -5
+KV_F32 = 0
+KV_BF16 = 1
+
+STATUS_NAMES = {KV_OK: "KV_OK", KV_EINVAL: "KV_EINVAL",
+                KV_ENOMEM: "KV_ENOMEM", KV_EREFCOUNT: "KV_EREFCOUNT",
+                KV_EHIP: "KV_EHIP", KV_EUNSUPPORTED: "KV_EUNSUPPORTED"}
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+
+# name -> (restype, argtypes); mirrors include/kvpaged.h
+SIGNATURES = {
+    "kv_last_error": (ctypes.c_char_p, []),
+    "kv_blocks_needed": (_I64, [_I64, _I32]),
+    "kv_pool_create": (_I32, [_I32, _I32, _PI32, ctypes.POINTER(_P)]),
+    "kv_pool_destroy": (None, [_P]),
+    "kv_block_alloc": (_I32, [_P, _I32, _PI32]),
+    "kv_block_free": (_I32, [_P, _I32, _PI32]),
+    "kv_block_share": (_I32, [_P, _I32, _PI32]),
+    "kv_block_cow": (_I32, [_P, _I32, _PI32, _PI32]),
+    "kv_block_refcount": (_I32, [_P, _I32]),
+    "kv_pool_num_free": (_I32, [_P]),
+    "kv_pool_num_blocks": (_I32, [_P]),
+    "kv_pool_block_size": (_I32, [_P]),
+    "kv_pool_free_list": (_I32, [_P, _PI32, _I32]),
+    "kv_seq_append": (_I32, [_P, _PI32, _I32, _PI32, _PI32, _I32, _PI64,
+                             _PI32, _I32, _PI32]),
+    "kv_slot_mapping": (_I32, [_PI32, _I32, _PI32, _PI32, _I32, _I32,
+                               _PI64]),
+    "kv_reshape_and_cache": (_I32, [_P, _P, _P, _I32, _P, _P, _I64, _I32,
+                                    _I32, _I32, _P]),
+    "kv_copy_blocks": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                              _I32, _P]),
+    "kv_decode_partition": (_I32, [_I32, _I32, _I32, _I32]),
+    "kv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "paged_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
+                                 _I32, _I32, _I32, _I32, _I32, _F, _I32, _P,
+                                 _SZ, _P]),
+    "contig_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                  _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
+    "paged_attn_prefill": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _P,
+                                  _I32, _P, _I32, _I32, _I32, _I32, _I32, _F,
+                                  _I32, _I32, _P]),
+    "contig_attn_prefill": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _P,
+                                   _I32, _I32, _I32, _I32, _F, _I32, _I32,
+                                   _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvpaged.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -c 'import "
+                f"__graft_entry__ as g; g.build()'` first")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+class KVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().kv_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def _check(st: int, where: str) -> None:
+    if st != KV_OK:
+        raise KVError(st, where)
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(_PI32)
+
+
+def _i64p(a: np.ndarray):
+    return a.ctypes.data_as(_PI64)
+
+
+def _as_i32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+# ----------------------------------------------------------------- host ---
+def kv_blocks_needed(num_tokens: int, block_size: int) -> int:
+    return int(lib().kv_blocks_needed(int(num_tokens), int(block_size)))
+
+
+def kv_last_error() -> str:
+    return lib().kv_last_error().decode(errors="replace")
+
+
+class KVPool:
+    """Owner of a native kv_pool (host block metadata)."""
+
+    def __init__(self, num_blocks: int, block_size: int,
+                 free_order: Optional[Sequence[int]] = None):
+        self._h = None
+        handle = _P()
+        order = None if free_order is None else _as_i32(free_order)
+        st = lib().kv_pool_create(int(num_blocks), int(block_size),
+                                  None if order is None else _i32p(order),
+                                  ctypes.byref(handle))
+        _check(st, "kv_pool_create")
+        self._h = handle
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            lib().kv_pool_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    # Status-returning forms (used by the parity tests).
+    def alloc_status(self, n: int) -> Tuple[int, list]:
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        st = lib().kv_block_alloc(self._h, int(n), _i32p(out))
+        return st, (out[:n].tolist() if st == KV_OK else [])
+
+    def free_status(self, ids) -> int:
+        a = _as_i32(ids)
+        return lib().kv_block_free(self._h, len(a), _i32p(a))
+
+    def share_status(self, ids) -> int:
+        a = _as_i32(ids)
+        return lib().kv_block_share(self._h, len(a), _i32p(a))
+
+    def cow_status(self, b: int) -> Tuple[int, int, int]:
+        out, need = ctypes.c_int32(-1), ctypes.c_int32(0)
+        st = lib().kv_block_cow(self._h, int(b), ctypes.byref(out),
+                                ctypes.byref(need))
+        if st != KV_OK:
+            return st, -1, 0
+        return st, out.value, need.value
+
+    # Raising forms.
+    def alloc(self, n: int) -> list:
+        st, ids = self.alloc_status(n)
+        _check(st, "kv_block_alloc")
+        return ids
+
+    def free(self, ids) -> None:
+        _check(self.free_status(ids), "kv_block_free")
+
+    def share(self, ids) -> None:
+        _check(self.share_status(ids), "kv_block_share")
+
+    def cow(self, b: int) -> Tuple[int, int]:
+        st, out, need = self.cow_status(b)
+        _check(st, "kv_block_cow")
+        return out, need
+
+    def refcount(self, b: int) -> int:
+        return int(lib().kv_block_refcount(self._h, int(b)))
+
+    def num_free(self) -> int:
+        return int(lib().kv_pool_num_free(self._h))
+
+    def free_list(self) -> list:
+        n = self.num_free()
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        lib().kv_pool_free_list(self._h, _i32p(out), n)
+        return out[:n].tolist()
+
+    def seq_append_status(self, tables: np.ndarray, lens: np.ndarray,
+                          n_new=None, cow_capacity: Optional[int] = None):
+        """kv_seq_append on host arrays tables [S, stride] int32 and lens
+        [S] int32 (both updated in place). Returns (status, slots int64,
+        cow pairs int32 [n, 2])."""
+        assert tables.dtype == np.int32 and tables.flags.c_contiguous
+        assert lens.dtype == np.int32 and lens.flags.c_contiguous
+        S = lens.shape[0]
+        nn = None if n_new is None else _as_i32(n_new)
+        total = S if nn is None else int(np.clip(nn, 0, None).sum())
+        slots = np.zeros(max(total, 1), dtype=np.int64)
+        cap = S if cow_capacity is None else int(cow_capacity)
+        pairs = np.zeros((max(cap, 1), 2), dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        st = lib().kv_seq_append(self._h, _i32p(tables), tables.shape[1],
+                                 _i32p(lens),
+                                 None if nn is None else _i32p(nn), S,
+                                 _i64p(slots), _i32p(pairs), cap,
+                                 ctypes.byref(ncow))
+        if st != KV_OK:
+            return st, np.zeros(0, np.int64), np.zeros((0, 2), np.int32)
+        return st, slots[:total], pairs[:ncow.value]
+
+    def seq_append(self, tables, lens, n_new=None, cow_capacity=None):
+        st, slots, pairs = self.seq_append_status(tables, lens, n_new,
+                                                  cow_capacity)
+        _check(st, "kv_seq_append")
+        return slots, pairs
+
+
+def kv_pool_create(num_blocks: int, block_size: int, free_order=None
+                   ) -> KVPool:
+    return KVPool(num_blocks, block_size, free_order)
+
+
+def kv_slot_mapping(block_tables: np.ndarray, seq_ids, positions,
+                    block_size: int) -> np.ndarray:
+    bt = _as_i32(block_tables)
+    sid = _as_i32(seq_ids)
+    pos = _as_i32(positions)
+    out = np.zeros(max(len(pos), 1), dtype=np.int64)
+    st = lib().kv_slot_mapping(_i32p(bt), bt.shape[1], _i32p(sid), _i32p(pos),
+                               len(pos), int(block_size), _i64p(out))
+    _check(st, "kv_slot_mapping")
+    return out[:len(pos)]
+
+
+# --------------------------------------------------------------- device ---
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return KV_F32
+    if t.dtype == torch.bfloat16:
+        return KV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name: str, dtype=None):
+    """Pointer of a contiguous CUDA tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def kv_reshape_and_cache(k, v, slots, k_cache, v_cache, stream=None) -> None:
+    torch = _torch()
+    n, hkv, d = k.shape
+    num_slots = k_cache.numel() // (hkv * d)
+    st = lib().kv_reshape_and_cache(
+        _dev(k, "k"), _dev(v, "v", k.dtype), _dev(slots, "slots", torch.int64),
+        n, _dev(k_cache, "k_cache", k.dtype), _dev(v_cache, "v_cache", k.dtype),
+        num_slots, hkv, d, _dtype_code(k), _stream(stream))
+    _check(st, "kv_reshape_and_cache")
+
+
+def kv_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
+    torch = _torch()
+    nb, bs, hkv, d = k_cache.shape
+    st = lib().kv_copy_blocks(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
+        _dev(src_dst, "src_dst", torch.int32), src_dst.shape[0], nb, bs, hkv,
+        d, _dtype_code(k_cache), _stream(stream))
+    _check(st, "kv_copy_blocks")
+
+
+def kv_decode_partition(num_seqs, num_q_heads, num_kv_heads, max_context
+                        ) -> int:
+    return int(lib().kv_decode_partition(num_seqs, num_q_heads, num_kv_heads,
+                                         max_context))
+
+
+def kv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                              max_context) -> int:
+    return int(lib().kv_decode_workspace_bytes(num_seqs, num_q_heads,
+                                               num_kv_heads, head_dim,
+                                               max_context))
+
+
+def decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                     max_context, device="cuda"):
+    """A device buffer of kv_decode_workspace_bytes (torch-allocated)."""
+    torch = _torch()
+    n = kv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                  head_dim, max_context)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                      max_context: int, scale: float, workspace=None,
+                      stream=None) -> None:
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if workspace is None:
+        workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
+    st = lib().paged_attn_decode(
+        _dev(out, "out", q.dtype), _dev(q, "q"),
+        _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        nb, _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context), S, hq, hkv, d, bs, float(scale), _dtype_code(q),
+        _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "paged_attn_decode")
+
+
+def contig_attn_decode(out, q, k, v, context_lens, max_context: int,
+                       scale: float, workspace=None, stream=None) -> None:
+    torch = _torch()
+    S, hq, d = q.shape
+    _, lmax, hkv, _ = k.shape
+    if workspace is None:
+        workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
+    st = lib().contig_attn_decode(
+        _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k, "k", q.dtype),
+        _dev(v, "v", q.dtype), lmax,
+        _dev(context_lens, "context_lens", torch.int32), int(max_context), S,
+        hq, hkv, d, float(scale), _dtype_code(q), _dev(workspace, "workspace"),
+        workspace.numel(), _stream(stream))
+    _check(st, "contig_attn_decode")
+
+
+def paged_attn_prefill(out, q, cu_q_lens, q_start_pos, max_q_len: int,
+                       k_cache, v_cache, block_tables, context_lens,
+                       scale: float, causal: bool = True, stream=None) -> None:
+    torch = _torch()
+    T, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    S = cu_q_lens.shape[0] - 1
+    st = lib().paged_attn_prefill(
+        _dev(out, "out", q.dtype), _dev(q, "q"),
+        _dev(cu_q_lens, "cu_q_lens", torch.int32),
+        _dev(q_start_pos, "q_start_pos", torch.int32), int(max_q_len),
+        _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        nb, _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        S, hq, hkv, d, bs, float(scale), 1 if causal else 0, _dtype_code(q),
+        _stream(stream))
+    _check(st, "paged_attn_prefill")
+
+
+def contig_attn_prefill(out, q, cu_q_lens, q_start_pos, max_q_len: int, k, v,
+                        context_lens, scale: float, causal: bool = True,
+                        stream=None) -> None:
+    torch = _torch()
+    T, hq, d = q.shape
+    S = cu_q_lens.shape[0] - 1
+    _, lmax, hkv, _ = k.shape
+    if k.shape[0] < S:
+        raise ValueError("k holds fewer sequences than cu_q_lens describes")
+    st = lib().contig_attn_prefill(
+        _dev(out, "out", q.dtype), _dev(q, "q"),
+        _dev(cu_q_lens, "cu_q_lens", torch.int32),
+        _dev(q_start_pos, "q_start_pos", torch.int32), int(max_q_len),
+        _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), lmax,
+        _dev(context_lens, "context_lens", torch.int32), S, hq, hkv, d,
+        float(scale), 1 if causal else 0, _dtype_code(q), _stream(stream))
+    _check(st, "contig_attn_prefill")

@@ -1,0 +1,292 @@
+"""GPU parity of the cache write and decode kernels against the fp64 oracle,
+through the C ABI. Pools start as NaN so that a kernel reading an unused or
+tail slot fails the comparison."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import helpers as H
+from native import ensure_built
+from oracle import attention as O
+from paged_kv_cache_191_amd import kvpaged as kv
+from paged_kv_cache_191_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    ensure_built()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def _draw(w, headroom=0):
+    return W.draw(w, lambda lens: H.pool_blocks_for(w, lens, headroom))
+
+
+def _decode_both(inp, nat, orc, ctx_np, seqs=None, contig=True):
+    w = inp.workload
+    scale = H.scale_of(w)
+    q_dev = inp.q.cuda()
+    max_ctx = int(ctx_np.max())
+    out = torch.empty_like(q_dev)
+    kv.paged_attn_decode(out, q_dev, nat.k_cache, nat.v_cache, nat.bt,
+                         nat.ctx, max_ctx, scale)
+    outs = {"paged": out}
+    if contig:
+        kc, vc = H.contig_from_inputs(inp, max_ctx)
+        oc = torch.empty_like(q_dev)
+        kv.contig_attn_decode(oc, q_dev, kc, vc, nat.ctx, max_ctx, scale)
+        outs["contig"] = oc
+        del kc, vc
+    torch.cuda.synchronize()
+    want = O.decode_paged(inp.q.float().numpy(), orc.k_pool, orc.v_pool,
+                          orc.tables, ctx_np, scale, seqs=seqs)
+    return {k: v.float().cpu().numpy() for k, v in outs.items()}, want
+
+
+def _check(outs, want, w, seqs=None):
+    tol = H.tolerance(w)
+    sel = slice(None) if seqs is None else list(seqs)
+    for name, got in outs.items():
+        err = H.max_abs(got[sel], want[sel])
+        _log(f"{w.name} {name}: max-abs {err:.3e} (tol {tol})")
+        assert err <= tol, (name, err)
+
+
+# ------------------------------------------------------------ cache write --
+@pytest.mark.parametrize("case", ["decode_tiny_f32", "small_bf16",
+                                  "prefix_cow"])
+def test_reshape_and_cache_bit_exact(case):
+    if case == "decode_tiny_f32":
+        w = W.WORKLOADS["decode_tiny_f32"]
+    elif case == "small_bf16":
+        w = W.WORKLOADS["llama3_8b_decode"].replace(
+            num_seqs=6, length_range=(1, 300), name="small_bf16")
+    else:
+        w = W.WORKLOADS["prefix_share_decode"].replace(
+            num_seqs=5, prefix_len=40, length_range=(0, 30), name="prefix_cow")
+    _log(f"case {case}")
+    inp = _draw(w, headroom=8)
+    cap = H.tables_capacity(int(W.context_lengths(inp).max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    for s in range(w.num_seqs):
+        assert nat.tables[s, :len(orc.tables[s])].tolist() == orc.tables[s]
+    assert nat.lens.tolist() == orc.lens
+    for dev, ref in ((nat.k_cache, orc.k_pool), (nat.v_cache, orc.v_pool)):
+        got = dev.float().cpu().numpy()
+        assert np.array_equal(got, ref, equal_nan=True)
+
+
+def test_copy_blocks_bit_exact():
+    w = W.WORKLOADS["decode_tiny_f32"].replace(pool_blocks=None)
+    inp = _draw(w, headroom=6)
+    nat = H.build_native(inp, 16, 8)
+    n = nat.k_cache.shape[0]
+    before_k = nat.k_cache.clone()
+    before_v = nat.v_cache.clone()
+    free = nat.pool.free_list()   # destinations: blocks no pair reads
+    pairs = np.array([[nat.tables[0, 0], free[0]], [nat.tables[3, 2], free[1]],
+                      [nat.tables[0, 0], free[2]], [n + 5, 0]], dtype=np.int32)
+    kv.kv_copy_blocks(nat.k_cache, nat.v_cache,
+                      torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    ref_k = before_k.cpu().numpy()
+    ref_v = before_v.cpu().numpy()
+    O.copy_blocks(ref_k, pairs[:3])
+    O.copy_blocks(ref_v, pairs[:3])
+    assert np.array_equal(nat.k_cache.cpu().numpy(), ref_k, equal_nan=True)
+    assert np.array_equal(nat.v_cache.cpu().numpy(), ref_v, equal_nan=True)
+
+
+# ----------------------------------------------------------------- decode --
+def test_decode_tiny_f32():
+    w = W.WORKLOADS["decode_tiny_f32"]
+    inp = _draw(w)
+    nat = H.build_native(inp, 16, 8)
+    orc = H.build_oracle(inp, 16)
+    ctx = W.context_lengths(inp)
+    outs, want = _decode_both(inp, nat, orc, ctx)
+    _check(outs, want, w)
+    # one-token context: the output is that token's V row
+    v0 = inp.v[int(inp.cu[2])].numpy()
+    assert np.array_equal(outs["paged"][2], v0)
+    assert np.array_equal(outs["paged"], outs["contig"])
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_decode"])
+def test_decode_full_size(name):
+    w = W.WORKLOADS[name]
+    _log(f"drawing {name}")
+    inp = _draw(w)
+    ctx = W.context_lengths(inp)
+    cap = H.tables_capacity(int(ctx.max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    outs, want = _decode_both(inp, nat, orc, ctx)
+    _check(outs, want, w)
+    assert np.array_equal(outs["paged"], outs["contig"])
+
+
+def test_decode_long_context_split():
+    # Yi-34B shape (G = 7, B = 64), shortened and ragged: many partitions.
+    w = W.WORKLOADS["yi34b_long_decode"].replace(
+        num_seqs=3, lengths=(20000, 4097, 131), name="yi34b_short")
+    inp = _draw(w)
+    ctx = W.context_lengths(inp)
+    cap = H.tables_capacity(int(ctx.max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    outs, want = _decode_both(inp, nat, orc, ctx)
+    _check(outs, want, w)
+    assert np.array_equal(outs["paged"], outs["contig"])
+
+
+def test_decode_yi34b_full_size_sampled():
+    w = W.WORKLOADS["yi34b_long_decode"]
+    _log("drawing yi34b_long_decode (6.4 GB of K/V)")
+    inp = _draw(w)
+    ctx = W.context_lengths(inp)
+    cap = H.tables_capacity(int(ctx.max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    outs, want = _decode_both(inp, nat, orc, ctx, seqs=[0, 3])
+    _check(outs, want, w, seqs=[0, 3])
+    assert np.array_equal(outs["paged"], outs["contig"])
+
+
+def test_decode_prefix_sharing_sampled():
+    w = W.WORKLOADS["prefix_share_decode"]
+    inp = _draw(w)
+    ctx = W.context_lengths(inp)
+    cap = H.tables_capacity(int(ctx.max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    prefix_blocks = w.prefix_len // w.block_size
+    assert all(nat.pool.refcount(int(b)) == w.num_seqs
+               for b in nat.tables[0, :prefix_blocks])
+    seqs = [0, 1, 17, 100, 254, 255]
+    outs, want = _decode_both(inp, nat, orc, ctx, seqs=seqs)
+    _check(outs, want, w, seqs=seqs)
+
+
+def test_decode_step_with_copy_on_write():
+    # 256 sequences share a 4104-token prefix (last block half full); each
+    # appends one token: 255 copies, the last sequence writes in place.
+    w = W.WORKLOADS["prefix_share_decode"].replace(
+        prefix_len=4104, length_range=(1, 1), name="prefix_cow_step")
+    inp = _draw(w, headroom=256)
+    ctx = W.context_lengths(inp)
+    cap = H.tables_capacity(int(ctx.max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap, upto=w.prefix_len)
+    orc = H.build_oracle(inp, w.block_size, upto=w.prefix_len)
+    # the step, device side
+    slots, pairs = nat.pool.seq_append(nat.tables, nat.lens)
+    assert len(pairs) == w.num_seqs - 1
+    kv.kv_copy_blocks(nat.k_cache, nat.v_cache,
+                      torch.from_numpy(pairs).cuda())
+    rows = torch.from_numpy(np.array([W.logical_rows(inp, s)[-1]
+                                      for s in range(w.num_seqs)]))
+    kv.kv_reshape_and_cache(inp.k[rows].cuda(), inp.v[rows].cuda(),
+                            torch.from_numpy(slots).cuda(), nat.k_cache,
+                            nat.v_cache)
+    nat.bt = torch.from_numpy(nat.tables).cuda()
+    nat.ctx = torch.from_numpy(nat.lens.copy()).cuda()
+    # the step, oracle side
+    from oracle import allocator as A
+    st, oslots, opairs = A.append_tokens(orc.pool, orc.tables, orc.lens,
+                                         [1] * w.num_seqs, 1 << 30)
+    assert st == A.OK
+    assert [tuple(p) for p in pairs.tolist()] == opairs
+    assert slots.tolist() == oslots
+    O.copy_blocks(orc.k_pool, opairs)
+    O.copy_blocks(orc.v_pool, opairs)
+    O.scatter_rows(orc.k_pool, inp.k[rows].float().numpy(), oslots)
+    O.scatter_rows(orc.v_pool, inp.v[rows].float().numpy(), oslots)
+    torch.cuda.synchronize()
+    assert np.array_equal(nat.k_cache.float().cpu().numpy(), orc.k_pool,
+                          equal_nan=True)
+    assert np.array_equal(nat.v_cache.float().cpu().numpy(), orc.v_pool,
+                          equal_nan=True)
+    seqs = [0, 1, 128, 254, 255]
+    outs, want = _decode_both(inp, nat, orc, ctx, seqs=seqs, contig=False)
+    _check(outs, want, w, seqs=seqs)
+
+
+def test_decode_step_appends_through_native_path():
+    # Llama-3-8B shape: contexts written up to L-1, then one decode step
+    # (append, cache write, attention) over all 64 sequences.
+    w = W.WORKLOADS["llama3_8b_decode"].replace(num_seqs=16)
+    inp = _draw(w, headroom=16)
+    ctx = W.context_lengths(inp)
+    cap = H.tables_capacity(int(ctx.max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap, upto=ctx - 1)
+    orc = H.build_oracle(inp, w.block_size)
+    slots, pairs = nat.pool.seq_append(nat.tables, nat.lens)
+    assert len(pairs) == 0 and nat.lens.tolist() == ctx.tolist()
+    rows = torch.from_numpy(np.array([W.logical_rows(inp, s)[-1]
+                                      for s in range(w.num_seqs)]))
+    kv.kv_reshape_and_cache(inp.k[rows].cuda(), inp.v[rows].cuda(),
+                            torch.from_numpy(slots).cuda(), nat.k_cache,
+                            nat.v_cache)
+    nat.bt = torch.from_numpy(nat.tables).cuda()
+    nat.ctx = torch.from_numpy(nat.lens.copy()).cuda()
+    outs, want = _decode_both(inp, nat, orc, ctx, contig=False)
+    _check(outs, want, w)
+
+
+def test_decode_physical_permutation_is_bit_identical():
+    w = W.WORKLOADS["llama3_8b_decode"].replace(num_seqs=8)
+    a = _draw(w)
+    b = _draw(w)
+    b.free_order = np.random.default_rng(77).permutation(len(b.free_order)
+                                                         ).astype(np.int32)
+    ctx = W.context_lengths(a)
+    cap = H.tables_capacity(int(ctx.max()), w.block_size)
+    na = H.build_native(a, 16, cap)
+    nb = H.build_native(b, 16, cap)
+    assert not np.array_equal(na.tables, nb.tables)
+    outs = []
+    for n in (na, nb, na):
+        o = torch.empty_like(a.q.cuda())
+        kv.paged_attn_decode(o, a.q.cuda(), n.k_cache, n.v_cache, n.bt,
+                             n.ctx, int(ctx.max()), H.scale_of(w))
+        outs.append(o.cpu())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
+@pytest.mark.parametrize("variant", ["g20_d128", "d64_bf16", "empty_and_one"])
+def test_decode_edge_shapes(variant):
+    base = W.WORKLOADS["llama3_8b_decode"]
+    if variant == "g20_d128":     # two head blocks of the MFMA path
+        w = base.replace(num_seqs=3, num_q_heads=40, num_kv_heads=2,
+                         lengths=(1, 700, 129), length_range=None,
+                         name=variant)
+    elif variant == "d64_bf16":   # generic path
+        w = base.replace(num_seqs=3, head_dim=64, lengths=(5, 300, 33),
+                         length_range=None, name=variant)
+    else:                         # empty context -> zeros; one token -> V0
+        w = base.replace(num_seqs=4, lengths=(0, 1, 16, 513),
+                         length_range=None, name=variant)
+    inp = _draw(w)
+    ctx = W.context_lengths(inp)
+    cap = H.tables_capacity(int(max(ctx.max(), 1)), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    outs, want = _decode_both(inp, nat, orc, ctx)
+    _check(outs, want, w)
+    if variant == "empty_and_one":
+        assert (outs["paged"][0] == 0).all()
+        v0 = inp.v[int(inp.cu[1])].float().numpy()      # [Hkv, D]
+        G = w.num_q_heads // w.num_kv_heads
+        assert np.array_equal(outs["paged"][1], np.repeat(v0, G, axis=0))
