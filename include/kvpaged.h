@@ -25,16 +25,18 @@
  *     `stream` (a hipStream_t; NULL = the default stream), return after the
  *     launch, and allocate no device memory. Launch failures return KV_EHIP.
  *   - Layouts (row-major, element type = `dtype`):
- *       paged K/V pool        [num_blocks, block_size, Hkv, D]
- *       contiguous K/V        [num_seqs, seq_stride, Hkv, D]
+ *       paged K/V pool        [num_blocks, Hkv, block_size, D]
+ *       contiguous K/V        [num_seqs, Hkv, seq_stride, D]
  *       new K/V rows          [num_tokens, Hkv, D]
  *       decode q / out        [num_seqs, Hq, D]
  *       prefill q / out       [total_q, Hq, D]   (sequence s owns rows
  *                                                 cu_q_lens[s]..cu_q_lens[s+1])
  *       block table           int32 [num_seqs, bt_stride]
- *     A slot numbers the token rows of a cache: slot = block * block_size +
- *     offset for the paged pool, s * seq_stride + position for the
- *     contiguous layout.
+ *     Both caches are head-major inside a block (or sequence): the D values
+ *     of one head for consecutive tokens are contiguous. A slot numbers the
+ *     tokens of a cache: slot = block * block_size + offset for the paged
+ *     pool, s * seq_stride + position for the contiguous layout (whose
+ *     "block" is the whole sequence).
  *   - Query head h reads KV head h / (Hq / Hkv). Attention is softmax of
  *     scale * q.k over the visible keys, accumulated in fp32; out has the
  *     dtype of q.
@@ -145,15 +147,16 @@ kv_status kv_slot_mapping(const int32_t* block_tables, int32_t bt_stride,
 /* ---------------------------------------------------------------------
  * Cache write [step 2: a new token's K and V go into its slot].
  * k, v: new rows [num_tokens, Hkv, D]; slots: device int64 [num_tokens].
- * Row i is copied to cache row slots[i] of k_cache/v_cache, which hold
- * num_slots token rows of Hkv*D elements (paged: num_blocks*block_size,
- * contiguous: num_seqs*seq_stride). Slots < 0 (padding) and slots >=
- * num_slots are skipped. Bit copy. */
+ * For every head h, k[i, h, :] goes to k_cache[slot / block_size, h,
+ * slot % block_size, :] (same for v). The caches hold num_slots tokens
+ * (paged: num_blocks * block_size; contiguous: num_seqs * seq_stride with
+ * block_size = seq_stride). Slots < 0 (padding) and slots >= num_slots are
+ * skipped. Bit copy. */
 kv_status kv_reshape_and_cache(const void* k, const void* v,
                                const int64_t* slots, int32_t num_tokens,
                                void* k_cache, void* v_cache, int64_t num_slots,
-                               int32_t num_kv_heads, int32_t head_dim,
-                               kv_dtype dtype, void* stream);
+                               int32_t block_size, int32_t num_kv_heads,
+                               int32_t head_dim, kv_dtype dtype, void* stream);
 
 /* Copy-on-write data move: for i < n, block src_dst[2i] -> src_dst[2i+1]
  * of both caches (device int32 pairs). The pairs must be independent: no
@@ -196,7 +199,7 @@ kv_status paged_attn_decode(void* out, const void* q, const void* k_cache,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
-/* Same on the contiguous layout [num_seqs, seq_stride, Hkv, D]. */
+/* Same on the contiguous layout [num_seqs, Hkv, seq_stride, D]. */
 kv_status contig_attn_decode(void* out, const void* q, const void* k,
                              const void* v, int32_t seq_stride,
                              const int32_t* context_lens, int32_t max_context,

@@ -5,8 +5,9 @@
 // ["PagedAttention Nedir?" (bitcanli.com), "PagedAttention Nasıl Çalışır?",
 // steps 2-3]; a shared block is copied before it is written
 // ["Makale Bülteni — PagedAttention ve vLLM", "İddia ve Gerçeklik"].
-// Both are plain byte moves bounded by HBM bandwidth: each row is moved in
-// 16-byte (or 4/2-byte) units, consecutive lanes on consecutive units.
+// Both are plain byte moves bounded by HBM bandwidth: each head row is moved
+// in 16-byte (or 4/2-byte) units, consecutive lanes on consecutive units.
+// Caches are head-major inside a block: [blocks, Hkv, block_size, D].
 
 #include "device_common.h"
 
@@ -14,25 +15,35 @@ namespace {
 
 using namespace kvp;
 
+// One work item = one unit of one head of one token of K or V. Source
+// rows are token-major [T, Hkv, D]; destinations are head-major inside a
+// block: unit u of head h of slot goes to
+// ((slot / B) * Hkv + h) * B + slot % B (in head rows of D).
 template <typename U>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(
     const U* __restrict__ k, const U* __restrict__ v,
     const int64_t* __restrict__ slots, int32_t num_tokens, U* k_cache,
-    U* v_cache, int64_t num_slots, int32_t units_per_row) {
-  // One work item = one unit of one row of K or V.
-  const int64_t per_tensor = (int64_t)num_tokens * units_per_row;
+    U* v_cache, int64_t num_slots, int32_t block_size, int32_t num_kv_heads,
+    int32_t units_per_head) {
+  const int64_t per_token = (int64_t)num_kv_heads * units_per_head;
+  const int64_t per_tensor = (int64_t)num_tokens * per_token;
   const int64_t total = 2 * per_tensor;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const bool is_v = i >= per_tensor;
     const int64_t j = is_v ? i - per_tensor : i;
-    const int64_t t = j / units_per_row;
-    const int64_t u = j - t * units_per_row;
+    const int64_t t = j / per_token;
+    const int64_t r = j - t * per_token;       // unit within the token row
+    const int64_t h = r / units_per_head;
+    const int64_t u = r - h * units_per_head;
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / block_size;
+    const int64_t off = slot - blk * block_size;
     const U* src = is_v ? v : k;
     U* dst = is_v ? v_cache : k_cache;
-    dst[slot * units_per_row + u] = src[t * units_per_row + u];
+    dst[((blk * num_kv_heads + h) * block_size + off) * units_per_head + u] =
+        src[t * per_token + r];
   }
 }
 
@@ -66,39 +77,45 @@ extern "C" kv_status kv_reshape_and_cache(const void* k, const void* v,
                                           const int64_t* slots,
                                           int32_t num_tokens, void* k_cache,
                                           void* v_cache, int64_t num_slots,
+                                          int32_t block_size,
                                           int32_t num_kv_heads,
                                           int32_t head_dim, kv_dtype dtype,
                                           void* stream) {
   if (dtype != KV_F32 && dtype != KV_BF16)
     return kvp_fail(KV_EINVAL, "kv_reshape_and_cache: unknown dtype %d",
                     (int)dtype);
-  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_slots < 0)
-    return kvp_fail(KV_EINVAL, "kv_reshape_and_cache: bad shape");
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_slots < 0 ||
+      block_size <= 0 || num_slots % block_size != 0)
+    return kvp_fail(KV_EINVAL, "kv_reshape_and_cache: bad shape (slots=%lld "
+                    "block_size=%d)", (long long)num_slots, block_size);
   if (num_tokens == 0) return KV_OK;
   if (!k || !v || !slots || !k_cache || !v_cache)
     return kvp_fail(KV_EINVAL, "kv_reshape_and_cache: NULL pointer");
-  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_size(dtype);
+  const int64_t head_bytes = (int64_t)head_dim * elem_size(dtype);
   hipStream_t st = (hipStream_t)stream;
   const int threads = 256;
   auto grid_for = [&](int64_t items) {
     int64_t g = (items + threads - 1) / threads;
     return (int)(g < 65536 ? g : 65536);
   };
-  if (row_bytes % 16 == 0) {
-    const int32_t upr = (int32_t)(row_bytes / 16);
-    scatter_rows_kernel<u32x4><<<grid_for(2LL * num_tokens * upr), threads, 0, st>>>(
+  const int64_t heads = (int64_t)num_tokens * num_kv_heads;
+  if (head_bytes % 16 == 0) {
+    const int32_t uph = (int32_t)(head_bytes / 16);
+    scatter_rows_kernel<u32x4><<<grid_for(2 * heads * uph), threads, 0, st>>>(
         (const u32x4*)k, (const u32x4*)v, slots, num_tokens, (u32x4*)k_cache,
-        (u32x4*)v_cache, num_slots, upr);
-  } else if (row_bytes % 4 == 0) {
-    const int32_t upr = (int32_t)(row_bytes / 4);
-    scatter_rows_kernel<uint32_t><<<grid_for(2LL * num_tokens * upr), threads, 0, st>>>(
+        (u32x4*)v_cache, num_slots, block_size, num_kv_heads, uph);
+  } else if (head_bytes % 4 == 0) {
+    const int32_t uph = (int32_t)(head_bytes / 4);
+    scatter_rows_kernel<uint32_t><<<grid_for(2 * heads * uph), threads, 0, st>>>(
         (const uint32_t*)k, (const uint32_t*)v, slots, num_tokens,
-        (uint32_t*)k_cache, (uint32_t*)v_cache, num_slots, upr);
+        (uint32_t*)k_cache, (uint32_t*)v_cache, num_slots, block_size,
+        num_kv_heads, uph);
   } else {
-    const int32_t upr = (int32_t)(row_bytes / 2);
-    scatter_rows_kernel<uint16_t><<<grid_for(2LL * num_tokens * upr), threads, 0, st>>>(
+    const int32_t uph = (int32_t)(head_bytes / 2);
+    scatter_rows_kernel<uint16_t><<<grid_for(2 * heads * uph), threads, 0, st>>>(
         (const uint16_t*)k, (const uint16_t*)v, slots, num_tokens,
-        (uint16_t*)k_cache, (uint16_t*)v_cache, num_slots, upr);
+        (uint16_t*)k_cache, (uint16_t*)v_cache, num_slots, block_size,
+        num_kv_heads, uph);
   }
   KVP_LAUNCH_CHECK("kv_reshape_and_cache");
   return KV_OK;

@@ -46,6 +46,7 @@ constexpr int kD = 128;      // head_dim of the MFMA path
 constexpr int kWaves = 4;    // waves per workgroup in the MFMA path
 constexpr int kTile = 32;    // tokens per wave iteration
 constexpr int kHeadBlk = 16; // query heads per MFMA column block
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 
 struct DecodeArgs {
   void* out;
@@ -92,16 +93,18 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
 template <bool PAGED>
 __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(
     DecodeArgs a) {
-  const int part_idx = blockIdx.x;
-  const int hblk = blockIdx.y % a.head_blocks;
-  const int g = blockIdx.y / a.head_blocks;
+  // KV heads vary fastest across consecutive workgroups, so the workgroups
+  // of one partition run together and read whole token rows (all heads).
+  const int hblk = blockIdx.x % a.head_blocks;
+  const int g = blockIdx.x / a.head_blocks;
+  const int part_idx = blockIdx.y;
   const int s = blockIdx.z;
   const int ctx = clamp_ctx(a, s, PAGED);
   const int nparts = ctx > 0 ? (ctx + a.part - 1) / a.part : 1;
   if (part_idx >= nparts) return;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int grp = lane >> 4;
@@ -134,12 +137,14 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(
 #pragma unroll
   for (int m = 0; m < 8; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t row_elems = (int64_t)a.hkv * kD;
-  const bf16* kbase = (const bf16*)a.k + (int64_t)g * kD;
-  const bf16* vbase = (const bf16*)a.v + (int64_t)g * kD;
+  // Head rows of D elements: head g of token `off` in block b is row
+  // (b * Hkv + g) * block_size + off (contiguous: (s * Hkv + g) * stride +
+  // position), so one head's tokens of a block are contiguous.
+  const bf16* kbase = (const bf16*)a.k;
+  const bf16* vbase = (const bf16*)a.v;
 
-  // Row index (slot) of the first token of every 16-token group of this
-  // wave's range, one group per lane (the range holds at most 64 groups).
+  // Head row of the first token of every 16-token group of this wave's
+  // range, one group per lane (the range holds at most 64 groups).
   // 16-token groups never straddle a block (block_size % 16 == 0 and w0 is
   // a multiple of 32), so a group's rows are row .. row + 15.
   int row_lane = 0;
@@ -149,13 +154,13 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(
       const int pos = w0 + 16 * lane;
       int b = a.bt[(int64_t)s * a.bt_stride + pos / a.block_size];
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      row_lane = b * a.block_size + pos % a.block_size;
+      row_lane = (b * a.hkv + g) * a.block_size + pos % a.block_size;
     }
   }
   // Last 16-token group that holds a valid token; groups past it re-read it
   // (in bounds) and are masked.
   const int last_grp = w1 > w0 ? ((w1 - 1 - w0) >> 4) : 0;
-  const int64_t seq_row0 = (int64_t)s * a.seq_stride;
+  const int64_t seq_row0 = ((int64_t)s * a.hkv + g) * a.seq_stride;
 
   // Row of the token `off` places after the start of group gi. Contiguous
   // rows are clamped to the last valid token so that a ragged tail never
@@ -173,18 +178,17 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(
     u32x4 kr[2][4];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const bf16* kp = kbase + row_of(gi0 + hf, r16) * row_elems + 8 * grp;
+      const bf16* kp = kbase + row_of(gi0 + hf, r16) * kD + 8 * grp;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kr[hf][i] = ld16(kp + 32 * i);
+      for (int i = 0; i < 4; ++i) kr[hf][i] = ld16_stream(kp + 32 * i);
     }
     // V: token rows tau(grp, e) = 16 (e / 4) + 4 grp + e % 4, d-chunk r16.
     u32x4 vr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const bf16* vp = vbase +
-                       row_of(gi0 + (e >> 2), 4 * grp + (e & 3)) * row_elems +
-                       8 * r16;
-      vr[e] = ld16(vp);
+      const bf16* vp =
+          vbase + row_of(gi0 + (e >> 2), 4 * grp + (e & 3)) * kD + 8 * r16;
+      vr[e] = ld16_stream(vp);
     }
 
     // S^T = K Q^T, two 16-token halves.
@@ -212,22 +216,27 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(
                      fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-
+    // Lazy rescaling: the reference max only moves when a score exceeds it
+    // by more than 2^8, so p <= 256 and most tiles skip the O rescale. The
+    // final division by l makes the result independent of the reference.
+    if (__any(mx > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) o[m] *= alpha;
+    }
     float p[2][4];
     float psum = 0.f;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[hf][r] = fast_exp2(x[hf][r] - m_new);
+        p[hf][r] = fast_exp2(x[hf][r] - m_run);
         psum += p[hf][r];
       }
-    l_part = l_part * alpha + psum;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) o[m] *= alpha;
+    l_part += psum;
 
     // P^T as the B operand of O^T += V^T P^T: k-slot e <-> token tau(grp, e).
     u32x4 pb;
@@ -334,22 +343,29 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeArgs a) {
   const int ctx = clamp_ctx(a, s, PAGED);
   const int nparts = ctx > 0 ? (ctx + a.part - 1) / a.part : 1;
   if (nparts <= 1) return;
+  const int lane = threadIdx.x;
   const int64_t base = ((int64_t)s * a.hq + h) * a.max_parts;
+  const float* ml = a.ws_ml + 2 * base;
+  // max and weighted sum over the partitions, lanes in parallel
   float M = -INFINITY;
-  for (int i = 0; i < nparts; ++i) M = fmaxf(M, a.ws_ml[2 * (base + i)]);
+  for (int i = lane; i < nparts; i += kWave) M = fmaxf(M, ml[2 * i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float L = 0.f;
-  for (int i = 0; i < nparts; ++i) {
-    const float mi = a.ws_ml[2 * (base + i)];
-    if (mi != -INFINITY) L += fast_exp2(mi - M) * a.ws_ml[2 * (base + i) + 1];
+  for (int i = lane; i < nparts; i += kWave) {
+    const float mi = ml[2 * i];
+    if (mi != -INFINITY) L += fast_exp2(mi - M) * ml[2 * i + 1];
   }
+  L = wave_sum(L);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   T* out = (T*)a.out + ((int64_t)s * a.hq + h) * a.head_dim;
-  for (int d = threadIdx.x; d < a.head_dim; d += kWave) {
+  const float* po = a.ws_o + base * a.head_dim;
+  for (int d = lane; d < a.head_dim; d += kWave) {
     float acc = 0.f;
     for (int i = 0; i < nparts; ++i) {
-      const float mi = a.ws_ml[2 * (base + i)];
+      const float mi = ml[2 * i];
       if (mi == -INFINITY) continue;
-      acc += fast_exp2(mi - M) * a.ws_o[(base + i) * a.head_dim + d];
+      acc += fast_exp2(mi - M) * po[(int64_t)i * a.head_dim + d];
     }
     out[d] = from_f32<T>(acc * inv);
   }
@@ -375,19 +391,18 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
     qv[i] = d < D ? to_f32<T>(qp[d]) : 0.f;
     acc[i] = 0.f;
   }
-  const int64_t row_elems = (int64_t)a.hkv * D;
   float m_run = -INFINITY, l = 0.f;
   for (int p = 0; p < ctx; ++p) {
-    int64_t row;
+    int64_t row;  // head row of (token p, KV head g)
     if (PAGED) {
       int b = a.bt[(int64_t)s * a.bt_stride + p / a.block_size];
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      row = (int64_t)b * a.block_size + p % a.block_size;
+      row = ((int64_t)b * a.hkv + g) * a.block_size + p % a.block_size;
     } else {
-      row = (int64_t)s * a.seq_stride + p;
+      row = ((int64_t)s * a.hkv + g) * a.seq_stride + p;
     }
-    const T* kp = (const T*)a.k + row * row_elems + (int64_t)g * D;
-    const T* vp = (const T*)a.v + row * row_elems + (int64_t)g * D;
+    const T* kp = (const T*)a.k + row * D;
+    const T* vp = (const T*)a.v + row * D;
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -466,8 +481,9 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
   if (paged && (a.block_size <= 0 || a.bt_stride <= 0 || a.num_blocks <= 0))
     return kvp_fail(KV_EINVAL, "%s: bad paging arguments (B=%d stride=%d N=%d)",
                     name, a.block_size, a.bt_stride, a.num_blocks);
-  if (paged && (int64_t)a.num_blocks * a.block_size > INT32_MAX)
-    return kvp_fail(KV_EUNSUPPORTED, "%s: pool of more than 2^31 slots", name);
+  if (paged && (int64_t)a.num_blocks * a.block_size * a.hkv > INT32_MAX)
+    return kvp_fail(KV_EUNSUPPORTED, "%s: pool of more than 2^31 head rows",
+                    name);
   if (!paged && a.seq_stride <= 0)
     return kvp_fail(KV_EINVAL, "%s: seq_stride must be > 0", name);
   if (a.num_seqs == 0) return KV_OK;
@@ -488,7 +504,7 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
       a.ws_o = (float*)workspace;
       a.ws_ml = a.ws_o + (size_t)a.num_seqs * a.hq * a.max_parts * a.head_dim;
     }
-    dim3 grid(a.max_parts, a.hkv * a.head_blocks, a.num_seqs);
+    dim3 grid(a.hkv * a.head_blocks, a.max_parts, a.num_seqs);
     if (paged)
       decode_mfma_kernel<true><<<grid, kWaves * kWave, 0, st>>>(a);
     else

@@ -142,9 +142,9 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(
   // Tile loader: thread tid moves keys 4n..4n+3, d-chunk 8c..8c+7.
   const int ln = tid >> 4;
   const int lc = tid & 15;
-  const int64_t row_elems = (int64_t)a.hkv * kD;
-  const bf16* kg = (const bf16*)a.k + (int64_t)kvh * kD + 8 * lc;
-  const bf16* vg = (const bf16*)a.v + (int64_t)kvh * kD + 8 * lc;
+  // Head rows of D elements (layout [blocks, Hkv, B, D] / [S, Hkv, L, D]).
+  const bf16* kg = (const bf16*)a.k + 8 * lc;
+  const bf16* vg = (const bf16*)a.v + 8 * lc;
   u32x4 kreg[4], vreg[4];
 
   auto load_tile = [&](int j) {
@@ -155,18 +155,20 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(
       const int kb = min(key0, ((kv_end - 1) >> 2) << 2);
       int b = a.bt[(int64_t)s * a.bt_stride + kb / a.block_size];
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      const int64_t row0 = (int64_t)b * a.block_size + kb % a.block_size;
+      const int64_t row0 =
+          ((int64_t)b * a.hkv + kvh) * a.block_size + kb % a.block_size;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        kreg[jj] = ld16(kg + (row0 + jj) * row_elems);
-        vreg[jj] = ld16(vg + (row0 + jj) * row_elems);
+        kreg[jj] = ld16(kg + (row0 + jj) * kD);
+        vreg[jj] = ld16(vg + (row0 + jj) * kD);
       }
     } else {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int64_t row = (int64_t)s * a.seq_stride + min(key0 + jj, kv_end - 1);
-        kreg[jj] = ld16(kg + row * row_elems);
-        vreg[jj] = ld16(vg + row * row_elems);
+        const int64_t row = ((int64_t)s * a.hkv + kvh) * a.seq_stride +
+                            min(key0 + jj, kv_end - 1);
+        kreg[jj] = ld16(kg + row * kD);
+        vreg[jj] = ld16(vg + row * kD);
       }
     }
   };
@@ -313,19 +315,18 @@ __global__ __launch_bounds__(kWave) void prefill_generic_kernel(PrefillArgs a) {
     qv[k] = d < D ? to_f32<T>(qp[d]) : 0.f;
     acc[k] = 0.f;
   }
-  const int64_t row_elems = (int64_t)a.hkv * D;
   float m_run = -INFINITY, l = 0.f;
   for (int p = 0; p < nvis; ++p) {
-    int64_t row;
+    int64_t row;  // head row of (key p, KV head g)
     if (PAGED) {
       int b = a.bt[(int64_t)s * a.bt_stride + p / a.block_size];
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      row = (int64_t)b * a.block_size + p % a.block_size;
+      row = ((int64_t)b * a.hkv + g) * a.block_size + p % a.block_size;
     } else {
-      row = (int64_t)s * a.seq_stride + p;
+      row = ((int64_t)s * a.hkv + g) * a.seq_stride + p;
     }
-    const T* kp = (const T*)a.k + row * row_elems + (int64_t)g * D;
-    const T* vp = (const T*)a.v + row * row_elems + (int64_t)g * D;
+    const T* kp = (const T*)a.k + row * D;
+    const T* vp = (const T*)a.v + row * D;
     float dot = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -365,8 +366,9 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
                     a.num_seqs, a.hq, a.hkv, a.head_dim);
   if (paged && (a.block_size <= 0 || a.bt_stride <= 0 || a.num_blocks <= 0))
     return kvp_fail(KV_EINVAL, "%s: bad paging arguments", name);
-  if (paged && (int64_t)a.num_blocks * a.block_size > INT32_MAX)
-    return kvp_fail(KV_EUNSUPPORTED, "%s: pool of more than 2^31 slots", name);
+  if (paged && (int64_t)a.num_blocks * a.block_size * a.hkv > INT32_MAX)
+    return kvp_fail(KV_EUNSUPPORTED, "%s: pool of more than 2^31 head rows",
+                    name);
   if (!paged && a.seq_stride <= 0)
     return kvp_fail(KV_EINVAL, "%s: seq_stride must be > 0", name);
   if (a.num_seqs == 0 || a.max_q_len == 0) return KV_OK;

@@ -57,7 +57,7 @@ SIGNATURES = {
     "kv_slot_mapping": (_I32, [_PI32, _I32, _PI32, _PI32, _I32, _I32,
                                _PI64]),
     "kv_reshape_and_cache": (_I32, [_P, _P, _P, _I32, _P, _P, _I64, _I32,
-                                    _I32, _I32, _P]),
+                                    _I32, _I32, _I32, _P]),
     "kv_copy_blocks": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                               _I32, _P]),
     "kv_decode_partition": (_I32, [_I32, _I32, _I32, _I32]),
@@ -292,19 +292,23 @@ def _stream(stream=None):
 
 
 def kv_reshape_and_cache(k, v, slots, k_cache, v_cache, stream=None) -> None:
+    """k, v [T, Hkv, D]; caches [blocks, Hkv, block_size, D] (paged) or
+    [S, Hkv, seq_stride, D] (contiguous; slot = s * seq_stride + pos)."""
     torch = _torch()
     n, hkv, d = k.shape
-    num_slots = k_cache.numel() // (hkv * d)
+    nb, chkv, bs, cd = k_cache.shape
+    if (chkv, cd) != (hkv, d):
+        raise ValueError("cache and rows disagree on Hkv or head_dim")
     st = lib().kv_reshape_and_cache(
         _dev(k, "k"), _dev(v, "v", k.dtype), _dev(slots, "slots", torch.int64),
         n, _dev(k_cache, "k_cache", k.dtype), _dev(v_cache, "v_cache", k.dtype),
-        num_slots, hkv, d, _dtype_code(k), _stream(stream))
+        nb * bs, bs, hkv, d, _dtype_code(k), _stream(stream))
     _check(st, "kv_reshape_and_cache")
 
 
 def kv_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
     torch = _torch()
-    nb, bs, hkv, d = k_cache.shape
+    nb, hkv, bs, d = k_cache.shape
     st = lib().kv_copy_blocks(
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
         _dev(src_dst, "src_dst", torch.int32), src_dst.shape[0], nb, bs, hkv,
@@ -339,7 +343,7 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                       stream=None) -> None:
     torch = _torch()
     S, hq, d = q.shape
-    nb, bs, hkv, _ = k_cache.shape
+    nb, hkv, bs, _ = k_cache.shape
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
     st = lib().paged_attn_decode(
@@ -356,7 +360,7 @@ def contig_attn_decode(out, q, k, v, context_lens, max_context: int,
                        scale: float, workspace=None, stream=None) -> None:
     torch = _torch()
     S, hq, d = q.shape
-    _, lmax, hkv, _ = k.shape
+    _, hkv, lmax, _ = k.shape
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
     st = lib().contig_attn_decode(
@@ -373,7 +377,7 @@ def paged_attn_prefill(out, q, cu_q_lens, q_start_pos, max_q_len: int,
                        scale: float, causal: bool = True, stream=None) -> None:
     torch = _torch()
     T, hq, d = q.shape
-    nb, bs, hkv, _ = k_cache.shape
+    nb, hkv, bs, _ = k_cache.shape
     S = cu_q_lens.shape[0] - 1
     st = lib().paged_attn_prefill(
         _dev(out, "out", q.dtype), _dev(q, "q"),
@@ -393,7 +397,7 @@ def contig_attn_prefill(out, q, cu_q_lens, q_start_pos, max_q_len: int, k, v,
     torch = _torch()
     T, hq, d = q.shape
     S = cu_q_lens.shape[0] - 1
-    _, lmax, hkv, _ = k.shape
+    _, hkv, lmax, _ = k.shape
     if k.shape[0] < S:
         raise ValueError("k holds fewer sequences than cu_q_lens describes")
     st = lib().contig_attn_prefill(

@@ -20,7 +20,7 @@ def _fill(inp, B, cap, dev):
     slots, pairs = pool.seq_append(tables, lens, inp.lengths.astype(np.int32))
     assert len(pairs) == 0
     tdt = W.torch_dtype(w.dtype)
-    kc = torch.full((len(inp.free_order), B, w.num_kv_heads, w.head_dim),
+    kc = torch.full((len(inp.free_order), w.num_kv_heads, B, w.head_dim),
                     float("nan"), dtype=tdt, device=dev)
     vc = torch.full_like(kc, float("nan"))
     kv.kv_reshape_and_cache(inp.k.to(dev), inp.v.to(dev),
@@ -50,11 +50,14 @@ def run() -> None:
         for s in range(S):
             if mt[s] != tables[s, :len(mt[s])].tolist():
                 raise AssertionError("allocation differs from the oracle")
-        kp = np.full(tuple(kc.shape), np.nan, dtype=np.float32)
+        n_pool = len(inp.free_order)
+        kp = np.full((n_pool, B, w.num_kv_heads, w.head_dim), np.nan,
+                     dtype=np.float32)
         vp = np.full_like(kp, np.nan)
         O.scatter_rows(kp, inp.k.float().numpy(), mslots)
         O.scatter_rows(vp, inp.v.float().numpy(), mslots)
-        if not np.array_equal(kc.float().cpu().numpy(), kp, equal_nan=True):
+        got = kc.permute(0, 2, 1, 3).float().cpu().numpy()
+        if not np.array_equal(got, kp, equal_nan=True):
             raise AssertionError("cache write differs from the oracle")
         q = inp.q.to(dev)
         out = torch.empty_like(q)
@@ -80,7 +83,8 @@ def run() -> None:
     mp = A.ModelPool(len(inp.free_order), B, inp.free_order)
     mt, ml = [[], []], [0, 0]
     st, mslots, _ = A.append_tokens(mp, mt, ml, inp.lengths.tolist(), cap)
-    kp = np.full(tuple(kc.shape), np.nan, dtype=np.float32)
+    kp = np.full((len(inp.free_order), B, w.num_kv_heads, w.head_dim), np.nan,
+                 dtype=np.float32)
     vp = np.full_like(kp, np.nan)
     O.scatter_rows(kp, inp.k.float().numpy(), mslots)
     O.scatter_rows(vp, inp.v.float().numpy(), mslots)

@@ -41,7 +41,7 @@ class NativeSide:
     pool: kv.KVPool
     tables: np.ndarray      # host int32 [S, cap]
     lens: np.ndarray        # host int32 [S]
-    k_cache: torch.Tensor   # device [N, B, Hkv, D]
+    k_cache: torch.Tensor   # device [N, Hkv, B, D] (head-major storage)
     v_cache: torch.Tensor
     bt: torch.Tensor        # device int32 [S, cap]
     ctx: torch.Tensor       # device int32 [S]
@@ -52,7 +52,7 @@ class OracleSide:
     pool: A.ModelPool
     tables: list
     lens: list
-    k_pool: np.ndarray      # float32 [N, B, Hkv, D], NaN where unused
+    k_pool: np.ndarray      # float32 [N, B, Hkv, D] (logical), NaN where unused
     v_pool: np.ndarray
 
 
@@ -82,7 +82,7 @@ def build_native(inp: W.Inputs, B: int, cap: int, device="cuda",
     tables = np.full((S, cap), -1, dtype=np.int32)
     lens = np.zeros(S, dtype=np.int32)
     tdt = W.torch_dtype(w.dtype)
-    k_cache = torch.full((n_pool, B, w.num_kv_heads, w.head_dim), float("nan"),
+    k_cache = torch.full((n_pool, w.num_kv_heads, B, w.head_dim), float("nan"),
                          dtype=tdt, device=device)
     v_cache = torch.full_like(k_cache, float("nan"))
 
@@ -157,19 +157,25 @@ def build_oracle(inp: W.Inputs, B: int, upto=None) -> OracleSide:
 
 
 def contig_from_inputs(inp: W.Inputs, lmax: int, device="cuda"):
-    """The contiguous layout [S, lmax, Hkv, D] of the same logical data,
+    """The contiguous layout [S, Hkv, lmax, D] of the same logical data,
     unused tail rows NaN."""
     w = inp.workload
     S = w.num_seqs
     tdt = W.torch_dtype(w.dtype)
-    k = torch.full((S, lmax, w.num_kv_heads, w.head_dim), float("nan"),
+    k = torch.full((S, w.num_kv_heads, lmax, w.head_dim), float("nan"),
                    dtype=tdt, device=device)
     v = torch.full_like(k, float("nan"))
     for s in range(S):
         rows = torch.from_numpy(rows_in_logical_order(inp, s))
-        k[s, :len(rows)] = inp.k[rows].to(device)
-        v[s, :len(rows)] = inp.v[rows].to(device)
+        k[s, :, :len(rows)] = inp.k[rows].to(device).transpose(0, 1)
+        v[s, :, :len(rows)] = inp.v[rows].to(device).transpose(0, 1)
     return k, v
+
+
+def logical_pool(cache: torch.Tensor) -> np.ndarray:
+    """A device cache [N, Hkv, B, D] viewed as the oracle's [N, B, Hkv, D],
+    as float32 on the host."""
+    return cache.permute(0, 2, 1, 3).float().cpu().numpy()
 
 
 def scale_of(w: W.Workload) -> float:

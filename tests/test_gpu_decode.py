@@ -82,8 +82,7 @@ def test_reshape_and_cache_bit_exact(case):
         assert nat.tables[s, :len(orc.tables[s])].tolist() == orc.tables[s]
     assert nat.lens.tolist() == orc.lens
     for dev, ref in ((nat.k_cache, orc.k_pool), (nat.v_cache, orc.v_pool)):
-        got = dev.float().cpu().numpy()
-        assert np.array_equal(got, ref, equal_nan=True)
+        assert np.array_equal(H.logical_pool(dev), ref, equal_nan=True)
 
 
 def test_copy_blocks_bit_exact():
@@ -99,12 +98,12 @@ def test_copy_blocks_bit_exact():
     kv.kv_copy_blocks(nat.k_cache, nat.v_cache,
                       torch.from_numpy(pairs).cuda())
     torch.cuda.synchronize()
-    ref_k = before_k.cpu().numpy()
-    ref_v = before_v.cpu().numpy()
+    ref_k = H.logical_pool(before_k)
+    ref_v = H.logical_pool(before_v)
     O.copy_blocks(ref_k, pairs[:3])
     O.copy_blocks(ref_v, pairs[:3])
-    assert np.array_equal(nat.k_cache.cpu().numpy(), ref_k, equal_nan=True)
-    assert np.array_equal(nat.v_cache.cpu().numpy(), ref_v, equal_nan=True)
+    assert np.array_equal(H.logical_pool(nat.k_cache), ref_k, equal_nan=True)
+    assert np.array_equal(H.logical_pool(nat.v_cache), ref_v, equal_nan=True)
 
 
 # ----------------------------------------------------------------- decode --
@@ -212,9 +211,9 @@ def test_decode_step_with_copy_on_write():
     O.scatter_rows(orc.k_pool, inp.k[rows].float().numpy(), oslots)
     O.scatter_rows(orc.v_pool, inp.v[rows].float().numpy(), oslots)
     torch.cuda.synchronize()
-    assert np.array_equal(nat.k_cache.float().cpu().numpy(), orc.k_pool,
+    assert np.array_equal(H.logical_pool(nat.k_cache), orc.k_pool,
                           equal_nan=True)
-    assert np.array_equal(nat.v_cache.float().cpu().numpy(), orc.v_pool,
+    assert np.array_equal(H.logical_pool(nat.v_cache), orc.v_pool,
                           equal_nan=True)
     seqs = [0, 1, 128, 254, 255]
     outs, want = _decode_both(inp, nat, orc, ctx, seqs=seqs, contig=False)
