@@ -174,17 +174,19 @@ kv_status kv_copy_blocks(void* k_cache, void* v_cache,
  * [step 4 of "PagedAttention Nasıl Çalışır?"; the kernel-side table read
  * described in "İddia ve Gerçeklik" of the vAttention newsletter].
  *
- * Long contexts are split into partitions of kv_decode_partition() tokens
- * whose partial softmax results are merged exactly; the workspace holds
- * the partials. kv_decode_workspace_bytes() gives the size needed for the
- * given shape (0 when no partition can be split); pass at least that.
- * max_context bounds every context_lens[s] (larger values are clamped to
- * it, and to bt_stride * block_size for the paged layout). Table entries
- * outside [0, num_blocks) are clamped into range, which keeps memory
- * accesses in bounds but makes that output meaningless. context_lens[s]
- * == 0 gives a zero output row. */
-int32_t kv_decode_partition(int32_t num_seqs, int32_t num_q_heads,
-                            int32_t num_kv_heads, int32_t max_context);
+ * The work is balanced across the GPU independently of the length mix: per
+ * KV head, the tokens of all sequences are laid end to end and cut into
+ * kv_decode_chunks() equal chunks, one workgroup each; a sequence cut by a
+ * chunk boundary leaves partial softmax results that a second kernel merges
+ * exactly. The workspace holds those partials;
+ * kv_decode_workspace_bytes() gives the size needed (0 when the kernel for
+ * the shape needs none). max_context bounds every context_lens[s] (larger
+ * values are clamped to it, and to bt_stride * block_size for the paged
+ * layout). Table entries outside [0, num_blocks) are clamped into range,
+ * which keeps memory accesses in bounds but makes that output meaningless.
+ * context_lens[s] == 0 gives a zero output row. Calls sharing one
+ * workspace must be ordered (same stream). */
+int32_t kv_decode_chunks(int32_t num_q_heads, int32_t num_kv_heads);
 size_t kv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_context);

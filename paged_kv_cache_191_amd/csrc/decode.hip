@@ -5,32 +5,38 @@
 // (bitcanli.com), "PagedAttention Nasıl Çalışır?", step 4]. The vAttention
 // newsletter ("İddia ve Gerçeklik") locates the cost of paging in this
 // loop: a table read per block, extra branching, and registers holding page
-// indices; the contiguous variant reads a plain [S, Lmax, Hkv, D] buffer.
-// Both variants below share one kernel body; only the row addressing
-// differs, so their timing difference is the table lookup.
+// indices; the contiguous variant reads a plain [S, Hkv, Lmax, D] buffer.
+// Both variants share one kernel body; only the row addressing differs, so
+// their timing difference is the table lookup.
 //
 // Fast path (bf16, head_dim 128, block_size % 16 == 0, any GQA group):
-//   * A workgroup owns one (sequence, KV head, head block of <= 16 query
-//     heads, partition of `part` tokens); its 4 waves split the partition.
-//     All query heads of a KV head are packed into one MFMA so each K/V byte
-//     is read once from HBM.
+//   * Balanced split ("stream-K"): per KV head, the tokens of all sequences
+//     are laid end to end and cut into n_chunks equal chunks; workgroup
+//     (unit, chunk) streams one chunk. Every workgroup moves the same bytes
+//     whatever the length mix. The chunk size is derived on the device from
+//     the context lengths, so the grid needs no host-side sums.
+//   * A chunk covers pieces ("segments") of one or more sequences. The 4
+//     waves of the workgroup share each segment tile by tile, then merge
+//     their softmax states through LDS. A segment that is a whole sequence
+//     writes the output; a cut sequence leaves a partial (max, sum,
+//     unnormalised output) that decode_combine_kernel merges exactly.
+//   * All query heads of a KV head (up to 16) share one MFMA column block,
+//     so each K/V byte is read once from HBM.
 //   * Per 32-token tile a wave computes S^T = K Q^T with
 //     v_mfma_f32_16x16x32_bf16 (tokens x heads), an online softmax in the
-//     log2 domain, and O^T += V^T P^T with the same MFMA (d x heads).
-//   * K is loaded straight into the MFMA A-operand layout (each lane 16 B
-//     of one token row). V is loaded as whole 256-byte token rows (16 lanes
-//     per row, fully coalesced) and transposed inside each lane's registers
-//     with v_perm_b32: the k (token) order of the PV product is chosen to be
-//     the order in which the S^T product leaves P in registers, so P never
-//     moves between lanes.
-//   * Block ids of the wave's range are fetched once (one lane per 16-token
-//     group) and broadcast with v_readlane, so each half-tile's base address
-//     is wave-uniform.
-//   * Masked tokens (past the context or the wave's range) are selected out
-//     (score -> -inf, V -> 0), never multiplied by 0, so NaN in unused slots
-//     cannot leak.
-//   * Partitions of one (sequence, head) are merged exactly by
-//     decode_combine_kernel using (max, sum, unnormalised output).
+//     log2 domain with lazy rescaling, and O^T += V^T P^T with the same MFMA.
+//   * K is loaded straight into the MFMA A-operand layout (each lane 16 B of
+//     one token row). V is loaded as whole 256-byte head rows (16 lanes per
+//     row) and transposed inside each lane's registers with v_perm_b32: the
+//     token order of the PV product is the order in which S^T leaves P in
+//     registers, so P never moves between lanes. K/V loads are non-temporal
+//     (read once).
+//   * Head-row bases of a wave's 16-token groups are fetched once per
+//     segment (one lane per group) and broadcast with v_readlane, so each
+//     half-tile's address is wave-uniform.
+//   * Tiles are 32-aligned in sequence positions (16-token groups never
+//     straddle a block); tokens outside the segment are selected out (score
+//     -inf, V 0), never multiplied by 0, so NaN in unused slots cannot leak.
 // Generic path (fp32, or shapes the fast path does not cover): one wave per
 // (sequence, query head), lanes over head_dim, tokens in order.
 
@@ -42,10 +48,12 @@ namespace {
 
 using namespace kvp;
 
-constexpr int kD = 128;      // head_dim of the MFMA path
-constexpr int kWaves = 4;    // waves per workgroup in the MFMA path
-constexpr int kTile = 32;    // tokens per wave iteration
-constexpr int kHeadBlk = 16; // query heads per MFMA column block
+constexpr int kD = 128;       // head_dim of the MFMA path
+constexpr int kWaves = 4;     // waves per workgroup in the MFMA path
+constexpr int kTile = 32;     // tokens per wave iteration
+constexpr int kHeadBlk = 16;  // query heads per MFMA column block
+constexpr int kMaxSeqs = 4096;  // sequences per launch of the MFMA path
+constexpr int kGroupsPerLoad = 64;  // 16-token groups prefetched per wave
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 
 struct DecodeArgs {
@@ -67,10 +75,10 @@ struct DecodeArgs {
   int32_t head_blocks;  // ceil(group / 16)
   int32_t head_dim;
   float scale_log2;     // scale * log2(e)
-  int32_t part;         // tokens per partition (multiple of kWaves * kTile)
-  int32_t max_parts;    // partition slots per (seq, head) in the workspace
-  float* ws_o;          // [S, Hq, max_parts, D] unnormalised partial outputs
-  float* ws_ml;         // [S, Hq, max_parts, 2] (max, sum) per partial
+  int32_t n_chunks;     // chunks per (KV head, head block)
+  float* ws_o;          // [n_chunks, 2, Hq, D] unnormalised partial outputs
+  float* ws_ml;         // [n_chunks, 2, Hq, 2] (reference max, sum)
+  int32_t* ws_cs;       // [S + 1] token offsets of the sequences
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
@@ -87,285 +95,341 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
   return c;
 }
 
+// Tokens per chunk for T tokens in total: T / n_chunks rounded up to 64.
+__device__ __forceinline__ int chunk_tokens(int total, int n_chunks) {
+  const int c = (total + n_chunks - 1) / n_chunks;
+  return c <= 64 ? 64 : ((c + 63) & ~63);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA fast path
 // ---------------------------------------------------------------------------
 template <bool PAGED>
-__global__ __launch_bounds__(kWaves * kWave) void decode_mfma_kernel(
+__global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     DecodeArgs a) {
-  // KV heads vary fastest across consecutive workgroups, so the workgroups
-  // of one partition run together and read whole token rows (all heads).
-  const int hblk = blockIdx.x % a.head_blocks;
-  const int g = blockIdx.x / a.head_blocks;
-  const int part_idx = blockIdx.y;
-  const int s = blockIdx.z;
-  const int ctx = clamp_ctx(a, s, PAGED);
-  const int nparts = ctx > 0 ? (ctx + a.part - 1) / a.part : 1;
-  if (part_idx >= nparts) return;
+  __shared__ int s_cs[kMaxSeqs + 1];
+  __shared__ int s_part[kWaves * kWave];
+  __shared__ float sm_o[kWaves][kHeadBlk][kD];
+  __shared__ float sm_ml[kWaves][kHeadBlk][2];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int grp = lane >> 4;
+  // KV heads vary fastest across consecutive workgroups, so the workgroups
+  // of one chunk run together.
+  const int hblk = blockIdx.x % a.head_blocks;
+  const int g = blockIdx.x / a.head_blocks;
+  const int chunk = blockIdx.y;
+  const int S = a.num_seqs;
 
-  const int t_begin = part_idx * a.part;
-  const int t_end = min(ctx, t_begin + a.part);
-  const int per_wave = a.part / kWaves;
-  const int w0 = t_begin + w * per_wave;
-  const int w1 = min(t_end, w0 + per_wave);
+  // --- token offsets of the sequences (exclusive scan of the lengths) ---
+  {
+    const int per = (S + kWaves * kWave - 1) / (kWaves * kWave);
+    const int lo = tid * per;
+    const int hi = min(S, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += clamp_ctx(a, i, PAGED);
+    s_part[tid] = sum;
+    __syncthreads();
+    // inclusive Hillis-Steele scan of the 256 partial sums
+    for (int o = 1; o < kWaves * kWave; o <<= 1) {
+      const int add = tid >= o ? s_part[tid - o] : 0;
+      __syncthreads();
+      s_part[tid] += add;
+      __syncthreads();
+    }
+    int run = s_part[tid] - sum;
+    for (int i = lo; i < hi; ++i) {
+      s_cs[i] = run;
+      run += clamp_ctx(a, i, PAGED);
+    }
+    if (tid == kWaves * kWave - 1) s_cs[S] = s_part[tid];
+    __syncthreads();
+  }
+  const int total = s_cs[S];
+  if (blockIdx.x == 0 && chunk == 0)
+    for (int i = tid; i <= S; i += kWaves * kWave) a.ws_cs[i] = s_cs[i];
+  const int C = chunk_tokens(total, a.n_chunks);
+  const int c0 = chunk * C;
+  if (c0 >= total) return;
+  const int c1 = min(total, c0 + C);
+
+  // sequence holding token c0: largest s with s_cs[s] <= c0
+  int s = 0;
+  {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_cs[mid] <= c0) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+  }
 
   const int h_in_group = hblk * kHeadBlk + r16;
   const bool h_valid = h_in_group < a.group;
-  const int qh = g * a.group + (h_valid ? h_in_group : 0);
-
-  // Q^T as the B operand of S^T = K Q^T: lane holds head r16, d = 32i+8grp+e.
-  bf16x8 qop[4];
-  {
-    const bf16* qp = (const bf16*)a.q + ((int64_t)s * a.hq + qh) * kD + 8 * grp;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 raw = ld16(qp + 32 * i);
-      if (!h_valid) raw = u32x4{0, 0, 0, 0};
-      qop[i] = as_bf16x8(raw);
-    }
-  }
-
-  float m_run = -INFINITY;  // running max (log2 domain) of head r16
-  float l_part = 0.f;       // this lane's share of the softmax denominator
-  f32x4 o[8];               // O^T: o[m][r] = O[head r16][32 grp + 8 r + m]
-#pragma unroll
-  for (int m = 0; m < 8; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Head rows of D elements: head g of token `off` in block b is row
-  // (b * Hkv + g) * block_size + off (contiguous: (s * Hkv + g) * stride +
-  // position), so one head's tokens of a block are contiguous.
+  const int nh = min(kHeadBlk, a.group - hblk * kHeadBlk);
   const bf16* kbase = (const bf16*)a.k;
   const bf16* vbase = (const bf16*)a.v;
 
-  // Head row of the first token of every 16-token group of this wave's
-  // range, one group per lane (the range holds at most 64 groups).
-  // 16-token groups never straddle a block (block_size % 16 == 0 and w0 is
-  // a multiple of 32), so a group's rows are row .. row + 15.
-  int row_lane = 0;
-  if (PAGED && w0 < w1) {
-    const int ngroups = (w1 - w0 + 15) >> 4;
-    if (lane < ngroups) {
-      const int pos = w0 + 16 * lane;
-      int b = a.bt[(int64_t)s * a.bt_stride + pos / a.block_size];
-      b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      row_lane = (b * a.hkv + g) * a.block_size + pos % a.block_size;
-    }
-  }
-  // Last 16-token group that holds a valid token; groups past it re-read it
-  // (in bounds) and are masked.
-  const int last_grp = w1 > w0 ? ((w1 - 1 - w0) >> 4) : 0;
-  const int64_t seq_row0 = ((int64_t)s * a.hkv + g) * a.seq_stride;
+  for (int pos = c0; pos < c1; ++s) {
+    const int seq_lo = s_cs[s];
+    const int L = s_cs[s + 1] - seq_lo;
+    if (L == 0) continue;
+    // segment [lo, hi) in sequence positions
+    const int lo = pos - seq_lo;
+    const int hi = min(c1 - seq_lo, L);
+    pos = seq_lo + hi;
 
-  // Row of the token `off` places after the start of group gi. Contiguous
-  // rows are clamped to the last valid token so that a ragged tail never
-  // reads past the sequence (masked afterwards).
-  auto row_of = [&](int gi, int off) -> int64_t {
-    gi = gi > last_grp ? last_grp : gi;
-    if (PAGED) return (int64_t)__builtin_amdgcn_readlane(row_lane, gi) + off;
-    const int pos = min(w0 + 16 * gi + off, w1 - 1);
-    return seq_row0 + pos;
-  };
-
-  for (int t = w0; t < w1; t += kTile) {
-    const int gi0 = (t - w0) >> 4;
-    // K: A operand of S^T (token r16 of each half, d = 32 i + 8 grp + e).
-    u32x4 kr[2][4];
+    const int qh = g * a.group + (h_valid ? h_in_group : 0);
+    bf16x8 qop[4];  // Q^T: B operand, head r16, d = 32 i + 8 grp + e
+    {
+      const bf16* qp =
+          (const bf16*)a.q + ((int64_t)s * a.hq + qh) * kD + 8 * grp;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const bf16* kp = kbase + row_of(gi0 + hf, r16) * kD + 8 * grp;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kr[hf][i] = ld16_stream(kp + 32 * i);
-    }
-    // V: token rows tau(grp, e) = 16 (e / 4) + 4 grp + e % 4, d-chunk r16.
-    u32x4 vr[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bf16* vp =
-          vbase + row_of(gi0 + (e >> 2), 4 * grp + (e & 3)) * kD + 8 * r16;
-      vr[e] = ld16_stream(vp);
-    }
-
-    // S^T = K Q^T, two 16-token halves.
-    f32x4 sc[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sc[hf] = mfma16(as_bf16x8(kr[hf][i]), qop[i], sc[hf]);
-    }
-
-    // Scores in the log2 domain; tokens past the wave's range -> -inf.
-    const bool full = (t + kTile) <= w1;
-    float x[2][4];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = sc[hf][r] * a.scale_log2;
-        const int pos = t + 16 * hf + 4 * grp + r;
-        x[hf][r] = (full || pos < w1) ? v : -INFINITY;
-      }
-    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy rescaling: the reference max only moves when a score exceeds it
-    // by more than 2^8, so p <= 256 and most tiles skip the O rescale. The
-    // final division by l makes the result independent of the reference.
-    if (__any(mx > m_run + kRescaleLog2)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_part *= alpha;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) o[m] *= alpha;
-    }
-    float p[2][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[hf][r] = fast_exp2(x[hf][r] - m_run);
-        psum += p[hf][r];
-      }
-    l_part += psum;
-
-    // P^T as the B operand of O^T += V^T P^T: k-slot e <-> token tau(grp, e).
-    u32x4 pb;
-    pb[0] = pack_bf16(p[0][0], p[0][1]);
-    pb[1] = pack_bf16(p[0][2], p[0][3]);
-    pb[2] = pack_bf16(p[1][0], p[1][1]);
-    pb[3] = pack_bf16(p[1][2], p[1][3]);
-    const bf16x8 pop = as_bf16x8(pb);
-
-    if (!full) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int pos = t + 16 * (e >> 2) + 4 * grp + (e & 3);
-        if (pos >= w1) vr[e] = u32x4{0, 0, 0, 0};
+      for (int i = 0; i < 4; ++i) {
+        u32x4 raw = ld16(qp + 32 * i);
+        if (!h_valid) raw = u32x4{0, 0, 0, 0};
+        qop[i] = as_bf16x8(raw);
       }
     }
-    // V^T rows d = 8 r16 + m: element e of A_m is V[tau(grp, e)][8 r16 + m].
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      u32x4 am;
-      const int wd = m >> 1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        am[j] = (m & 1) ? pick_hi(vr[2 * j][wd], vr[2 * j + 1][wd])
-                        : pick_lo(vr[2 * j][wd], vr[2 * j + 1][wd]);
-      o[m] = mfma16(as_bf16x8(am), pop, o[m]);
-    }
-  }
 
-  // Denominator of head r16: sum over the four lane groups.
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
+    float m_run = -INFINITY;  // reference max (log2 domain) of head r16
+    float l_part = 0.f;       // this lane's share of the denominator
+    f32x4 o[8];               // O^T: o[m][r] = O[head r16][32 grp + 8 r + m]
+#pragma unroll
+    for (int m = 0; m < 8; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Merge the waves' partial results through LDS.
-  __shared__ float sm_o[kWaves][kHeadBlk][kD];
-  __shared__ float sm_ml[kWaves][kHeadBlk][2];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float* dst = &sm_o[w][r16][32 * grp + 8 * r];
-    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0][r], o[1][r], o[2][r], o[3][r]};
-    *reinterpret_cast<f32x4*>(dst + 4) =
-        f32x4{o[4][r], o[5][r], o[6][r], o[7][r]};
-  }
-  if (grp == 0) {
-    sm_ml[w][r16][0] = m_run;
-    sm_ml[w][r16][1] = l_part;
-  }
-  __syncthreads();
+    // 32-aligned tiles covering [lo, hi); wave w takes tiles w, w+4, ...
+    const int t_al = lo & ~(kTile - 1);
+    const int n_tiles = (hi - t_al + kTile - 1) / kTile;
+    const int last_grp_pos = (hi - 1) & ~15;  // start of the last valid group
+    const int64_t seq_row0 = ((int64_t)s * a.hkv + g) * a.seq_stride;
 
-  const int nh = min(kHeadBlk, a.group - hblk * kHeadBlk);
-  for (int it = tid; it < kHeadBlk * (kD / 8); it += kWaves * kWave) {
-    const int h = it / (kD / 8);
-    const int c = it % (kD / 8);
-    if (h >= nh) continue;
-    float M = -INFINITY;
+    for (int kb0 = 0; kb0 < n_tiles; kb0 += kWaves * (kGroupsPerLoad / 2)) {
+      // head row of each 16-token group of this wave's next tiles
+      int row_lane = 0;
+      if (PAGED) {
+        const int k = kb0 + w + kWaves * (lane >> 1);
+        int gpos = t_al + kTile * k + 16 * (lane & 1);
+        gpos = min(gpos, last_grp_pos);
+        int b = a.bt[(int64_t)s * a.bt_stride + gpos / a.block_size];
+        b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+        row_lane = (b * a.hkv + g) * a.block_size + gpos % a.block_size;
+      }
+      // Head row of token `off` of half hf of this wave's j-th tile here.
+      auto row_of = [&](int j, int hf, int off) -> int64_t {
+        if (PAGED)
+          return (int64_t)__builtin_amdgcn_readlane(row_lane, 2 * j + hf) +
+                 off;
+        const int k = kb0 + w + kWaves * j;
+        const int p = min(t_al + kTile * k + 16 * hf + off, hi - 1);
+        return seq_row0 + p;
+      };
+      const int k_end = min(n_tiles, kb0 + kWaves * (kGroupsPerLoad / 2));
+      for (int j = 0; kb0 + w + kWaves * j < k_end; ++j) {
+        const int t = t_al + kTile * (kb0 + w + kWaves * j);
+        // K: A operand of S^T (token r16 of each half, d = 32 i + 8 grp + e)
+        u32x4 kr[2][4];
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_ml[ww][h][0]);
-    float L = 0.f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
+        for (int hf = 0; hf < 2; ++hf) {
+          const bf16* kp = kbase + row_of(j, hf, r16) * kD + 8 * grp;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float mw = sm_ml[ww][h][0];
-        if (mw == -INFINITY) continue;
-        const float cw = fast_exp2(mw - M);
-        L += cw * sm_ml[ww][h][1];
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(&sm_o[ww][h][8 * c]);
-        const f32x4 hi =
-            *reinterpret_cast<const f32x4*>(&sm_o[ww][h][8 * c + 4]);
+          for (int i = 0; i < 4; ++i) kr[hf][i] = ld16_stream(kp + 32 * i);
+        }
+        // V: rows tau(grp, e) = 16 (e / 4) + 4 grp + e % 4, d-chunk r16
+        u32x4 vr[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[j] += cw * lo[j];
-          acc[4 + j] += cw * hi[j];
+        for (int e = 0; e < 8; ++e)
+          vr[e] = ld16_stream(vbase + row_of(j, e >> 2, 4 * grp + (e & 3)) * kD +
+                              8 * r16);
+
+        f32x4 sc[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[hf] = mfma16(as_bf16x8(kr[hf][i]), qop[i], sc[hf]);
+        }
+
+        const bool full = t >= lo && t + kTile <= hi;
+        float x[2][4];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v = sc[hf][r] * a.scale_log2;
+            const int p = t + 16 * hf + 4 * grp + r;
+            x[hf][r] = (full || (p >= lo && p < hi)) ? v : -INFINITY;
+          }
+        float mx =
+            fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                  fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // Lazy rescaling: the reference max moves only when a score exceeds
+        // it by more than 2^8 (so p <= 256); the final division by the sum
+        // makes the result independent of the reference.
+        if (__any(mx > m_run + kRescaleLog2)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_part *= alpha;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) o[m] *= alpha;
+        }
+        float p[2][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[hf][r] = fast_exp2(x[hf][r] - m_run);
+            psum += p[hf][r];
+          }
+        l_part += psum;
+
+        // P^T: B operand of O^T += V^T P^T, k-slot e <-> token tau(grp, e)
+        u32x4 pb;
+        pb[0] = pack_bf16(p[0][0], p[0][1]);
+        pb[1] = pack_bf16(p[0][2], p[0][3]);
+        pb[2] = pack_bf16(p[1][0], p[1][1]);
+        pb[3] = pack_bf16(p[1][2], p[1][3]);
+        const bf16x8 pop = as_bf16x8(pb);
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int pe = t + 16 * (e >> 2) + 4 * grp + (e & 3);
+            if (pe < lo || pe >= hi) vr[e] = u32x4{0, 0, 0, 0};
+          }
+        }
+        // V^T rows d = 8 r16 + m: element e of A_m is V[tau(grp, e)][8r16+m]
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          u32x4 am;
+          const int wd = m >> 1;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            am[q4] = (m & 1) ? pick_hi(vr[2 * q4][wd], vr[2 * q4 + 1][wd])
+                             : pick_lo(vr[2 * q4][wd], vr[2 * q4 + 1][wd]);
+          o[m] = mfma16(as_bf16x8(am), pop, o[m]);
         }
       }
     }
-    const int head = g * a.group + hblk * kHeadBlk + h;
-    if (nparts == 1) {
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      u32x4 ov;
+
+    // --- merge the waves' states of this segment through LDS ---
+    l_part += __shfl_xor(l_part, 16);
+    l_part += __shfl_xor(l_part, 32);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ov[j] = pack_bf16(acc[2 * j] * inv, acc[2 * j + 1] * inv);
-      st16((bf16*)a.out + ((int64_t)s * a.hq + head) * kD + 8 * c, ov);
-    } else {
-      const int64_t slot = ((int64_t)s * a.hq + head) * a.max_parts + part_idx;
-      float* po = a.ws_o + slot * kD + 8 * c;
-      *reinterpret_cast<f32x4*>(po) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-      if (c == 0) {
-        a.ws_ml[2 * slot] = M;
-        a.ws_ml[2 * slot + 1] = L;
+    for (int r = 0; r < 4; ++r) {
+      float* dst = &sm_o[w][r16][32 * grp + 8 * r];
+      *reinterpret_cast<f32x4*>(dst) =
+          f32x4{o[0][r], o[1][r], o[2][r], o[3][r]};
+      *reinterpret_cast<f32x4*>(dst + 4) =
+          f32x4{o[4][r], o[5][r], o[6][r], o[7][r]};
+    }
+    if (grp == 0) {
+      sm_ml[w][r16][0] = m_run;
+      sm_ml[w][r16][1] = l_part;
+    }
+    __syncthreads();
+    const bool whole = lo == 0 && hi == L;
+    // slot 0: a continuation (lo > 0); slot 1: first piece of a sequence
+    // that continues in later chunks.
+    const int slot = lo > 0 ? 0 : 1;
+    for (int it = tid; it < kHeadBlk * (kD / 8); it += kWaves * kWave) {
+      const int h = it / (kD / 8);
+      const int c = it % (kD / 8);
+      if (h >= nh) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_ml[ww][h][0]);
+      float Ls = 0.f;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float mw = sm_ml[ww][h][0];
+          if (mw == -INFINITY) continue;
+          const float cw = fast_exp2(mw - M);
+          Ls += cw * sm_ml[ww][h][1];
+          const f32x4 lo4 = *reinterpret_cast<const f32x4*>(&sm_o[ww][h][8 * c]);
+          const f32x4 hi4 =
+              *reinterpret_cast<const f32x4*>(&sm_o[ww][h][8 * c + 4]);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            acc[jj] += cw * lo4[jj];
+            acc[4 + jj] += cw * hi4[jj];
+          }
+        }
+      }
+      const int head = g * a.group + hblk * kHeadBlk + h;
+      if (whole) {
+        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+        u32x4 ov;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          ov[jj] = pack_bf16(acc[2 * jj] * inv, acc[2 * jj + 1] * inv);
+        st16((bf16*)a.out + ((int64_t)s * a.hq + head) * kD + 8 * c, ov);
+      } else {
+        const int64_t idx = ((int64_t)chunk * 2 + slot) * a.hq + head;
+        float* po = a.ws_o + idx * kD + 8 * c;
+        *reinterpret_cast<f32x4*>(po) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<f32x4*>(po + 4) =
+            f32x4{acc[4], acc[5], acc[6], acc[7]};
+        if (c == 0) {
+          a.ws_ml[2 * idx] = M;
+          a.ws_ml[2 * idx + 1] = Ls;
+        }
       }
     }
+    __syncthreads();
   }
 }
 
-// Exact merge of the partitions of one (sequence, query head):
-// o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i with M = max_i m_i.
-template <typename T, bool PAGED>
+// Exact merge of the partials of one (sequence, query head) that spans
+// several chunks: o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i with
+// M = max_i m_i. Also writes zeros for empty contexts.
+template <typename T>
 __global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int ctx = clamp_ctx(a, s, PAGED);
-  const int nparts = ctx > 0 ? (ctx + a.part - 1) / a.part : 1;
-  if (nparts <= 1) return;
   const int lane = threadIdx.x;
-  const int64_t base = ((int64_t)s * a.hq + h) * a.max_parts;
-  const float* ml = a.ws_ml + 2 * base;
-  // max and weighted sum over the partitions, lanes in parallel
+  const int* cs = a.ws_cs;
+  const int total = cs[a.num_seqs];
+  const int seq_lo = cs[s], seq_hi = cs[s + 1];
+  T* out = (T*)a.out + ((int64_t)s * a.hq + h) * a.head_dim;
+  if (seq_hi == seq_lo) {
+    for (int d = lane; d < a.head_dim; d += kWave) out[d] = from_f32<T>(0.f);
+    return;
+  }
+  const int C = chunk_tokens(total, a.n_chunks);
+  const int ca = seq_lo / C, cb = (seq_hi - 1) / C;
+  if (ca == cb) return;  // written whole by decode_sk_kernel
+  const int n = cb - ca + 1;
+  // partial i: chunk ca + i, slot 1 for i == 0, slot 0 after
+  auto idx_of = [&](int i) -> int64_t {
+    return ((int64_t)(ca + i) * 2 + (i == 0 ? 1 : 0)) * a.hq + h;
+  };
   float M = -INFINITY;
-  for (int i = lane; i < nparts; i += kWave) M = fmaxf(M, ml[2 * i]);
+  for (int i = lane; i < n; i += kWave) M = fmaxf(M, a.ws_ml[2 * idx_of(i)]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float L = 0.f;
-  for (int i = lane; i < nparts; i += kWave) {
-    const float mi = ml[2 * i];
-    if (mi != -INFINITY) L += fast_exp2(mi - M) * ml[2 * i + 1];
+  for (int i = lane; i < n; i += kWave) {
+    const float mi = a.ws_ml[2 * idx_of(i)];
+    if (mi != -INFINITY) L += fast_exp2(mi - M) * a.ws_ml[2 * idx_of(i) + 1];
   }
   L = wave_sum(L);
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  T* out = (T*)a.out + ((int64_t)s * a.hq + h) * a.head_dim;
-  const float* po = a.ws_o + base * a.head_dim;
   for (int d = lane; d < a.head_dim; d += kWave) {
     float acc = 0.f;
-    for (int i = 0; i < nparts; ++i) {
-      const float mi = ml[2 * i];
+    for (int i = 0; i < n; ++i) {
+      const float mi = a.ws_ml[2 * idx_of(i)];
       if (mi == -INFINITY) continue;
-      acc += fast_exp2(mi - M) * po[(int64_t)i * a.head_dim + d];
+      acc += fast_exp2(mi - M) * a.ws_o[idx_of(i) * a.head_dim + d];
     }
     out[d] = from_f32<T>(acc * inv);
   }
@@ -435,32 +499,46 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-int env_part_override() {
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int env_chunks_override() {
   static int cached = -2;
   if (cached == -2) {
-    const char* e = getenv("KVPAGED_DECODE_PART");
+    const char* e = getenv("KVPAGED_DECODE_CHUNKS");
     cached = e ? atoi(e) : 0;
   }
   return cached;
 }
 
-// Tokens per partition of the MFMA path: the largest of 4096..128 that
-// still gives at least ~2048 workgroups for the longest context.
-int choose_part(int num_seqs, int num_kv_heads, int head_blocks,
-                int max_context) {
-  const int ov = env_part_override();
-  if (ov > 0) {
-    int p = (ov + kWaves * kTile - 1) / (kWaves * kTile) * (kWaves * kTile);
-    return p > 4096 ? 4096 : p;
-  }
-  const int64_t units = (int64_t)num_seqs * num_kv_heads * head_blocks;
-  int part = 4096;
-  while (part > kWaves * kTile) {
-    const int64_t parts = (max_context + part - 1) / part;
-    if (units * parts >= 2048) break;
-    part >>= 1;
-  }
-  return part;
+// Chunks per (KV head, head block): enough workgroups for one resident
+// round (3 workgroups of 4 waves per CU), split evenly over the units.
+int choose_chunks(int num_kv_heads, int head_blocks) {
+  const int ov = env_chunks_override();
+  if (ov > 0) return ov;
+  const int units = num_kv_heads * head_blocks;
+  const int target = device_cus() * 3;
+  const int n = (target + units - 1) / units;
+  return n < 1 ? 1 : n;
+}
+
+size_t sk_workspace_bytes(int num_seqs, int hq, int n_chunks) {
+  const size_t o = (size_t)n_chunks * 2 * hq * kD * sizeof(float);
+  const size_t ml = (size_t)n_chunks * 2 * hq * 2 * sizeof(float);
+  const size_t cs = (size_t)(num_seqs + 1) * sizeof(int32_t);
+  return o + ml + cs;
 }
 
 bool fast_path_ok(kv_dtype dtype, int head_dim, int block_size, bool paged) {
@@ -493,29 +571,41 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
 
   if (fast_path_ok(dtype, a.head_dim, a.block_size, paged)) {
     a.head_blocks = (a.group + kHeadBlk - 1) / kHeadBlk;
-    a.part = choose_part(a.num_seqs, a.hkv, a.head_blocks, a.max_ctx);
-    a.max_parts = a.max_ctx > 0 ? (a.max_ctx + a.part - 1) / a.part : 1;
-    if (a.max_parts > 1) {
-      const size_t need = (size_t)a.num_seqs * a.hq * a.max_parts *
-                          (a.head_dim + 2) * sizeof(float);
-      if (!workspace || ws_bytes < need)
-        return kvp_fail(KV_EINVAL, "%s: workspace of %zu bytes needed, %zu given",
-                        name, need, ws_bytes);
-      a.ws_o = (float*)workspace;
-      a.ws_ml = a.ws_o + (size_t)a.num_seqs * a.hq * a.max_parts * a.head_dim;
-    }
-    dim3 grid(a.hkv * a.head_blocks, a.max_parts, a.num_seqs);
-    if (paged)
-      decode_mfma_kernel<true><<<grid, kWaves * kWave, 0, st>>>(a);
-    else
-      decode_mfma_kernel<false><<<grid, kWaves * kWave, 0, st>>>(a);
-    KVP_LAUNCH_CHECK(name);
-    if (a.max_parts > 1) {
-      dim3 g2(a.hq, a.num_seqs);
+    a.n_chunks = choose_chunks(a.hkv, a.head_blocks);
+    const int per_launch = a.num_seqs < kMaxSeqs ? a.num_seqs : kMaxSeqs;
+    if ((int64_t)per_launch * a.max_ctx > INT32_MAX)
+      return kvp_fail(KV_EUNSUPPORTED, "%s: more than 2^31 context tokens in "
+                      "one launch", name);
+    const size_t need = sk_workspace_bytes(per_launch, a.hq, a.n_chunks);
+    if (!workspace || ws_bytes < need)
+      return kvp_fail(KV_EINVAL, "%s: workspace of %zu bytes needed, %zu given",
+                      name, need, ws_bytes);
+    a.ws_o = (float*)workspace;
+    a.ws_ml = a.ws_o + (size_t)a.n_chunks * 2 * a.hq * kD;
+    a.ws_cs = (int32_t*)(a.ws_ml + (size_t)a.n_chunks * 2 * a.hq * 2);
+    // Batches of more than kMaxSeqs sequences run as several launches on
+    // the same stream, in order, sharing the workspace.
+    for (int s0 = 0; s0 < a.num_seqs; s0 += kMaxSeqs) {
+      DecodeArgs b = a;
+      b.num_seqs = min(kMaxSeqs, a.num_seqs - s0);
+      b.out = (bf16*)a.out + (size_t)s0 * a.hq * kD;
+      b.q = (const bf16*)a.q + (size_t)s0 * a.hq * kD;
+      b.ctx = a.ctx + s0;
+      if (paged) {
+        b.bt = a.bt + (size_t)s0 * a.bt_stride;
+      } else {
+        const size_t seq_elems = (size_t)a.hkv * a.seq_stride * kD;
+        b.k = (const bf16*)a.k + (size_t)s0 * seq_elems;
+        b.v = (const bf16*)a.v + (size_t)s0 * seq_elems;
+      }
+      dim3 grid(a.hkv * a.head_blocks, a.n_chunks);
       if (paged)
-        decode_combine_kernel<bf16, true><<<g2, kWave, 0, st>>>(a);
+        decode_sk_kernel<true><<<grid, kWaves * kWave, 0, st>>>(b);
       else
-        decode_combine_kernel<bf16, false><<<g2, kWave, 0, st>>>(a);
+        decode_sk_kernel<false><<<grid, kWaves * kWave, 0, st>>>(b);
+      KVP_LAUNCH_CHECK(name);
+      dim3 g2(a.hq, b.num_seqs);
+      decode_combine_kernel<bf16><<<g2, kWave, 0, st>>>(b);
       KVP_LAUNCH_CHECK(name);
     }
     return KV_OK;
@@ -541,14 +631,11 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
 
 }  // namespace
 
-extern "C" int32_t kv_decode_partition(int32_t num_seqs, int32_t num_q_heads,
-                                       int32_t num_kv_heads,
-                                       int32_t max_context) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      num_q_heads % num_kv_heads || max_context < 0)
+extern "C" int32_t kv_decode_chunks(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
     return KV_EINVAL;
   const int hb = (num_q_heads / num_kv_heads + kHeadBlk - 1) / kHeadBlk;
-  return choose_part(num_seqs, num_kv_heads, hb, max_context);
+  return choose_chunks(num_kv_heads, hb);
 }
 
 extern "C" size_t kv_decode_workspace_bytes(int32_t num_seqs,
@@ -556,15 +643,15 @@ extern "C" size_t kv_decode_workspace_bytes(int32_t num_seqs,
                                             int32_t num_kv_heads,
                                             int32_t head_dim,
                                             int32_t max_context) {
+  (void)max_context;
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      num_q_heads % num_kv_heads || head_dim <= 0 || max_context <= 0)
+      num_q_heads % num_kv_heads || head_dim <= 0)
     return 0;
+  if (head_dim != kD) return 0;  // the generic path needs no workspace
   const int hb = (num_q_heads / num_kv_heads + kHeadBlk - 1) / kHeadBlk;
-  const int part = choose_part(num_seqs, num_kv_heads, hb, max_context);
-  const int64_t parts = (max_context + part - 1) / part;
-  if (parts <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * parts * (head_dim + 2) *
-         sizeof(float);
+  const int n = choose_chunks(num_kv_heads, hb);
+  const int per_launch = num_seqs < kMaxSeqs ? num_seqs : kMaxSeqs;
+  return sk_workspace_bytes(per_launch, num_q_heads, n);
 }
 
 extern "C" kv_status paged_attn_decode(

@@ -60,7 +60,7 @@ SIGNATURES = {
                                     _I32, _I32, _I32, _P]),
     "kv_copy_blocks": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                               _I32, _P]),
-    "kv_decode_partition": (_I32, [_I32, _I32, _I32, _I32]),
+    "kv_decode_chunks": (_I32, [_I32, _I32]),
     "kv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "paged_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
                                  _I32, _I32, _I32, _I32, _I32, _F, _I32, _P,
@@ -316,10 +316,8 @@ def kv_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
     _check(st, "kv_copy_blocks")
 
 
-def kv_decode_partition(num_seqs, num_q_heads, num_kv_heads, max_context
-                        ) -> int:
-    return int(lib().kv_decode_partition(num_seqs, num_q_heads, num_kv_heads,
-                                         max_context))
+def kv_decode_chunks(num_q_heads, num_kv_heads) -> int:
+    return int(lib().kv_decode_chunks(num_q_heads, num_kv_heads))
 
 
 def kv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,

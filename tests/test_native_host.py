@@ -212,9 +212,10 @@ def test_pool_create_rejects_bad_order():
 
 
 def test_decode_workspace_sizes():
-    # one partition needs no workspace; long contexts do
-    assert kv.kv_decode_workspace_bytes(64, 32, 8, 128, 64) == 0
-    p = kv.kv_decode_partition(4, 56, 8, 196608)
-    assert p > 0 and p % 128 == 0
+    # partials: [chunks, 2, Hq, D + 2] fp32, plus S + 1 token offsets
+    c = kv.kv_decode_chunks(56, 8)
+    assert c >= 1
     n = kv.kv_decode_workspace_bytes(4, 56, 8, 128, 196608)
-    assert n == 4 * 56 * (-(-196608 // p)) * (128 + 2) * 4
+    assert n == c * 2 * 56 * (128 + 2) * 4 + (4 + 1) * 4
+    assert kv.kv_decode_workspace_bytes(4, 56, 8, 64, 100) == 0  # generic
+    assert kv.kv_decode_chunks(32, 5) < 0
