@@ -39,7 +39,7 @@
  *     "block" is the whole sequence).
  *   - Query head h reads KV head h / (Hq / Hkv). Attention is softmax of
  *     scale * q.k over the visible keys, accumulated in fp32; out has the
- *     dtype of q.
+ *     dtype of q. scale must be finite and > 0 (KV_EINVAL otherwise).
  *   - The allocator is single-threaded: one host thread per pool.
  */
 #ifndef KVPAGED_H

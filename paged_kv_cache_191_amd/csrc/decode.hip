@@ -389,49 +389,62 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   }
 }
 
-// Exact merge of the partials of one (sequence, query head) that spans
-// several chunks: o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i with
-// M = max_i m_i. Also writes zeros for empty contexts.
-template <typename T>
-__global__ __launch_bounds__(kWave) void decode_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int lane = threadIdx.x;
+// Exact merge of the partials of a sequence that spans several chunks:
+// o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i with M = max_i m_i, for
+// every query head. Grid (sequence, slice of 64 items); one (head, 8-wide d
+// chunk) item per thread; the pieces are folded in one pass with a running
+// max. Also writes zeros for empty contexts.
+constexpr int kCombineThreads = 64;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
+    DecodeArgs a) {
+  const int s = blockIdx.x;
   const int* cs = a.ws_cs;
   const int total = cs[a.num_seqs];
   const int seq_lo = cs[s], seq_hi = cs[s + 1];
-  T* out = (T*)a.out + ((int64_t)s * a.hq + h) * a.head_dim;
+  const int items = a.hq * (kD / 8);
+  bf16* out = (bf16*)a.out + (int64_t)s * a.hq * kD;
+  const int it = blockIdx.y * kCombineThreads + threadIdx.x;
+  if (it >= items) return;
   if (seq_hi == seq_lo) {
-    for (int d = lane; d < a.head_dim; d += kWave) out[d] = from_f32<T>(0.f);
+    st16(out + 8 * it, u32x4{0, 0, 0, 0});
     return;
   }
   const int C = chunk_tokens(total, a.n_chunks);
   const int ca = seq_lo / C, cb = (seq_hi - 1) / C;
   if (ca == cb) return;  // written whole by decode_sk_kernel
   const int n = cb - ca + 1;
-  // partial i: chunk ca + i, slot 1 for i == 0, slot 0 after
-  auto idx_of = [&](int i) -> int64_t {
-    return ((int64_t)(ca + i) * 2 + (i == 0 ? 1 : 0)) * a.hq + h;
-  };
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += kWave) M = fmaxf(M, a.ws_ml[2 * idx_of(i)]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float L = 0.f;
-  for (int i = lane; i < n; i += kWave) {
-    const float mi = a.ws_ml[2 * idx_of(i)];
-    if (mi != -INFINITY) L += fast_exp2(mi - M) * a.ws_ml[2 * idx_of(i) + 1];
-  }
-  L = wave_sum(L);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int d = lane; d < a.head_dim; d += kWave) {
-    float acc = 0.f;
+  {
+    const int h = it / (kD / 8);
+    const int c = it % (kD / 8);
+    float M = -INFINITY, L = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int i = 0; i < n; ++i) {
-      const float mi = a.ws_ml[2 * idx_of(i)];
+      // piece i: chunk ca + i; slot 1 (first piece) for i == 0, else slot 0
+      const int64_t idx = ((int64_t)(ca + i) * 2 + (i == 0 ? 1 : 0)) * a.hq + h;
+      const float mi = a.ws_ml[2 * idx];
+      const float li = a.ws_ml[2 * idx + 1];
+      const f32x4 lo4 = *reinterpret_cast<const f32x4*>(a.ws_o + idx * kD + 8 * c);
+      const f32x4 hi4 =
+          *reinterpret_cast<const f32x4*>(a.ws_o + idx * kD + 8 * c + 4);
       if (mi == -INFINITY) continue;
-      acc += fast_exp2(mi - M) * a.ws_o[idx_of(i) * a.head_dim + d];
+      const float m_new = fmaxf(M, mi);
+      const float old_scale = fast_exp2(M - m_new);
+      const float new_scale = fast_exp2(mi - m_new);
+      M = m_new;
+      L = L * old_scale + li * new_scale;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = acc[j] * old_scale + lo4[j] * new_scale;
+        acc[4 + j] = acc[4 + j] * old_scale + hi4[j] * new_scale;
+      }
     }
-    out[d] = from_f32<T>(acc * inv);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    u32x4 ov;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ov[j] = pack_bf16(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+    st16(out + 8 * it, ov);
   }
 }
 
@@ -551,6 +564,8 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
                      hipStream_t st) {
   if (dtype != KV_F32 && dtype != KV_BF16)
     return kvp_fail(KV_EINVAL, "%s: unknown dtype %d", name, (int)dtype);
+  if (!(a.scale_log2 > 0.f) || !(a.scale_log2 < INFINITY))
+    return kvp_fail(KV_EINVAL, "%s: scale must be finite and > 0", name);
   if (a.num_seqs < 0 || a.hq <= 0 || a.hkv <= 0 || a.hq % a.hkv != 0 ||
       a.head_dim <= 0 || a.max_ctx < 0)
     return kvp_fail(KV_EINVAL,
@@ -604,8 +619,9 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
       else
         decode_sk_kernel<false><<<grid, kWaves * kWave, 0, st>>>(b);
       KVP_LAUNCH_CHECK(name);
-      dim3 g2(a.hq, b.num_seqs);
-      decode_combine_kernel<bf16><<<g2, kWave, 0, st>>>(b);
+      dim3 g2(b.num_seqs, (a.hq * (kD / 8) + kCombineThreads - 1) /
+                              kCombineThreads);
+      decode_combine_kernel<<<g2, kCombineThreads, 0, st>>>(b);
       KVP_LAUNCH_CHECK(name);
     }
     return KV_OK;

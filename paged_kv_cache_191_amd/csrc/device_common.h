@@ -43,12 +43,13 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) {
 __device__ __forceinline__ float bf16_hi(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
 }
-// Round-to-nearest-even fp32 -> bf16 of two values, packed (lo, hi).
+// Round-to-nearest-even fp32 -> bf16 of two values, packed (lo, hi): one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  bf16 a = static_cast<bf16>(lo);
-  bf16 b = static_cast<bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Select the low (or high) 16-bit halves of two dwords into one dword:
@@ -58,6 +59,19 @@ __device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) {
 }
 __device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane j receives element (j & 3) of the 8-byte chunks addressed by lanes
+// (j >> 2) + 4k, k = 0..3. With lane s pointing at row r0 + (s >> 2),
+// column c0 + 4 (s & 3) of a row-major 16-bit matrix, lane j receives rows
+// r0..r0+3 of column c0 + j.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_addr) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(lds_addr));
+  return __builtin_bit_cast(u32x2, r);
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -25,6 +25,8 @@
 //     in the tiles that need them.
 // Generic path (other dtypes/shapes): one wave per (query row, head).
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace {
@@ -35,8 +37,6 @@ constexpr int kD = 128;
 constexpr int kBM = 32;            // query rows per workgroup
 constexpr int kBN = 64;            // keys per tile
 constexpr int kWaves = 4;          // = query heads per workgroup
-constexpr int kKStride = kD + 8;   // LDS row stride of the K tile (elements)
-constexpr int kVStride = kBN + 8;  // LDS row stride of the V^T tile
 
 struct PrefillArgs {
   void* out;
@@ -74,31 +74,28 @@ __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int s,
   return c;
 }
 
-// Column of key k (0..63) in the V^T tile: within each 16-key group, bits 2
-// and 3 of the key index swap, so that the 8 keys a lane feeds to one PV
-// MFMA are contiguous.
-__device__ __forceinline__ int vt_col(int k) {
-  const int k16 = k & 15;
-  return (k & ~15) | (((k16 >> 2) & 1) << 3) | ((k16 >> 3) << 2) | (k16 & 3);
+// K and V tiles in LDS: row-major [64 keys][128 d], 256-byte rows with no
+// padding; the 16-byte chunk c of row r is stored at chunk c ^ swizzle(r),
+// so that the rows read together land in distinct LDS banks:
+//   K (read by ds_read_b128, 16 rows at one chunk): swizzle = r & 15;
+//   V (read by transpose reads, 4 rows x 32-64 bytes): swizzle =
+//     {0, 6, 12, 10}[r & 3].
+__device__ __forceinline__ int k_elem(int row, int d) {
+  return row * kD + ((((d >> 3) ^ (row & 15))) << 3) + (d & 7);
 }
-// Row of head-dim index d in the V^T tile: inside each 32-row block, row
-// 8a + 4g + b holds d = 16g + 4a + b, so that the O^T accumulator of a lane
-// covers 16 contiguous d.
-__device__ __forceinline__ int vt_row(int d) {
-  const int dd = d & 31;
-  return (d & ~31) | (((dd >> 2) & 3) << 3) | ((dd >> 4) << 2) | (dd & 3);
+__device__ __forceinline__ int v_elem(int row, int d) {
+  const int swz = (0xAC60 >> (4 * (row & 3))) & 15;
+  return row * kD + ((((d >> 3) ^ swz)) << 3) + (d & 7);
 }
 
-__device__ __forceinline__ uint32_t pick16(u32x4 a, u32x4 b, int m) {
-  const uint32_t x = a[m >> 1], y = b[m >> 1];
-  return (m & 1) ? pick_hi(x, y) : pick_lo(x, y);
-}
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
 template <bool PAGED>
-__global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(
+__global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
     PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 sk[2][kBN * kKStride];
-  __shared__ __attribute__((aligned(16))) bf16 svt[2][kD * kVStride];
+  __shared__ __attribute__((aligned(16))) bf16 sk[2][kBN * kD];
+  __shared__ __attribute__((aligned(16))) bf16 sv[2][kBN * kD];
 
   const int s = blockIdx.z;
   const int qbeg = a.cu_q[s];
@@ -114,7 +111,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(
   kv_end = kv_end < 0 ? 0 : kv_end;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g2 = lane >> 5;
@@ -139,69 +136,48 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = -INFINITY, l_part = 0.f;
 
-  // Tile loader: thread tid moves keys 4n..4n+3, d-chunk 8c..8c+7.
-  const int ln = tid >> 4;
-  const int lc = tid & 15;
-  // Head rows of D elements (layout [blocks, Hkv, B, D] / [S, Hkv, L, D]).
-  const bf16* kg = (const bf16*)a.k + 8 * lc;
-  const bf16* vg = (const bf16*)a.v + 8 * lc;
-  u32x4 kreg[4], vreg[4];
-
-  auto load_tile = [&](int j) {
-    const int key0 = j * kBN + 4 * ln;
+  // Tile loader: wave w moves keys 16w..16w+15 of the tile, four rows per
+  // instruction, straight from global memory into LDS (lane i of an
+  // instruction fills 16-byte LDS unit i). Keys past the context re-read
+  // the last valid key (finite data; their scores are masked).
+  const int ld_row = lane >> 4;           // row within the 4-row group
+  const int ld_pc = lane & 15;            // physical 16-byte chunk
+  const int64_t head_row0 = (int64_t)kvh * (PAGED ? a.block_size : a.seq_stride);
+  auto load_tile = [&](int buf, int j) {
+    const int g0 = j * kBN + 16 * w;      // first key of this wave's group
+    int64_t grp_row;                       // head row of key `base`
+    int base;
     if (PAGED) {
-      // Four consecutive keys share a block; past the context, re-read the
-      // last valid group of four (in bounds, masked later).
-      const int kb = min(key0, ((kv_end - 1) >> 2) << 2);
-      int b = a.bt[(int64_t)s * a.bt_stride + kb / a.block_size];
+      base = min(g0, (kv_end - 1) & ~15);
+      int b = a.bt[(int64_t)s * a.bt_stride + base / a.block_size];
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      const int64_t row0 =
-          ((int64_t)b * a.hkv + kvh) * a.block_size + kb % a.block_size;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        kreg[jj] = ld16(kg + (row0 + jj) * kD);
-        vreg[jj] = ld16(vg + (row0 + jj) * kD);
-      }
+      grp_row = (int64_t)b * a.hkv * a.block_size + head_row0 +
+                base % a.block_size;
     } else {
+      base = 0;
+      grp_row = (int64_t)s * a.hkv * a.seq_stride + head_row0;
+    }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int64_t row = ((int64_t)s * a.hkv + kvh) * a.seq_stride +
-                            min(key0 + jj, kv_end - 1);
-        kreg[jj] = ld16(kg + row * kD);
-        vreg[jj] = ld16(vg + row * kD);
-      }
+    for (int n = 0; n < 4; ++n) {
+      const int row = 16 * w + 4 * n + ld_row;               // tile row
+      const int key = min(g0 + 4 * n + ld_row, kv_end - 1);
+      const int64_t hrow = grp_row + (key - base);
+      const int kc = ld_pc ^ (row & 15);
+      const int vc = ld_pc ^ ((0xAC60 >> (4 * (row & 3))) & 15);
+      __builtin_amdgcn_global_load_lds(
+          (gptr_t)((const bf16*)a.k + hrow * kD + 8 * kc),
+          (lptr_t)(&sk[buf][(16 * w + 4 * n) * kD]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (gptr_t)((const bf16*)a.v + hrow * kD + 8 * vc),
+          (lptr_t)(&sv[buf][(16 * w + 4 * n) * kD]), 16, 0, 0);
     }
   };
 
-  auto store_tile = [&](int buf, int j) {
-    const int key0 = j * kBN + 4 * ln;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      st16(&sk[buf][(4 * ln + jj) * kKStride + 8 * lc], kreg[jj]);
-      if (key0 + jj >= kv_end) vreg[jj] = u32x4{0, 0, 0, 0};
-    }
-    const int col = vt_col(4 * ln);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      u32x2 val;
-      val[0] = pick16(vreg[0], vreg[1], m);
-      val[1] = pick16(vreg[2], vreg[3], m);
-      *reinterpret_cast<u32x2*>(&svt[buf][vt_row(8 * lc + m) * kVStride + col]) =
-          val;
-    }
-  };
-
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
-  if (n_tiles > 0) load_tile(0);
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    store_tile(buf, j);
-    __syncthreads();
-    if (j + 1 < n_tiles) load_tile(j + 1);
-
+  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile = [&](int buf, int j, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
     const bf16* K_ = sk[buf];
-    const bf16* VT = svt[buf];
-    // S^T = K Q^T for the two 32-key halves of the tile.
+    const bf16* V_ = sv[buf];
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -210,49 +186,56 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const bf16x8 ka = as_bf16x8(
-            ld16(&K_[(32 * kb + l32) * kKStride + 16 * ks + 8 * g2]));
+            ld16(&K_[k_elem(32 * kb + l32, 16 * ks + 8 * g2)]));
         sacc[kb] = mfma32(ka, qop[ks], sacc[kb]);
       }
     }
-    // Scores (log2 domain) with the causal/context mask where needed.
+    // Raw scores; keys past the context or after the query -> -inf.
     const int tile0 = j * kBN;
-    const bool need_mask = (tile0 + kBN > kv_end) ||
-                           (a.causal && tile0 + kBN - 1 > pos_first);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb][r] * a.scale_log2;
-        if (need_mask) {
+        if (MASK) {
           const int key = tile0 + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
           const bool dead = key >= kv_end || (a.causal && key > my_pos);
-          x = dead ? -INFINITY : x;
+          sacc[kb][r] = dead ? -INFINITY : sacc[kb][r];
         }
-        sacc[kb][r] = x;
-        mx = fmaxf(mx, x);
+        mx = fmaxf(mx, sacc[kb][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    // A query row whose keys are all masked so far keeps m = -inf; use 0 as
-    // the reference so that exp2 stays finite (its p are all 0).
-    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_ref);
-    m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    // Lazy rescaling (log2 domain): the reference max moves only when a
+    // score exceeds it by more than 2^8; the final division by the sum
+    // makes the result independent of the reference. A row with no visible
+    // key yet keeps m = -inf and p = 0.
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    }
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(sacc[kb][r] - m_ref);
+        const float p = fast_exp2(__builtin_fmaf(sacc[kb][r], a.scale_log2,
+                                                 -m_ref));
         sacc[kb][r] = p;
         psum += p;
       }
-    l_part = l_part * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    l_part += psum;
 
-    // O^T += V^T P^T, 16 keys per MFMA.
+    // O^T += V^T P^T, 16 keys per MFMA. P^T (B operand): lane holds query
+    // l32, k-slot e <-> key 16 kk + 8 (e / 4) + 4 g2 + e % 4 of the tile,
+    // which is where S^T left it. V^T (A operand): two transpose reads give
+    // lane l (d = 32 db + l % 32) the same 8 keys.
+    const int trs = lane & 15;
+    const int trd = 16 * ((lane >> 4) & 1) + 4 * (trs & 3);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int kb = kk >> 1;
@@ -262,32 +245,55 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(
       for (int e = 0; e < 4; ++e)
         pb[e] = pack_bf16(sacc[kb][rb + 2 * e], sacc[kb][rb + 2 * e + 1]);
       const bf16x8 pop = as_bf16x8(pb);
+      const int r0 = 16 * kk + 4 * g2 + (trs >> 2);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8 va = as_bf16x8(
-            ld16(&VT[(32 * db + l32) * kVStride + 16 * kk + 8 * g2]));
+        const u32x2 lo = lds_read_tr16(&V_[v_elem(r0, 32 * db + trd)]);
+        const u32x2 hi = lds_read_tr16(&V_[v_elem(r0 + 8, 32 * db + trd)]);
+        const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
         oacc[db] = mfma32(va, pop, oacc[db]);
       }
     }
-  }
+  };
+
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  // Tiles below n_full need no mask: every key is in the context and at or
+  // before the first query of the block.
+  int n_full = kv_end / kBN;
+  if (a.causal) n_full = min(n_full, (pos_first + 1) / kBN);
+  // Two loops (unmasked tiles, then the boundary tiles) so that the
+  // accumulators never pass through a join inside the loop. Each iteration:
+  // wait for this tile's loads, barrier (they are visible and every wave is
+  // done with the other buffer), start the next tile's loads, compute.
+  auto run_tiles = [&](int j0, int j1, auto masked) {
+    for (int j = j0; j < j1; ++j) {
+      const int buf = j & 1;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (j + 1 < n_tiles) load_tile(buf ^ 1, j + 1);
+      tile(buf, j, masked);
+    }
+  };
+  if (n_tiles > 0) load_tile(0, 0);
+  run_tiles(0, n_full, std::false_type{});
+  run_tiles(n_full, n_tiles, std::true_type{});
 
   l_part += __shfl_xor(l_part, 32);
   if (l32 < nrows) {
     const float inv = l_part > 0.f ? 1.f / l_part : 0.f;
+    // O^T: lane holds query l32, d = 32 db + 8 (r / 4) + 4 g2 + r % 4.
     bf16* op = (bf16*)a.out + ((int64_t)(qbeg + q0 + l32) * a.hq + h) * kD +
-               16 * g2;
+               4 * g2;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      u32x4 lo, hi;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[e] = pack_bf16(oacc[db][2 * e] * inv, oacc[db][2 * e + 1] * inv);
-        hi[e] = pack_bf16(oacc[db][8 + 2 * e] * inv,
-                          oacc[db][8 + 2 * e + 1] * inv);
+      for (int a4 = 0; a4 < 4; ++a4) {
+        u32x2 v2;
+        v2[0] = pack_bf16(oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv);
+        v2[1] =
+            pack_bf16(oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * a4) = v2;
       }
-      st16(op + 32 * db, lo);
-      st16(op + 32 * db + 8, hi);
-    }
   }
 }
 
@@ -360,6 +366,8 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
                       kv_dtype dtype, hipStream_t st) {
   if (dtype != KV_F32 && dtype != KV_BF16)
     return kvp_fail(KV_EINVAL, "%s: unknown dtype %d", name, (int)dtype);
+  if (!(a.scale_log2 > 0.f) || !(a.scale_log2 < INFINITY))
+    return kvp_fail(KV_EINVAL, "%s: scale must be finite and > 0", name);
   if (a.num_seqs < 0 || a.hq <= 0 || a.hkv <= 0 || a.hq % a.hkv != 0 ||
       a.head_dim <= 0 || a.max_q_len < 0)
     return kvp_fail(KV_EINVAL, "%s: bad shape (S=%d Hq=%d Hkv=%d D=%d)", name,
