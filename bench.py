@@ -1,29 +1,46 @@
 """Benchmark of the paged-KV hot path on one MI355X.
 
-A step is one decode step of the Llama-3-8B-shaped batch (64 sequences,
-32 query / 8 KV heads, head_dim 128, bf16, block size 16, contexts uniform in
-512..4096, Q/K/V ~ N(0, 1)):
-  host   kv_seq_append: allocation when a block fills, slot mapping;
+A step is one decode step of a batch of sequences, each growing by one token:
+  host   kv_seq_append: allocation when a block fills (copy-on-write of a
+         shared, partly filled block), slot mapping;
   upload one pinned host->device copy of slots, lengths and block table;
   device kv_reshape_and_cache of the new token's K/V, paged_attn_decode
-         (partitions + exact merge).
-Each sequence grows by one token per step. Four independent replicas of the
-whole batch (pools, tables, queries) rotate so that no step finds its K/V in
-the 256 MB last-level cache.
+         (stream-K partitions + exact merge).
+Four independent replicas of the whole batch (pools, tables, queries) rotate
+so that no step finds its K/V in the 256 MB last-level cache.
 
-`value` = decode algorithmic bytes (K+V once per KV head, q, o, block table,
-lengths) summed over the timed steps / wall time of those steps.
+Workloads (--workload; shapes of the model layers the vAttention evaluation
+names, synthetic N(0, 1) bf16 values, head_dim 128):
+  llama3_8b_decode     (default) 64 sequences, 32 q / 8 kv heads, block 16,
+                       contexts uniform in 512..4096;
+  yi34b_long_decode    4 sequences of 196608 tokens, 56 q / 8 kv heads,
+                       block 64;
+  prefix_share_decode  256 sequences sharing a 4096-token prefix (256 blocks
+                       at refcount 256, written once) plus own suffixes
+                       uniform in 64..1024, 32 q / 8 kv heads, block 16; also
+                       the copy-on-write case: a 4104-token prefix whose last
+                       block is half full, so the first appended token of
+                       255 of the 256 sequences copies it.
+
+`value` = decode algorithmic bytes (K+V once per KV head, q, o, block-table
+entries, lengths) summed over the timed steps / wall time of those steps.
+With a shared prefix the prefix counts once (unique bytes); the bytes the
+sequences read logically are reported beside it as "effective" GB/s, which
+can exceed the HBM peak because the shared blocks are served from cache.
 The same JSON line carries:
   roofline     - the decode op alone (HIP events around each call on its
-                 stream) against 8 TB/s;
+                 stream) against 8 TB/s, with the HBM traffic counted by
+                 hardware counters when they were taken on these sources;
   contig       - the same steps on the contiguous layout, and the
-                 paged-vs-contiguous overhead of the decode op;
-  prefill      - one chunked-prefill pass of the Yi-6B-shaped workload (4 x
-                 32768 tokens, 2048-token chunks, 32/4 heads) per layout
-                 (paged B=16, paged B=64, contiguous): TFLOP/s of the
-                 attention calls against 2.5 PFLOP/s bf16;
+                 paged-vs-contiguous time of the decode op;
+  prefill      - (default workload) one chunked-prefill pass of the
+                 Yi-6B-shaped workload (4 x 32768 tokens, 2048-token chunks,
+                 32/4 heads) per layout (paged B=16, paged B=64, contiguous):
+                 TFLOP/s of the attention calls against 2.5 PFLOP/s bf16;
+  memory       - block-internal waste of the paged pool next to the
+                 contiguous reservation's;
   cpu_baseline - the fp64 oracle on this host's cores on the same decode
-                 workload.
+                 workload (all threads, then one).
 """
 from __future__ import annotations
 
@@ -43,35 +60,98 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = ("decode KV-read HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA "
           "peak), paged vs contig")
+DECODE_WORKLOADS = ("llama3_8b_decode", "yi34b_long_decode",
+                    "prefix_share_decode")
+COW_PREFIX = 4104
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def decode_bytes(lens: np.ndarray, hq: int, hkv: int, d: int, B: int,
-                 paged: bool, esize: int = 2) -> int:
+TRAFFIC_PROFILES = {
+    "llama3_8b_decode": os.path.join(ROOT, "profiles",
+                                     "hbm_traffic_decode_llama3_8b.txt"),
+}
+
+
+def recorded_traffic(workload: str = "llama3_8b_decode"):
+    """HBM bytes per decode launch from the committed counter summary
+    (FETCH_SIZE/WRITE_SIZE, calibrated on a plain copy), or None when no
+    summary exists for the workload or the decode sources differ from the
+    ones the counters were taken on."""
+    import hashlib
+    path = TRAFFIC_PROFILES.get(workload)
+    if path is None:
+        return None
+    try:
+        text = open(path).read().splitlines()
+    except OSError:
+        return None
+    value = None
+    for line in text:
+        if line.startswith("traffic_bytes_per_launch:"):
+            value = int(line.split(":")[1])
+        elif line.startswith("source_sha256 "):
+            rel, digest = line[len("source_sha256 "):].rsplit(": ", 1)
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest.strip():
+                    return None
+    return value
+
+
+def decode_bytes(ctx: np.ndarray, hq: int, hkv: int, d: int, B: int,
+                 paged: bool, esize: int = 2, shared: int = 0) -> int:
     """Algorithmic bytes of one decode call: K and V of every context token
-    once per KV head, q and o, the block-table entries in use, lengths."""
-    kvb = int(lens.sum()) * hkv * d * 2 * esize
-    qo = 2 * len(lens) * hq * d * esize
-    table = int(sum(-(-int(n) // B) for n in lens)) * 4 if paged else 0
-    return kvb + qo + table + 4 * len(lens)
+    once per KV head, q and o, the block-table entries in use, lengths.
+    ``shared`` leading tokens of every context sit in the same physical
+    blocks for all sequences and count once."""
+    toks = int(ctx.sum()) - shared * (len(ctx) - 1) if shared else \
+        int(ctx.sum())
+    kvb = toks * hkv * d * 2 * esize
+    qo = 2 * len(ctx) * hq * d * esize
+    table = int(sum(-(-int(n) // B) for n in ctx)) * 4 if paged else 0
+    return kvb + qo + table + 4 * len(ctx)
+
+
+def pool_blocks(kv, w, lengths, headroom: int = 0) -> int:
+    """Blocks for every sequence with no slack, plus ``headroom``; with a
+    shared prefix, its blocks once plus each sequence's blocks past the last
+    full prefix block."""
+    B = w.block_size
+    if w.kind == "prefix":
+        P = w.prefix_len
+        own = sum(kv.kv_blocks_needed(P + int(n), B) - P // B
+                  for n in lengths)
+        return kv.kv_blocks_needed(P, B) + own + headroom
+    return sum(kv.kv_blocks_needed(int(n), B) for n in lengths) + headroom
+
+
+def stats_ms(ms) -> dict:
+    ms = np.asarray(ms, dtype=np.float64)
+    return {"mean": float(ms.mean()), "median": float(np.median(ms)),
+            "p10": float(np.percentile(ms, 10)),
+            "p90": float(np.percentile(ms, 90))}
 
 
 class DecodeReplica:
-    """One independent copy of the decode batch, paged or contiguous."""
+    """One independent copy of the decode batch, paged or contiguous. The
+    contexts minus their newest token are written through the product path
+    (append + cache write); with a shared prefix, sequence 0 writes it and
+    the others take shared references to its blocks (fork)."""
 
-    def __init__(self, inp, new_k, new_v, paged: bool, steps: int, device):
+    def __init__(self, inp, k_dev, v_dev, new_k, new_v, paged: bool,
+                 steps: int, device):
         import torch
         from paged_kv_cache_191_amd import kvpaged as kv
+        from paged_kv_cache_191_amd import workloads as W
         self.kv = kv
         self.torch = torch
         w = inp.workload
         self.w = w
         self.paged = paged
         S, B = w.num_seqs, w.block_size
-        ctx = inp.lengths.astype(np.int64)
+        ctx = W.context_lengths(inp).astype(np.int64)
         self.lmax = int(ctx.max()) + steps + 1
         self.cap = -(-self.lmax // B)
         n_pool = len(inp.free_order)
@@ -92,32 +172,46 @@ class DecodeReplica:
         tdt = inp.k.dtype
         self.h_table[:] = -1
         self.h_lens[:] = 0
+        self.shared = 0
         if paged:
             self.pool = kv.KVPool(n_pool, B, inp.free_order)
             self.k = torch.empty((n_pool, w.num_kv_heads, B, w.head_dim),
                                  dtype=tdt, device=device)
             self.v = torch.empty_like(self.k)
-            # contexts minus the newest token, written through the product
-            # path (append + cache write), one sequence at a time
-            for s in range(S):
+
+            def write(s, first, count):
                 n_new = np.zeros(S, dtype=np.int32)
-                n_new[s] = int(ctx[s]) - 1
-                slots, _ = self.pool.seq_append(self.h_table, self.h_lens,
-                                                n_new)
-                rows = torch.arange(int(inp.cu[s]), int(inp.cu[s + 1]) - 1)
-                kv.kv_reshape_and_cache(inp.k[rows].to(device),
-                                        inp.v[rows].to(device),
+                n_new[s] = count
+                slots, pairs = self.pool.seq_append(self.h_table, self.h_lens,
+                                                    n_new)
+                assert len(pairs) == 0
+                rows = torch.from_numpy(
+                    W.logical_rows(inp, s)[first:first + count]).to(device)
+                kv.kv_reshape_and_cache(k_dev[rows], v_dev[rows],
                                         torch.from_numpy(slots).to(device),
                                         self.k, self.v)
+
+            P = inp.prefix_rows
+            if P:
+                write(0, 0, P)
+                nb = kv.kv_blocks_needed(P, B)
+                for s in range(1, S):
+                    self.pool.share(self.h_table[0, :nb].tolist())
+                    self.h_table[s, :nb] = self.h_table[0, :nb]
+                    self.h_lens[s] = P
+                self.shared = (P // B) * B
+            for s in range(S):
+                first = int(self.h_lens[s])
+                write(s, first, int(ctx[s]) - 1 - first)
         else:
             self.k = torch.empty((S, w.num_kv_heads, self.lmax, w.head_dim),
                                  dtype=tdt, device=device)
             self.v = torch.empty_like(self.k)
             for s in range(S):
                 n = int(ctx[s]) - 1
-                rows = slice(int(inp.cu[s]), int(inp.cu[s]) + n)
-                self.k[s, :, :n] = inp.k[rows].to(device).transpose(0, 1)
-                self.v[s, :, :n] = inp.v[rows].to(device).transpose(0, 1)
+                rows = torch.from_numpy(W.logical_rows(inp, s)[:n]).to(device)
+                self.k[s, :, :n] = k_dev[rows].transpose(0, 1)
+                self.v[s, :, :n] = v_dev[rows].transpose(0, 1)
                 self.h_lens[s] = n
         self.ws = kv.decode_workspace(S, w.num_q_heads, w.num_kv_heads,
                                       w.head_dim, self.lmax, device)
@@ -145,11 +239,13 @@ class DecodeReplica:
         kv = self.kv
         self.d_buf.copy_(self.h_buf, non_blocking=True)
         self.uploaded.record()
+        if ev is not None:
+            ev[0].record()
         kv.kv_reshape_and_cache(self.new_k, self.new_v, self.d_slots, self.k,
                                 self.v)
         max_ctx = int(self.h_lens.max())
         if ev is not None:
-            ev[0].record()
+            ev[1].record()
         if self.paged:
             kv.paged_attn_decode(self.out, self.q, self.k, self.v,
                                  self.d_table, self.d_lens, max_ctx,
@@ -158,53 +254,149 @@ class DecodeReplica:
             kv.contig_attn_decode(self.out, self.q, self.k, self.v,
                                   self.d_lens, max_ctx, self.scale, self.ws)
         if ev is not None:
-            ev[1].record()
+            ev[2].record()
+
+
+def new_token_kv(w, device):
+    """K/V of the token each sequence appends per step (seeded, bf16)."""
+    import torch
+    g = np.random.default_rng([w.seed, 50])
+    shape = (w.num_seqs, w.num_kv_heads, w.head_dim)
+    mk = [torch.from_numpy(g.standard_normal(shape, dtype=np.float32)).to(
+        torch.bfloat16).to(device) for _ in range(2)]
+    return mk[0], mk[1]
 
 
 def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
                device):
     import torch
     w = inp.workload
-    g = np.random.default_rng([w.seed, 50])
-    shape = (w.num_seqs, w.num_kv_heads, w.head_dim)
-    new_k = torch.from_numpy(g.standard_normal(shape, dtype=np.float32)).to(
-        torch.bfloat16).to(device)
-    new_v = torch.from_numpy(g.standard_normal(shape, dtype=np.float32)).to(
-        torch.bfloat16).to(device)
-    reps_ = [DecodeReplica(inp, new_k, new_v, paged, steps + warmup, device)
-             for _ in range(reps)]
+    new_k, new_v = new_token_kv(w, device)
+    k_dev, v_dev = inp.k.to(device), inp.v.to(device)
+    reps_ = [DecodeReplica(inp, k_dev, v_dev, new_k, new_v, paged,
+                           steps + warmup, device) for _ in range(reps)]
+    del k_dev, v_dev
     for i in range(warmup):
         r = reps_[i % reps]
         r.host_append()
         r.device_step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    total_bytes = 0
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+           for _ in range(steps)]
+    total_bytes = logical_bytes = 0
     t0 = time.perf_counter()
     for i in range(steps):
         r = reps_[i % reps]
         r.host_append()
-        total_bytes += decode_bytes(r.h_lens, w.num_q_heads, w.num_kv_heads,
-                                    w.head_dim, w.block_size, paged)
+        args = (r.h_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                w.block_size, paged)
+        total_bytes += decode_bytes(*args, shared=r.shared)
+        logical_bytes += decode_bytes(*args)
         r.device_step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    op_ms = [a.elapsed_time(b) for a, b in evs]
+    op = stats_ms([b.elapsed_time(c) for _, b, c in evs])
+    rc = stats_ms([a.elapsed_time(b) for a, b, _ in evs])
     res = {
         "wall_s": wall,
         "ms_per_step": 1e3 * wall / steps,
         "step_GBps": total_bytes / wall / 1e9,
-        "decode_op_ms_mean": float(np.mean(op_ms)),
-        "decode_op_ms_p10": float(np.percentile(op_ms, 10)),
-        "decode_op_ms_p90": float(np.percentile(op_ms, 90)),
+        "decode_op_ms_mean": op["mean"],
+        "decode_op_ms_median": op["median"],
+        "decode_op_ms_p10": op["p10"],
+        "decode_op_ms_p90": op["p90"],
         "bytes_per_step": total_bytes / steps,
+        "reshape_and_cache_us_median": 1e3 * rc["median"],
     }
-    res["decode_op_GBps"] = res["bytes_per_step"] / (
-        res["decode_op_ms_mean"] * 1e-3) / 1e9
+    res["decode_op_GBps"] = res["bytes_per_step"] / (op["mean"] * 1e-3) / 1e9
+    if logical_bytes != total_bytes:
+        res["logical_bytes_per_step"] = logical_bytes / steps
+        res["decode_op_effective_GBps"] = (logical_bytes / steps) / (
+            op["mean"] * 1e-3) / 1e9
+    # the new rows: K and V, read once and written once
+    tok_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2 * 2
+    res["reshape_and_cache_GBps"] = tok_bytes / (rc["median"] * 1e-3) / 1e9
     del reps_
     torch.cuda.empty_cache()
     return res
+
+
+def run_cow(w, steps: int, warmup: int, device):
+    """Copy-on-write step: 256 sequences forked from a COW_PREFIX-token
+    prefix whose last block is half full each append one token; 255 of them
+    copy that block (kv_copy_blocks), the last finds it unshared and writes
+    in place. Every repetition starts from a fresh allocator with the same
+    free order, so the prefix rows (written once) stay valid."""
+    import torch
+    from paged_kv_cache_191_amd import kvpaged as kv
+    from paged_kv_cache_191_amd import workloads as W
+    wc = w.replace(prefix_len=COW_PREFIX, name="prefix_share_cow")
+    S, B, P = wc.num_seqs, wc.block_size, COW_PREFIX
+    nb_prefix = kv.kv_blocks_needed(P, B)
+    n_pool = nb_prefix + S
+    inp = W.draw(wc, lambda L: n_pool)
+    cap = kv.kv_blocks_needed(P + 1, B)
+    tdt = inp.k.dtype
+    kc = torch.empty((n_pool, wc.num_kv_heads, B, wc.head_dim), dtype=tdt,
+                     device=device)
+    vc = torch.empty_like(kc)
+    new_k, new_v = new_token_kv(wc, device)
+    q = inp.q.to(device)
+    out = torch.empty_like(q)
+    ws = kv.decode_workspace(S, wc.num_q_heads, wc.num_kv_heads, wc.head_dim,
+                             P + 1, device)
+    scale = 1.0 / float(np.sqrt(wc.head_dim))
+    times, host_us, n_pairs = [], [], 0
+    for i in range(warmup + steps):
+        t_h = time.perf_counter()
+        pool = kv.KVPool(n_pool, B, inp.free_order)
+        table = np.full((S, cap), -1, dtype=np.int32)
+        lens = np.zeros(S, dtype=np.int32)
+        n_new = np.zeros(S, dtype=np.int32)
+        n_new[0] = P
+        slots0, _ = pool.seq_append(table, lens, n_new)
+        for s in range(1, S):
+            pool.share(table[0, :nb_prefix].tolist())
+            table[s, :nb_prefix] = table[0, :nb_prefix]
+            lens[s] = P
+        slots, pairs = pool.seq_append(table, lens)
+        host_us.append(1e6 * (time.perf_counter() - t_h))
+        n_pairs = len(pairs)
+        if i == 0:
+            rows = torch.arange(P, device=device)
+            kv.kv_reshape_and_cache(inp.k.to(device)[rows],
+                                    inp.v.to(device)[rows],
+                                    torch.from_numpy(slots0).to(device), kc,
+                                    vc)
+        d_pairs = torch.from_numpy(pairs).to(device)
+        d_slots = torch.from_numpy(slots).to(device)
+        d_table = torch.from_numpy(table).to(device)
+        d_lens = torch.from_numpy(lens).to(device)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        kv.kv_copy_blocks(kc, vc, d_pairs)
+        ev[1].record()
+        kv.kv_reshape_and_cache(new_k, new_v, d_slots, kc, vc)
+        kv.paged_attn_decode(out, q, kc, vc, d_table, d_lens,
+                             int(lens.max()), scale, ws)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if i >= warmup:
+            times.append((ev[0].elapsed_time(ev[1]),
+                          ev[0].elapsed_time(ev[2])))
+        pool.close()
+    copy_ms = stats_ms([a for a, _ in times])
+    step_ms = stats_ms([b for _, b in times])
+    copy_bytes = 2 * n_pairs * B * wc.num_kv_heads * wc.head_dim * 2 * 2
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"prefix_tokens": P, "cow_copies": n_pairs,
+            "copy_blocks_us_median": 1e3 * copy_ms["median"],
+            "copy_blocks_GBps": copy_bytes / (copy_ms["median"] * 1e-3) / 1e9,
+            "step_incl_cow_us_median": 1e3 * step_ms["median"],
+            "step_incl_cow_us_p10": 1e3 * step_ms["p10"],
+            "step_incl_cow_us_p90": 1e3 * step_ms["p90"],
+            "host_fork_and_append_us_median": float(np.median(host_us))}
 
 
 def prefill_pass(inp, layout: str, device):
@@ -250,26 +442,27 @@ def prefill_pass(inp, layout: str, device):
             rows = (np.arange(S)[:, None] * N + c0 +
                     np.arange(C)[None, :]).reshape(-1)
             rows_d = torch.from_numpy(rows).to(device)
-            kv.kv_reshape_and_cache(k_dev[rows_d], v_dev[rows_d],
-                                    torch.from_numpy(slots).to(device), kc, vc)
+            k_new, v_new = k_dev[rows_d], v_dev[rows_d]
+            d_slots = torch.from_numpy(slots).to(device)
             cu = torch.arange(0, S * C + 1, C, dtype=torch.int32,
                               device=device)
             start = torch.full((S,), c0, dtype=torch.int32, device=device)
             ctx = torch.from_numpy(lens.copy()).to(device)
+            d_table = torch.from_numpy(table).to(device)
             q = q_dev[rows_d]
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
+            kv.kv_reshape_and_cache(k_new, v_new, d_slots, kc, vc)
+            ev[1].record()
             if layout == "contig":
                 kv.contig_attn_prefill(out, q, cu, start, C, kc, vc, ctx,
                                        scale, True)
             else:
-                kv.paged_attn_prefill(out, q, cu, start, C, kc, vc,
-                                      torch.from_numpy(table).to(device), ctx,
-                                      scale, True)
-            e1.record()
+                kv.paged_attn_prefill(out, q, cu, start, C, kc, vc, d_table,
+                                      ctx, scale, True)
+            ev[2].record()
             if timed:
-                times.append((e0, e1))
+                times.append(ev)
                 # unmasked causal pairs of this chunk, 4*d*Hq flops each
                 pairs = S * (C * c0 + C * (C + 1) // 2)
                 flops_total += 4.0 * w.head_dim * w.num_q_heads * pairs
@@ -279,24 +472,51 @@ def prefill_pass(inp, layout: str, device):
     t0 = time.perf_counter()
     one_pass(True)
     wall = time.perf_counter() - t0
-    attn_ms = sum(a.elapsed_time(b) for a, b in times)
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in times)
+    rc_ms = [e[0].elapsed_time(e[1]) for e in times]
+    # new rows per chunk: K and V, read once and written once
+    rc_bytes = S * C * w.num_kv_heads * w.head_dim * 2 * 2 * 2
     del kc, vc, q_dev, k_dev, v_dev, out
     torch.cuda.empty_cache()
     return {"attn_ms": attn_ms, "pass_wall_ms": 1e3 * wall,
             "TFLOPs": flops_total / (attn_ms * 1e-3) / 1e12,
-            "tflop": flops_total / 1e12}
+            "tflop": flops_total / 1e12,
+            "reshape_and_cache_us_median": 1e3 * float(np.median(rc_ms)),
+            "reshape_and_cache_GBps": rc_bytes / (float(np.median(rc_ms)) *
+                                                  1e-3) / 1e9}
+
+
+def memory_waste(inp, lmax_reserved: int) -> dict:
+    """Unused slots of the paged pool (the tail of each sequence's last
+    block; a shared prefix held once) next to a contiguous reservation of
+    ``lmax_reserved`` tokens per sequence (a shared prefix copied into every
+    sequence), at the drawn contexts."""
+    from paged_kv_cache_191_amd import kvpaged as kv
+    from paged_kv_cache_191_amd import workloads as W
+    w = inp.workload
+    held = pool_blocks(kv, w, inp.lengths) * w.block_size
+    unique = int(inp.lengths.sum()) + int(inp.prefix_rows)
+    logical = int(W.context_lengths(inp).sum())
+    reserved = len(inp.lengths) * lmax_reserved
+    return {"paged_held_tokens": held,
+            "paged_waste": round(1.0 - unique / held, 5),
+            "contig_reserved_tokens": reserved,
+            "contig_reservation_waste": round(1.0 - logical / reserved, 5),
+            "contig_reserved_over_paged_held": round(reserved / held, 3)}
 
 
 def cpu_baseline(inp, budget_s: float = 12.0):
     """The fp64 oracle (as it stands) on this host: paged decode of the
-    same workload, gather + conversion + attention timed, pool build not."""
+    same workload, gather + conversion + attention timed, pool build not.
+    Timed with every BLAS thread, then with one."""
     from oracle import allocator as A
     from oracle import attention as O
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] +
                       [1])
     except Exception:
+        threadpool_limits = None
         threads = 1
     w = inp.workload
     B = w.block_size
@@ -305,6 +525,7 @@ def cpu_baseline(inp, budget_s: float = 12.0):
     tables, lens = [[] for _ in range(S)], [0] * S
     st, slots, _ = A.append_tokens(pool, tables, lens, inp.lengths.tolist(),
                                    1 << 30)
+    assert st == A.OK
     kp = np.zeros((len(inp.free_order), B, w.num_kv_heads, w.head_dim),
                   dtype=np.float32)
     vp = np.zeros_like(kp)
@@ -312,23 +533,55 @@ def cpu_baseline(inp, budget_s: float = 12.0):
     O.scatter_rows(vp, inp.v.float().numpy(), slots)
     q = inp.q.float().numpy()
     scale = 1.0 / float(np.sqrt(w.head_dim))
-    done, nbytes = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        s = done % S
-        O.decode_paged(q, kp, vp, tables, lens, scale, seqs=[s])
-        nbytes += decode_bytes(np.array([lens[s]]), w.num_q_heads,
-                               w.num_kv_heads, w.head_dim, B, True)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s and done >= S:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+
+    def timed(budget):
+        done, nbytes = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            s = done % S
+            O.decode_paged(q, kp, vp, tables, lens, scale, seqs=[s])
+            nbytes += decode_bytes(np.array([lens[s]]), w.num_q_heads,
+                                   w.num_kv_heads, w.head_dim, B, True)
+            done += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        return done, nbytes, time.perf_counter() - t0
+
+    done, nbytes, dt = timed(budget_s)
+    one = None
+    if threadpool_limits is not None and threads > 1:
+        with threadpool_limits(limits=1):
+            d1, b1, t1 = timed(budget_s / 3)
+        one = round(b1 / t1 / 1e9, 4)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
             "sample": f"{done} sequence decodes of the {w.name} batch "
-                      f"({done / S:.2f} passes), {dt:.1f} s of fp64 oracle "
-                      f"time (gather through the table, bf16->fp64, "
-                      f"attention)"}
+                      f"({done / S:.2f} passes over its {S} sequences), "
+                      f"{dt:.1f} s of fp64 oracle time (gather through the "
+                      f"table, bf16->fp64, attention)",
+            "value_one_thread": one, "nproc": os.cpu_count(),
+            "cpu_model": cpu_model}
+
+
+def calibration_copy(device) -> None:
+    """One plain 1 GiB device copy: the reference kernel for hardware
+    traffic counters."""
+    import torch
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def main() -> int:
@@ -337,10 +590,20 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--workload", default="llama3_8b_decode",
+                    choices=DECODE_WORKLOADS)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode steps (prefill / profiling runs); "
+                         "no bench line is printed")
+    ap.add_argument("--prefill-layouts", default="paged_b16,paged_b64,contig")
     ap.add_argument("--no-contig", action="store_true")
+    ap.add_argument("--no-cow", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference "
+                         "kernel for hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not "
@@ -358,45 +621,66 @@ def main() -> int:
         return 1
     device = torch.device("cuda:0")
 
-    wd = W.WORKLOADS["llama3_8b_decode"]
+    if args.calibration_copy:
+        calibration_copy(device)
+
+    wd = W.WORKLOADS[args.workload]
+    default_workload = args.workload == "llama3_8b_decode"
     headroom = wd.num_seqs * (-(-(args.steps + args.warmup) // wd.block_size)
                               + 1)
-    log("drawing llama3_8b_decode")
-    inp = W.draw(wd, lambda L: sum(kv.kv_blocks_needed(int(n), wd.block_size)
-                                   for n in L) + headroom)
-    log("paged decode steps")
-    paged = run_decode(inp, True, args.steps, args.warmup, args.replicas,
-                       device)
-    contig = None
-    if not args.no_contig:
-        log("contiguous decode steps")
-        contig = run_decode(inp, False, args.steps, args.warmup,
-                            args.replicas, device)
+    paged = contig = inp = cow = None
+    if not args.no_decode:
+        log(f"drawing {wd.name}")
+        inp = W.draw(wd, lambda L: pool_blocks(kv, wd, L, headroom))
+        log("paged decode steps")
+        paged = run_decode(inp, True, args.steps, args.warmup, args.replicas,
+                           device)
+        if not args.no_contig:
+            log("contiguous decode steps")
+            contig = run_decode(inp, False, args.steps, args.warmup,
+                                args.replicas, device)
+        if wd.kind == "prefix" and not args.no_cow:
+            log("copy-on-write step")
+            cow = run_cow(wd, args.steps, args.warmup, device)
 
     prefill = None
-    if not args.no_prefill:
+    if not args.no_prefill and (default_workload or args.no_decode):
         prefill = {}
+        wanted = args.prefill_layouts.split(",")
         for name, layout in (("yi6b_chunked_prefill_b16", "paged_b16"),
                              ("yi6b_chunked_prefill_b64", "paged_b64"),
                              ("yi6b_chunked_prefill_b16", "contig")):
+            if layout not in wanted:
+                continue
             wp = W.WORKLOADS[name]
             log(f"prefill {layout}")
-            pin = W.draw(wp, lambda L: sum(
-                kv.kv_blocks_needed(int(n), wp.block_size) for n in L))
+            pin = W.draw(wp, lambda L: pool_blocks(kv, wp, L))
             r = prefill_pass(pin, "contig" if layout == "contig" else "paged",
                              device)
             r["frac_of_peak"] = r["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
             prefill[layout] = r
-        for b in ("paged_b16", "paged_b64"):
-            prefill[b]["overhead_vs_contig"] = (
-                prefill[b]["attn_ms"] / prefill["contig"]["attn_ms"] - 1.0)
+        if "contig" in prefill:
+            for b in ("paged_b16", "paged_b64"):
+                if b in prefill:
+                    prefill[b]["overhead_vs_contig"] = (
+                        prefill[b]["attn_ms"] / prefill["contig"]["attn_ms"]
+                        - 1.0)
+    if args.no_decode:
+        log(f"prefill only: {json.dumps(prefill)}")
+        return 0
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wd.kind == "decode":
         log("cpu baseline (fp64 oracle)")
         cpu = cpu_baseline(inp, args.cpu_budget)
 
     achieved = paged["decode_op_GBps"]
+    ctx_desc = {"llama3_8b_decode": "U{512..4096}",
+                "yi34b_long_decode": "196608",
+                "prefix_share_decode": "4096 shared + U{64..1024}"}
+    lmax_reserved = {"llama3_8b_decode": 4096,
+                     "yi34b_long_decode": 196608,
+                     "prefix_share_decode": 4096 + 1024}[wd.name]
     line = {
         "metric": METRIC,
         "value": round(paged["step_GBps"], 2),
@@ -411,28 +695,32 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "llama3_8b_decode",
+            "workload": wd.name,
             "num_seqs": wd.num_seqs, "num_q_heads": wd.num_q_heads,
             "num_kv_heads": wd.num_kv_heads, "head_dim": wd.head_dim,
-            "block_size": wd.block_size, "context": "U{512..4096}",
+            "block_size": wd.block_size, "context": ctx_desc[wd.name],
             "step": "append+upload+reshape_and_cache+paged_attn_decode",
             "replicas": args.replicas,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-            "kernel": "paged_attn_decode (decode_mfma_kernel + "
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": recorded_traffic(wd.name),
+            "kernel": "paged_attn_decode (decode_sk_kernel + "
                       "decode_combine_kernel)",
             "bytes_per_launch": int(paged["bytes_per_step"]),
             "ms_per_launch": round(paged["decode_op_ms_mean"], 4),
         },
         "decode_paged": {k: round(v, 4) for k, v in paged.items()},
+        "memory": memory_waste(inp, lmax_reserved),
     }
     if contig:
         line["decode_contig"] = {k: round(v, 4) for k, v in contig.items()}
         line["decode_paged_vs_contig_overhead"] = round(
             paged["decode_op_ms_mean"] / contig["decode_op_ms_mean"] - 1.0, 4)
+    if cow:
+        line["copy_on_write"] = {k: round(v, 4) for k, v in cow.items()}
     if prefill:
         line["prefill"] = {k: {kk: round(vv, 4) for kk, vv in v.items()}
                            for k, v in prefill.items()}
