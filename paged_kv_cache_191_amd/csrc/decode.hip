@@ -10,11 +10,13 @@
 // their timing difference is the table lookup.
 //
 // Fast path (bf16, head_dim 128, block_size % 16 == 0, any GQA group):
-//   * Balanced split ("stream-K"): per KV head, the tokens of all sequences
-//     are laid end to end and cut into n_chunks equal chunks; workgroup
-//     (unit, chunk) streams one chunk. Every workgroup moves the same bytes
-//     whatever the length mix. The chunk size is derived on the device from
-//     the context lengths, so the grid needs no host-side sums.
+//   * Balanced split ("stream-K"): per KV head, the 32-token tiles of all
+//     sequences (ceil(L / 32) per sequence) are laid end to end and cut into
+//     n_chunks equal chunks; workgroup (unit, chunk) streams one chunk. Every
+//     workgroup moves the same bytes whatever the length mix, and a piece of
+//     a sequence always starts on a tile boundary, so no tile is read by two
+//     workgroups. The chunk size is derived on the device from the context
+//     lengths, so the grid needs no host-side sums.
 //   * A chunk covers pieces ("segments") of one or more sequences. The 4
 //     waves of the workgroup share each segment tile by tile, then merge
 //     their softmax states through LDS. A segment that is a whole sequence
@@ -35,8 +37,10 @@
 //     segment (one lane per group) and broadcast with v_readlane, so each
 //     half-tile's address is wave-uniform.
 //   * Tiles are 32-aligned in sequence positions (16-token groups never
-//     straddle a block); tokens outside the segment are selected out (score
-//     -inf, V 0), never multiplied by 0, so NaN in unused slots cannot leak.
+//     straddle a block); a half tile wholly past the context re-reads the
+//     last context group (rows already in flight, served by the cache);
+//     tokens past the context are selected out (score -inf, V 0), never
+//     multiplied by 0, so NaN in unused slots cannot leak.
 // Generic path (fp32, or shapes the fast path does not cover): one wave per
 // (sequence, query head), lanes over head_dim, tokens in order.
 
@@ -95,10 +99,14 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
   return c;
 }
 
-// Tokens per chunk for T tokens in total: T / n_chunks rounded up to 64.
-__device__ __forceinline__ int chunk_tokens(int total, int n_chunks) {
+__device__ __forceinline__ int tiles_of(int tokens) {
+  return (tokens + kTile - 1) / kTile;
+}
+
+// Tiles per chunk for T tiles in total.
+__device__ __forceinline__ int chunk_tiles(int total, int n_chunks) {
   const int c = (total + n_chunks - 1) / n_chunks;
-  return c <= 64 ? 64 : ((c + 63) & ~63);
+  return c < 1 ? 1 : c;
 }
 
 // ---------------------------------------------------------------------------
@@ -124,13 +132,13 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   const int chunk = blockIdx.y;
   const int S = a.num_seqs;
 
-  // --- token offsets of the sequences (exclusive scan of the lengths) ---
+  // --- tile offsets of the sequences (exclusive scan of the tile counts) ---
   {
     const int per = (S + kWaves * kWave - 1) / (kWaves * kWave);
     const int lo = tid * per;
     const int hi = min(S, lo + per);
     int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += clamp_ctx(a, i, PAGED);
+    for (int i = lo; i < hi; ++i) sum += tiles_of(clamp_ctx(a, i, PAGED));
     s_part[tid] = sum;
     __syncthreads();
     // inclusive Hillis-Steele scan of the 256 partial sums
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     int run = s_part[tid] - sum;
     for (int i = lo; i < hi; ++i) {
       s_cs[i] = run;
-      run += clamp_ctx(a, i, PAGED);
+      run += tiles_of(clamp_ctx(a, i, PAGED));
     }
     if (tid == kWaves * kWave - 1) s_cs[S] = s_part[tid];
     __syncthreads();
@@ -151,12 +159,12 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   const int total = s_cs[S];
   if (blockIdx.x == 0 && chunk == 0)
     for (int i = tid; i <= S; i += kWaves * kWave) a.ws_cs[i] = s_cs[i];
-  const int C = chunk_tokens(total, a.n_chunks);
+  const int C = chunk_tiles(total, a.n_chunks);
   const int c0 = chunk * C;
   if (c0 >= total) return;
   const int c1 = min(total, c0 + C);
 
-  // sequence holding token c0: largest s with s_cs[s] <= c0
+  // sequence holding tile c0: largest s with s_cs[s] <= c0
   int s = 0;
   {
     int lo = 0, hi = S - 1;
@@ -175,12 +183,15 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
 
   for (int pos = c0; pos < c1; ++s) {
     const int seq_lo = s_cs[s];
-    const int L = s_cs[s + 1] - seq_lo;
-    if (L == 0) continue;
-    // segment [lo, hi) in sequence positions
-    const int lo = pos - seq_lo;
-    const int hi = min(c1 - seq_lo, L);
-    pos = seq_lo + hi;
+    const int nt = s_cs[s + 1] - seq_lo;
+    if (nt == 0) continue;
+    // segment: tiles [lo_t, hi_t) of the sequence, tokens [lo, hi)
+    const int lo_t = pos - seq_lo;
+    const int hi_t = min(c1 - seq_lo, nt);
+    pos = seq_lo + hi_t;
+    const int L = clamp_ctx(a, s, PAGED);
+    const int lo = kTile * lo_t;
+    const int hi = min(kTile * hi_t, L);
 
     const int qh = g * a.group + (h_valid ? h_in_group : 0);
     bf16x8 qop[4];  // Q^T: B operand, head r16, d = 32 i + 8 grp + e
@@ -201,9 +212,9 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
 #pragma unroll
     for (int m = 0; m < 8; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // 32-aligned tiles covering [lo, hi); wave w takes tiles w, w+4, ...
-    const int t_al = lo & ~(kTile - 1);
-    const int n_tiles = (hi - t_al + kTile - 1) / kTile;
+    // tiles covering [lo, hi); wave w takes tiles w, w+4, ...
+    const int t_al = lo;
+    const int n_tiles = hi_t - lo_t;
     const int last_grp_pos = (hi - 1) & ~15;  // start of the last valid group
     const int64_t seq_row0 = ((int64_t)s * a.hkv + g) * a.seq_stride;
 
@@ -231,6 +242,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
       for (int j = 0; kb0 + w + kWaves * j < k_end; ++j) {
         const int t = t_al + kTile * (kb0 + w + kWaves * j);
         // K: A operand of S^T (token r16 of each half, d = 32 i + 8 grp + e)
+        // K: A operand of S^T (token r16 of each half, d = 32 i + 8 grp + e)
         u32x4 kr[2][4];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -254,7 +266,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
             sc[hf] = mfma16(as_bf16x8(kr[hf][i]), qop[i], sc[hf]);
         }
 
-        const bool full = t >= lo && t + kTile <= hi;
+        const bool full = t + kTile <= hi;
         float x[2][4];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -262,7 +274,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
           for (int r = 0; r < 4; ++r) {
             const float v = sc[hf][r] * a.scale_log2;
             const int p = t + 16 * hf + 4 * grp + r;
-            x[hf][r] = (full || (p >= lo && p < hi)) ? v : -INFINITY;
+            x[hf][r] = (full || p < hi) ? v : -INFINITY;
           }
         float mx =
             fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int pe = t + 16 * (e >> 2) + 4 * grp + (e & 3);
-            if (pe < lo || pe >= hi) vr[e] = u32x4{0, 0, 0, 0};
+            if (pe >= hi) vr[e] = u32x4{0, 0, 0, 0};
           }
         }
         // V^T rows d = 8 r16 + m: element e of A_m is V[tau(grp, e)][8r16+m]
@@ -335,10 +347,10 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
       sm_ml[w][r16][1] = l_part;
     }
     __syncthreads();
-    const bool whole = lo == 0 && hi == L;
+    const bool whole = lo_t == 0 && hi_t == nt;
     // slot 0: a continuation (lo > 0); slot 1: first piece of a sequence
     // that continues in later chunks.
-    const int slot = lo > 0 ? 0 : 1;
+    const int slot = lo_t > 0 ? 0 : 1;
     for (int it = tid; it < kHeadBlk * (kD / 8); it += kWaves * kWave) {
       const int h = it / (kD / 8);
       const int c = it % (kD / 8);
@@ -391,60 +403,73 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
 
 // Exact merge of the partials of a sequence that spans several chunks:
 // o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i with M = max_i m_i, for
-// every query head. Grid (sequence, slice of 64 items); one (head, 8-wide d
-// chunk) item per thread; the pieces are folded in one pass with a running
-// max. Also writes zeros for empty contexts.
-constexpr int kCombineThreads = 64;
+// every query head. Grid (sequence, query head), one wave each: lane
+// (j, c) = (lane / 16, lane % 16) folds pieces j, j+4, ... of d chunk c (8
+// values) with a running max; the four lane groups are then merged by
+// shuffles. Also writes zeros for empty contexts.
+constexpr int kCombineThreads = kWave;
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     DecodeArgs a) {
   const int s = blockIdx.x;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int c = lane & 15;
+  const int j = lane >> 4;
   const int* cs = a.ws_cs;
   const int total = cs[a.num_seqs];
   const int seq_lo = cs[s], seq_hi = cs[s + 1];
-  const int items = a.hq * (kD / 8);
-  bf16* out = (bf16*)a.out + (int64_t)s * a.hq * kD;
-  const int it = blockIdx.y * kCombineThreads + threadIdx.x;
-  if (it >= items) return;
+  bf16* out = (bf16*)a.out + ((int64_t)s * a.hq + h) * kD;
   if (seq_hi == seq_lo) {
-    st16(out + 8 * it, u32x4{0, 0, 0, 0});
+    if (j == 0) st16(out + 8 * c, u32x4{0, 0, 0, 0});
     return;
   }
-  const int C = chunk_tokens(total, a.n_chunks);
+  const int C = chunk_tiles(total, a.n_chunks);
   const int ca = seq_lo / C, cb = (seq_hi - 1) / C;
   if (ca == cb) return;  // written whole by decode_sk_kernel
   const int n = cb - ca + 1;
-  {
-    const int h = it / (kD / 8);
-    const int c = it % (kD / 8);
-    float M = -INFINITY, L = 0.f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int i = 0; i < n; ++i) {
-      // piece i: chunk ca + i; slot 1 (first piece) for i == 0, else slot 0
-      const int64_t idx = ((int64_t)(ca + i) * 2 + (i == 0 ? 1 : 0)) * a.hq + h;
-      const float mi = a.ws_ml[2 * idx];
-      const float li = a.ws_ml[2 * idx + 1];
-      const f32x4 lo4 = *reinterpret_cast<const f32x4*>(a.ws_o + idx * kD + 8 * c);
-      const f32x4 hi4 =
-          *reinterpret_cast<const f32x4*>(a.ws_o + idx * kD + 8 * c + 4);
-      if (mi == -INFINITY) continue;
-      const float m_new = fmaxf(M, mi);
-      const float old_scale = fast_exp2(M - m_new);
-      const float new_scale = fast_exp2(mi - m_new);
-      M = m_new;
-      L = L * old_scale + li * new_scale;
+  float M = -INFINITY, L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int i = j; i < n; i += 4) {
+    // piece i: chunk ca + i; slot 1 (first piece) for i == 0, else slot 0
+    const int64_t idx = ((int64_t)(ca + i) * 2 + (i == 0 ? 1 : 0)) * a.hq + h;
+    const float mi = a.ws_ml[2 * idx];
+    const float li = a.ws_ml[2 * idx + 1];
+    const f32x4 lo4 = *reinterpret_cast<const f32x4*>(a.ws_o + idx * kD + 8 * c);
+    const f32x4 hi4 =
+        *reinterpret_cast<const f32x4*>(a.ws_o + idx * kD + 8 * c + 4);
+    if (mi == -INFINITY) continue;
+    const float m_new = fmaxf(M, mi);
+    const float old_scale = fast_exp2(M - m_new);
+    const float new_scale = fast_exp2(mi - m_new);
+    M = m_new;
+    L = L * old_scale + li * new_scale;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[j] = acc[j] * old_scale + lo4[j] * new_scale;
-        acc[4 + j] = acc[4 + j] * old_scale + hi4[j] * new_scale;
-      }
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = acc[e] * old_scale + lo4[e] * new_scale;
+      acc[4 + e] = acc[4 + e] * old_scale + hi4[e] * new_scale;
     }
+  }
+  // merge the four lane groups (lanes c, c + 16, c + 32, c + 48)
+  float Mall = fmaxf(M, __shfl_xor(M, 16));
+  Mall = fmaxf(Mall, __shfl_xor(Mall, 32));
+  const float f = M == -INFINITY ? 0.f : fast_exp2(M - Mall);
+  L *= f;
+  L += __shfl_xor(L, 16);
+  L += __shfl_xor(L, 32);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc[e] *= f;
+    acc[e] += __shfl_xor(acc[e], 16);
+    acc[e] += __shfl_xor(acc[e], 32);
+  }
+  if (j == 0) {
     const float inv = L > 0.f ? 1.f / L : 0.f;
     u32x4 ov;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      ov[j] = pack_bf16(acc[2 * j] * inv, acc[2 * j + 1] * inv);
-    st16(out + 8 * it, ov);
+    for (int e = 0; e < 4; ++e)
+      ov[e] = pack_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    st16(out + 8 * c, ov);
   }
 }
 
@@ -619,8 +644,7 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
       else
         decode_sk_kernel<false><<<grid, kWaves * kWave, 0, st>>>(b);
       KVP_LAUNCH_CHECK(name);
-      dim3 g2(b.num_seqs, (a.hq * (kD / 8) + kCombineThreads - 1) /
-                              kCombineThreads);
+      dim3 g2(b.num_seqs, a.hq);
       decode_combine_kernel<<<g2, kCombineThreads, 0, st>>>(b);
       KVP_LAUNCH_CHECK(name);
     }
