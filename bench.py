@@ -141,7 +141,7 @@ class DecodeReplica:
     the others take shared references to its blocks (fork)."""
 
     def __init__(self, inp, k_dev, v_dev, new_k, new_v, paged: bool,
-                 steps: int, device):
+                 steps: int, device, shared_op: bool = False):
         import torch
         from paged_kv_cache_191_amd import kvpaged as kv
         from paged_kv_cache_191_amd import workloads as W
@@ -213,8 +213,20 @@ class DecodeReplica:
                 self.k[s, :, :n] = k_dev[rows].transpose(0, 1)
                 self.v[s, :, :n] = v_dev[rows].transpose(0, 1)
                 self.h_lens[s] = n
-        self.ws = kv.decode_workspace(S, w.num_q_heads, w.num_kv_heads,
-                                      w.head_dim, self.lmax, device)
+        # shared_op: decode through paged_attn_decode_shared_prefix with
+        # one group (all sequences) sharing the prefix's whole blocks
+        self.shared_op = shared_op and paged and self.shared > 0
+        if self.shared_op:
+            self.ws = kv.decode_shared_prefix_workspace(
+                S, w.num_q_heads, w.num_kv_heads, w.head_dim, self.lmax,
+                self.shared, device)
+            self.g_starts = torch.tensor([0, S], dtype=torch.int32,
+                                         device=device)
+            self.g_shared = torch.tensor([self.shared], dtype=torch.int32,
+                                         device=device)
+        else:
+            self.ws = kv.decode_workspace(S, w.num_q_heads, w.num_kv_heads,
+                                          w.head_dim, self.lmax, device)
         # the staging buffer is rewritten only after its last upload is done
         self.uploaded = torch.cuda.Event()
         self.uploaded.record()
@@ -246,7 +258,12 @@ class DecodeReplica:
         max_ctx = int(self.h_lens.max())
         if ev is not None:
             ev[1].record()
-        if self.paged:
+        if self.shared_op:
+            kv.paged_attn_decode_shared_prefix(
+                self.out, self.q, self.k, self.v, self.d_table, self.d_lens,
+                max_ctx, self.g_starts, self.g_shared, self.w.num_seqs,
+                self.shared, self.scale, self.ws)
+        elif self.paged:
             kv.paged_attn_decode(self.out, self.q, self.k, self.v,
                                  self.d_table, self.d_lens, max_ctx,
                                  self.scale, self.ws)
@@ -268,13 +285,14 @@ def new_token_kv(w, device):
 
 
 def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
-               device):
+               device, shared_op: bool = False):
     import torch
     w = inp.workload
     new_k, new_v = new_token_kv(w, device)
     k_dev, v_dev = inp.k.to(device), inp.v.to(device)
     reps_ = [DecodeReplica(inp, k_dev, v_dev, new_k, new_v, paged,
-                           steps + warmup, device) for _ in range(reps)]
+                           steps + warmup, device, shared_op)
+             for _ in range(reps)]
     del k_dev, v_dev
     for i in range(warmup):
         r = reps_[i % reps]
@@ -325,7 +343,7 @@ def run_cow(w, steps: int, warmup: int, device):
     """Copy-on-write step: 256 sequences forked from a COW_PREFIX-token
     prefix whose last block is half full each append one token; 255 of them
     copy that block (kv_copy_blocks), the last finds it unshared and writes
-    in place. Every repetition starts from a fresh allocator with the same
+    in place; the decode then shares the prefix's whole blocks. Every repetition starts from a fresh allocator with the same
     free order, so the prefix rows (written once) stay valid."""
     import torch
     from paged_kv_cache_191_amd import kvpaged as kv
@@ -343,8 +361,11 @@ def run_cow(w, steps: int, warmup: int, device):
     new_k, new_v = new_token_kv(wc, device)
     q = inp.q.to(device)
     out = torch.empty_like(q)
-    ws = kv.decode_workspace(S, wc.num_q_heads, wc.num_kv_heads, wc.head_dim,
-                             P + 1, device)
+    shared = (P // B) * B  # whole blocks still shared after the copies
+    ws = kv.decode_shared_prefix_workspace(S, wc.num_q_heads, wc.num_kv_heads,
+                                           wc.head_dim, P + 1, shared, device)
+    g_starts = torch.tensor([0, S], dtype=torch.int32, device=device)
+    g_shared = torch.tensor([shared], dtype=torch.int32, device=device)
     scale = 1.0 / float(np.sqrt(wc.head_dim))
     times, host_us, n_pairs = [], [], 0
     for i in range(warmup + steps):
@@ -377,8 +398,9 @@ def run_cow(w, steps: int, warmup: int, device):
         kv.kv_copy_blocks(kc, vc, d_pairs)
         ev[1].record()
         kv.kv_reshape_and_cache(new_k, new_v, d_slots, kc, vc)
-        kv.paged_attn_decode(out, q, kc, vc, d_table, d_lens,
-                             int(lens.max()), scale, ws)
+        kv.paged_attn_decode_shared_prefix(out, q, kc, vc, d_table, d_lens,
+                                           int(lens.max()), g_starts,
+                                           g_shared, S, shared, scale, ws)
         ev[2].record()
         torch.cuda.synchronize()
         if i >= warmup:
@@ -628,13 +650,18 @@ def main() -> int:
     default_workload = args.workload == "llama3_8b_decode"
     headroom = wd.num_seqs * (-(-(args.steps + args.warmup) // wd.block_size)
                               + 1)
-    paged = contig = inp = cow = None
+    paged = contig = inp = cow = plain = None
     if not args.no_decode:
         log(f"drawing {wd.name}")
         inp = W.draw(wd, lambda L: pool_blocks(kv, wd, L, headroom))
         log("paged decode steps")
+        shared_op = wd.kind == "prefix"
         paged = run_decode(inp, True, args.steps, args.warmup, args.replicas,
-                           device)
+                           device, shared_op)
+        if shared_op:
+            log("paged decode steps without prefix sharing")
+            plain = run_decode(inp, True, args.steps, args.warmup,
+                               args.replicas, device)
         if not args.no_contig:
             log("contiguous decode steps")
             contig = run_decode(inp, False, args.steps, args.warmup,
@@ -699,7 +726,9 @@ def main() -> int:
             "num_seqs": wd.num_seqs, "num_q_heads": wd.num_q_heads,
             "num_kv_heads": wd.num_kv_heads, "head_dim": wd.head_dim,
             "block_size": wd.block_size, "context": ctx_desc[wd.name],
-            "step": "append+upload+reshape_and_cache+paged_attn_decode",
+            "step": "append+upload+reshape_and_cache+" + (
+                "paged_attn_decode_shared_prefix" if plain else
+                "paged_attn_decode"),
             "replicas": args.replicas,
         },
         "roofline": {
@@ -707,14 +736,19 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": recorded_traffic(wd.name),
-            "kernel": "paged_attn_decode (decode_sk_kernel + "
-                      "decode_combine_kernel)",
+            "kernel": ("paged_attn_decode_shared_prefix (prefill_mfma_kernel"
+                       "<true,true> + decode_sk_kernel + decode_combine_kernel)"
+                       if plain else "paged_attn_decode (decode_sk_kernel + "
+                       "decode_combine_kernel)"),
             "bytes_per_launch": int(paged["bytes_per_step"]),
             "ms_per_launch": round(paged["decode_op_ms_mean"], 4),
         },
         "decode_paged": {k: round(v, 4) for k, v in paged.items()},
         "memory": memory_waste(inp, lmax_reserved),
     }
+    if plain:
+        line["decode_paged_without_sharing"] = {k: round(v, 4)
+                                                for k, v in plain.items()}
     if contig:
         line["decode_contig"] = {k: round(v, 4) for k, v in contig.items()}
         line["decode_paged_vs_contig_overhead"] = round(

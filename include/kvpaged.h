@@ -211,6 +211,48 @@ kv_status contig_attn_decode(void* out, const void* q, const void* k,
                              size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
+ * Decode with shared prefixes. Same result as paged_attn_decode (same
+ * arguments up to block_size), for batches where groups of consecutive
+ * sequences hold the same first tokens in the same physical blocks: a
+ * prompt forked with kv_block_share, its blocks at refcount > 1
+ * ["Makale Bülteni — PagedAttention ve vLLM", "İddia ve Gerçeklik";
+ * "PagedAttention Nedir?", "Prefix Sharing Nasıl Çalışır?"]. The shared
+ * tokens' K/V are read once per group instead of once per sequence.
+ *   group_starts  device int32 [num_groups + 1]: group g is sequences
+ *                 group_starts[g] .. group_starts[g+1]-1; the groups must
+ *                 partition 0..num_seqs-1 in order (a sequence that shares
+ *                 nothing is a group of one with shared_lens 0).
+ *   shared_lens   device int32 [num_groups]: leading tokens of every
+ *                 member's context that sit in the same physical blocks as
+ *                 the group's first member's; read through that member's
+ *                 table. Must not exceed any member's context_lens.
+ *   num_groups, max_group_size (largest group), max_shared_len (largest
+ *                 shared_lens entry): host bounds that size the launch.
+ * Shared tokens are used in whole 16-token groups (the rest of a partial
+ * group is read per sequence). Values outside these rules keep memory
+ * accesses in bounds but make the affected outputs meaningless.
+ * The workspace must hold kv_decode_shared_prefix_workspace_bytes() bytes.
+ * The sharing pass needs bf16, head_dim 128, (Hq/Hkv) % 4 == 0, block_size
+ * % 16 == 0 and at most 4096 sequences; other calls (and max_shared_len <
+ * 16) run paged_attn_decode unchanged. */
+size_t kv_decode_shared_prefix_workspace_bytes(int32_t num_seqs,
+                                               int32_t num_q_heads,
+                                               int32_t num_kv_heads,
+                                               int32_t head_dim,
+                                               int32_t max_context,
+                                               int32_t max_shared_len);
+
+kv_status paged_attn_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+    const int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, const int32_t* group_starts,
+    const int32_t* shared_lens, int32_t num_groups, int32_t max_group_size,
+    int32_t max_shared_len, float scale, kv_dtype dtype, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
  * Chunked prefill attention. Sequence s has cu_q_lens[s+1]-cu_q_lens[s]
  * queries at absolute positions q_start_pos[s] + i and a context of
  * context_lens[s] tokens already in the cache (including this chunk's

@@ -43,6 +43,15 @@
 //     multiplied by 0, so NaN in unused slots cannot leak.
 // Generic path (fp32, or shapes the fast path does not cover): one wave per
 // (sequence, query head), lanes over head_dim, tokens in order.
+//
+// Shared prefix (paged_attn_decode_shared_prefix): when groups of sequences
+// hold the same first tokens in the same physical blocks (a forked prompt,
+// blocks at refcount > 1 ["Makale Bülteni — PagedAttention ve vLLM",
+// "İddia ve Gerçeklik"; "PagedAttention Nedir?", "Prefix Sharing Nasıl
+// Çalışır?"]), an MFMA pass (prefill.hip) attends every member's query to
+// the shared tokens, reading them once per group, and leaves exact partials.
+// The stream-K pass above then covers only each sequence's own tokens and
+// folds those partials in; the result is the same attention.
 
 #include <stdlib.h>
 
@@ -82,7 +91,15 @@ struct DecodeArgs {
   int32_t n_chunks;     // chunks per (KV head, head block)
   float* ws_o;          // [n_chunks, 2, Hq, D] unnormalised partial outputs
   float* ws_ml;         // [n_chunks, 2, Hq, 2] (reference max, sum)
-  int32_t* ws_cs;       // [S + 1] token offsets of the sequences
+  int32_t* ws_cs;       // [S + 1] tile offsets of the sequences
+  // shared prefix (all NULL / 0 for plain decode)
+  const int32_t* plen;  // [S] leading tokens covered by the prefix partials
+  const float* pre_o;   // [n_psplit, pre_stride, Hq, D]
+  const float* pre_ml;  // [n_psplit, pre_stride, Hq, 2]
+  int32_t n_psplit;
+  int32_t pre_stride;   // sequences between two pieces of pre_o / pre_ml
+  float* whole_o;       // [S, Hq, D] own part of a sequence in one chunk
+  float* whole_ml;      // [S, Hq, 2]
 };
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
@@ -97,6 +114,32 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
     c = a.seq_stride;
   }
   return c;
+}
+
+// Leading tokens of sequence s (context L) that the prefix partials cover;
+// a multiple of 16, so the sequence's own tiles start on a 16-token group.
+__device__ __forceinline__ int shared_of(const DecodeArgs& a, int s, int L) {
+  if (!a.plen) return 0;
+  int p = a.plen[s];
+  p = p < 0 ? 0 : (p > L ? L : p);
+  return p & ~15;
+}
+
+// Folds piece (mi, li, acc_i[8]) into the running (M, Ls, acc).
+__device__ __forceinline__ void fold_piece(float& M, float& Ls, float* acc,
+                                           float mi, float li, f32x4 lo4,
+                                           f32x4 hi4) {
+  if (mi == -INFINITY) return;
+  const float m_new = fmaxf(M, mi);
+  const float old_scale = fast_exp2(M - m_new);
+  const float new_scale = fast_exp2(mi - m_new);
+  M = m_new;
+  Ls = Ls * old_scale + li * new_scale;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[e] = acc[e] * old_scale + lo4[e] * new_scale;
+    acc[4 + e] = acc[4 + e] * old_scale + hi4[e] * new_scale;
+  }
 }
 
 __device__ __forceinline__ int tiles_of(int tokens) {
@@ -138,7 +181,10 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     const int lo = tid * per;
     const int hi = min(S, lo + per);
     int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += tiles_of(clamp_ctx(a, i, PAGED));
+    for (int i = lo; i < hi; ++i) {
+      const int L = clamp_ctx(a, i, PAGED);
+      sum += tiles_of(L - shared_of(a, i, L));
+    }
     s_part[tid] = sum;
     __syncthreads();
     // inclusive Hillis-Steele scan of the 256 partial sums
@@ -151,7 +197,8 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     int run = s_part[tid] - sum;
     for (int i = lo; i < hi; ++i) {
       s_cs[i] = run;
-      run += tiles_of(clamp_ctx(a, i, PAGED));
+      const int L = clamp_ctx(a, i, PAGED);
+      run += tiles_of(L - shared_of(a, i, L));
     }
     if (tid == kWaves * kWave - 1) s_cs[S] = s_part[tid];
     __syncthreads();
@@ -190,8 +237,9 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     const int hi_t = min(c1 - seq_lo, nt);
     pos = seq_lo + hi_t;
     const int L = clamp_ctx(a, s, PAGED);
-    const int lo = kTile * lo_t;
-    const int hi = min(kTile * hi_t, L);
+    const int P = shared_of(a, s, L);  // tokens before the own tiles
+    const int lo = P + kTile * lo_t;
+    const int hi = min(P + kTile * hi_t, L);
 
     const int qh = g * a.group + (h_valid ? h_in_group : 0);
     bf16x8 qop[4];  // Q^T: B operand, head r16, d = 32 i + 8 grp + e
@@ -378,7 +426,18 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
         }
       }
       const int head = g * a.group + hblk * kHeadBlk + h;
-      if (whole) {
+      if (whole && P > 0) {
+        // own part done; decode_combine_kernel adds the prefix partials
+        const int64_t idx = (int64_t)s * a.hq + head;
+        float* po = a.whole_o + idx * kD + 8 * c;
+        *reinterpret_cast<f32x4*>(po) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<f32x4*>(po + 4) =
+            f32x4{acc[4], acc[5], acc[6], acc[7]};
+        if (c == 0) {
+          a.whole_ml[2 * idx] = M;
+          a.whole_ml[2 * idx + 1] = Ls;
+        }
+      } else if (whole) {
         const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
         u32x4 ov;
 #pragma unroll
@@ -401,7 +460,8 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   }
 }
 
-// Exact merge of the partials of a sequence that spans several chunks:
+// Exact merge of the partials of a sequence that spans several chunks
+// (and of its shared-prefix partials, if any):
 // o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i with M = max_i m_i, for
 // every query head. Grid (sequence, query head), one wave each: lane
 // (j, c) = (lane / 16, lane % 16) folds pieces j, j+4, ... of d chunk c (8
@@ -419,36 +479,52 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   const int total = cs[a.num_seqs];
   const int seq_lo = cs[s], seq_hi = cs[s + 1];
   bf16* out = (bf16*)a.out + ((int64_t)s * a.hq + h) * kD;
-  if (seq_hi == seq_lo) {
+  // the shared-prefix path is paged only
+  const int P = a.plen ? shared_of(a, s, clamp_ctx(a, s, true)) : 0;
+  const int n_pre = P > 0 ? a.n_psplit : 0;
+  int n_own = 0, ca = 0;
+  bool own_whole = false;  // own part in one chunk, left in whole_o
+  if (seq_hi > seq_lo) {
+    const int C = chunk_tiles(total, a.n_chunks);
+    ca = seq_lo / C;
+    const int cb = (seq_hi - 1) / C;
+    if (ca == cb) {
+      if (n_pre == 0) return;  // written whole by decode_sk_kernel
+      own_whole = true;
+      n_own = 1;
+    } else {
+      n_own = cb - ca + 1;
+    }
+  } else if (n_pre == 0) {
     if (j == 0) st16(out + 8 * c, u32x4{0, 0, 0, 0});
     return;
   }
-  const int C = chunk_tiles(total, a.n_chunks);
-  const int ca = seq_lo / C, cb = (seq_hi - 1) / C;
-  if (ca == cb) return;  // written whole by decode_sk_kernel
-  const int n = cb - ca + 1;
+  const int n = n_own + n_pre;
   float M = -INFINITY, L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
   for (int i = j; i < n; i += 4) {
-    // piece i: chunk ca + i; slot 1 (first piece) for i == 0, else slot 0
-    const int64_t idx = ((int64_t)(ca + i) * 2 + (i == 0 ? 1 : 0)) * a.hq + h;
-    const float mi = a.ws_ml[2 * idx];
-    const float li = a.ws_ml[2 * idx + 1];
-    const f32x4 lo4 = *reinterpret_cast<const f32x4*>(a.ws_o + idx * kD + 8 * c);
-    const f32x4 hi4 =
-        *reinterpret_cast<const f32x4*>(a.ws_o + idx * kD + 8 * c + 4);
-    if (mi == -INFINITY) continue;
-    const float m_new = fmaxf(M, mi);
-    const float old_scale = fast_exp2(M - m_new);
-    const float new_scale = fast_exp2(mi - m_new);
-    M = m_new;
-    L = L * old_scale + li * new_scale;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] = acc[e] * old_scale + lo4[e] * new_scale;
-      acc[4 + e] = acc[4 + e] * old_scale + hi4[e] * new_scale;
+    const float* po;
+    const float* pml;
+    if (own_whole && i == 0) {
+      const int64_t idx = (int64_t)s * a.hq + h;
+      po = a.whole_o + idx * kD;
+      pml = a.whole_ml + 2 * idx;
+    } else if (i < n_own) {
+      // own piece i: chunk ca + i; slot 1 (first piece) for i == 0, else 0
+      const int64_t idx =
+          ((int64_t)(ca + i) * 2 + (i == 0 ? 1 : 0)) * a.hq + h;
+      po = a.ws_o + idx * kD;
+      pml = a.ws_ml + 2 * idx;
+    } else {
+      const int64_t idx =
+          ((int64_t)(i - n_own) * a.pre_stride + s) * a.hq + h;
+      po = a.pre_o + idx * kD;
+      pml = a.pre_ml + 2 * idx;
     }
+    fold_piece(M, L, acc, pml[0], pml[1],
+               *reinterpret_cast<const f32x4*>(po + 8 * c),
+               *reinterpret_cast<const f32x4*>(po + 8 * c + 4));
   }
   // merge the four lane groups (lanes c, c + 16, c + 32, c + 48)
   float Mall = fmaxf(M, __shfl_xor(M, 16));
@@ -631,6 +707,13 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
       b.out = (bf16*)a.out + (size_t)s0 * a.hq * kD;
       b.q = (const bf16*)a.q + (size_t)s0 * a.hq * kD;
       b.ctx = a.ctx + s0;
+      if (a.plen) {
+        b.plen = a.plen + s0;
+        b.pre_o = a.pre_o + (size_t)s0 * a.hq * kD;
+        b.pre_ml = a.pre_ml + (size_t)s0 * a.hq * 2;
+        b.whole_o = a.whole_o + (size_t)s0 * a.hq * kD;
+        b.whole_ml = a.whole_ml + (size_t)s0 * a.hq * 2;
+      }
       if (paged) {
         b.bt = a.bt + (size_t)s0 * a.bt_stride;
       } else {
@@ -669,7 +752,163 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
   return KV_OK;
 }
 
+// Shared-prefix pieces: enough MFMA workgroups for two per CU, at least 256
+// keys per piece, pieces a multiple of 64 keys.
+int env_psplit_override() {
+  static int cached = -2;
+  if (cached == -2) {
+    const char* e = getenv("KVPAGED_PREFIX_SPLITS");
+    cached = e ? atoi(e) : 0;
+  }
+  return cached;
+}
+
+void choose_psplit(int num_seqs, int hq, int max_shared, int* nsplit,
+                   int* ksplit) {
+  const int ms = max_shared < 16 ? 16 : max_shared;
+  const int rowblocks = (num_seqs + 31) / 32;
+  const int per_split = rowblocks * (hq / 4);
+  int n = (2 * device_cus() + per_split - 1) / per_split;
+  if (env_psplit_override() > 0) n = env_psplit_override();
+  const int max_n = (ms + 255) / 256;
+  n = n < 1 ? 1 : (n > max_n ? max_n : n);
+  const int ks = (((ms + n - 1) / n) + 63) & ~63;
+  *ksplit = ks;
+  *nsplit = (ms + ks - 1) / ks;
+}
+
+bool shared_fast_ok(kv_dtype dtype, int hq, int hkv, int head_dim,
+                    int block_size) {
+  return dtype == KV_BF16 && head_dim == kD && block_size % 16 == 0 &&
+         hkv > 0 && hq % hkv == 0 && (hq / hkv) % 4 == 0;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// [plen: S int32][pre_o, pre_ml: nsplit pieces][whole_o, whole_ml]
+size_t shared_extra_bytes(int num_seqs, int hq, int nsplit) {
+  return align256((size_t)num_seqs * sizeof(int32_t)) +
+         (size_t)(nsplit + 1) * num_seqs * hq * (kD + 2) * sizeof(float);
+}
+
 }  // namespace
+
+extern "C" size_t kv_decode_shared_prefix_workspace_bytes(
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t max_context, int32_t max_shared_len) {
+  const size_t base = kv_decode_workspace_bytes(num_seqs, num_q_heads,
+                                                num_kv_heads, head_dim,
+                                                max_context);
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      !shared_fast_ok(KV_BF16, num_q_heads, num_kv_heads, head_dim, 16))
+    return base;
+  int nsplit, ksplit;
+  choose_psplit(num_seqs, num_q_heads, max_shared_len, &nsplit, &ksplit);
+  return align256(base) + shared_extra_bytes(num_seqs, num_q_heads, nsplit);
+}
+
+extern "C" kv_status paged_attn_decode_shared_prefix(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+    const int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, const int32_t* group_starts,
+    const int32_t* shared_lens, int32_t num_groups, int32_t max_group_size,
+    int32_t max_shared_len, float scale, kv_dtype dtype, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* name = "paged_attn_decode_shared_prefix";
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.ctx = context_lens;
+  a.max_ctx = max_context;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale_log2 = scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  if (num_groups < 0 || max_group_size < 0 || max_shared_len < 0 ||
+      max_context < 0 || num_seqs < 0)
+    return kvp_fail(KV_EINVAL, "%s: negative size argument", name);
+  if (num_seqs > 0 && (num_groups < 1 || num_groups > num_seqs ||
+                       max_group_size < 1 || max_group_size > num_seqs))
+    return kvp_fail(KV_EINVAL,
+                    "%s: need 1 <= num_groups <= num_seqs and 1 <= "
+                    "max_group_size <= num_seqs", name);
+  // Shapes without the MFMA prefix pass, or no shared tokens: the plain
+  // decode computes the same attention.
+  if (num_seqs <= 0 || max_shared_len < 16 ||
+      !shared_fast_ok(dtype, num_q_heads, num_kv_heads, head_dim,
+                      block_size) ||
+      num_seqs > kMaxSeqs)
+    return run_decode(name, true, a, dtype, workspace, workspace_bytes, st);
+  if (!group_starts || !shared_lens || !workspace)
+    return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
+  const size_t need = kv_decode_shared_prefix_workspace_bytes(
+      num_seqs, num_q_heads, num_kv_heads, head_dim, max_context,
+      max_shared_len);
+  if (workspace_bytes < need)
+    return kvp_fail(KV_EINVAL, "%s: workspace of %zu bytes needed, %zu given",
+                    name, need, workspace_bytes);
+  int nsplit, ksplit;
+  choose_psplit(num_seqs, num_q_heads, max_shared_len, &nsplit, &ksplit);
+  const size_t base = align256(kv_decode_workspace_bytes(
+      num_seqs, num_q_heads, num_kv_heads, head_dim, max_context));
+  char* wp = (char*)workspace + base;
+  int32_t* plen = (int32_t*)wp;
+  float* pre_o = (float*)(wp + align256((size_t)num_seqs * sizeof(int32_t)));
+  float* pre_ml = pre_o + (size_t)nsplit * num_seqs * num_q_heads * kD;
+  float* whole_o = pre_ml + (size_t)nsplit * num_seqs * num_q_heads * 2;
+  float* whole_ml = whole_o + (size_t)num_seqs * num_q_heads * kD;
+  if (block_size <= 0 || bt_stride <= 0 || num_blocks <= 0 || !block_tables ||
+      !context_lens || !q || !k_cache || !v_cache || !out)
+    return kvp_fail(KV_EINVAL, "%s: bad paging arguments or NULL pointer",
+                    name);
+  if ((int64_t)num_blocks * block_size * num_kv_heads > INT32_MAX)
+    return kvp_fail(KV_EUNSUPPORTED, "%s: pool of more than 2^31 head rows",
+                    name);
+  if (!(a.scale_log2 > 0.f) || !(a.scale_log2 < INFINITY))
+    return kvp_fail(KV_EINVAL, "%s: scale must be finite and > 0", name);
+  KvpPrefixJob job = {};
+  job.q = q;
+  job.k = k_cache;
+  job.v = v_cache;
+  job.bt = block_tables;
+  job.bt_stride = bt_stride;
+  job.num_blocks = num_blocks;
+  job.block_size = block_size;
+  job.ctx = context_lens;
+  job.members = num_seqs;
+  job.hq = num_q_heads;
+  job.hkv = num_kv_heads;
+  job.group_starts = group_starts;
+  job.shared_lens = shared_lens;
+  job.num_groups = num_groups;
+  job.max_group_size = max_group_size;
+  job.nsplit = nsplit;
+  job.ksplit = ksplit;
+  job.scale_log2 = a.scale_log2;
+  job.plen = plen;
+  job.po = pre_o;
+  job.pml = pre_ml;
+  kv_status r = kvp_prefix_partials(job, st);
+  if (r != KV_OK) return r;
+  a.plen = plen;
+  a.pre_o = pre_o;
+  a.pre_ml = pre_ml;
+  a.n_psplit = nsplit;
+  a.pre_stride = num_seqs;
+  a.whole_o = whole_o;
+  a.whole_ml = whole_ml;
+  return run_decode(name, true, a, dtype, workspace, workspace_bytes, st);
+}
 
 extern "C" int32_t kv_decode_chunks(int32_t num_q_heads, int32_t num_kv_heads) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)

@@ -4,3 +4,36 @@
 
 // Record a message for kv_last_error() and return `st`.
 kv_status kvp_fail(kv_status st, const char* fmt, ...);
+
+#include <hip/hip_runtime.h>
+
+// One launch of the shared-prefix partial attention (prefill.hip): the
+// decode queries of the members of each group against the group's shared
+// tokens, read through the first member's table, split into nsplit pieces
+// of ksplit keys. Writes plen[member] (shared tokens the member's own pass
+// skips) and the partials po/pml. bf16, head_dim 128, (Hq/Hkv) % 4 == 0,
+// block_size % 16 == 0.
+struct KvpPrefixJob {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* bt;
+  int32_t bt_stride;
+  int32_t num_blocks;
+  int32_t block_size;
+  const int32_t* ctx;
+  int32_t members;
+  int32_t hq;
+  int32_t hkv;
+  const int32_t* group_starts;
+  const int32_t* shared_lens;
+  int32_t num_groups;
+  int32_t max_group_size;
+  int32_t nsplit;
+  int32_t ksplit;
+  float scale_log2;
+  int32_t* plen;
+  float* po;
+  float* pml;
+};
+kv_status kvp_prefix_partials(const KvpPrefixJob& job, hipStream_t st);

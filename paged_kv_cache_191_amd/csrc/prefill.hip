@@ -24,6 +24,13 @@
 //   * Causal and context masks are selects (-inf scores, zero V rows), only
 //     in the tiles that need them.
 // Generic path (other dtypes/shapes): one wave per (query row, head).
+//
+// The same tile loop also serves decode with a shared prefix: the queries
+// of all member sequences of a group (one decode query each, any number of
+// members) attend to the group's shared tokens, which are read once per
+// group through the first member's block table. The key range is split
+// into pieces; each piece leaves an unnormalised partial (max, sum, output)
+// per (member, head) that the decode kernels fold in exactly.
 
 #include <type_traits>
 
@@ -59,6 +66,15 @@ struct PrefillArgs {
   int32_t head_dim;
   float scale_log2;
   int32_t causal;
+  // shared-prefix partials (cu_q = group starts, num_seqs = groups)
+  const int32_t* shared;  // [groups] shared tokens of each group
+  int32_t* plen;          // [members] shared tokens each member skips
+  float* po;              // [nsplit, members, Hq, D] partial outputs
+  float* pml;             // [nsplit, members, Hq, 2] (reference max, sum)
+  int32_t members;
+  int32_t nsplit;
+  int32_t ksplit;         // keys per piece (multiple of 64)
+  int32_t rowblocks;      // query blocks of kBM members per group
 };
 
 __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int s,
@@ -91,32 +107,81 @@ __device__ __forceinline__ int v_elem(int row, int d) {
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-template <bool PAGED>
+// PREFIX: the shared-prefix partials described at the top of this file
+// (paged only). Otherwise chunked prefill writing normalised outputs.
+template <bool PAGED, bool PREFIX>
 __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
     PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sk[2][kBN * kD];
   __shared__ __attribute__((aligned(16))) bf16 sv[2][kBN * kD];
 
-  const int s = blockIdx.z;
-  const int qbeg = a.cu_q[s];
-  const int nq = a.cu_q[s + 1] - qbeg;
-  // Heaviest (latest) query blocks first.
-  const int q0 = (gridDim.x - 1 - blockIdx.x) * kBM;
-  if (q0 >= nq) return;
-  const int ctx = clamp_ctx(a, s, PAGED);
-  const int nrows = min(kBM, nq - q0);
-  const int pos_first = a.q_start[s] + q0;
-  const int pos_last = pos_first + nrows - 1;
-  int kv_end = a.causal ? min(ctx, pos_last + 1) : ctx;
-  kv_end = kv_end < 0 ? 0 : kv_end;
-
   const int tid = threadIdx.x;
+  // PREFIX: one linear grid, query blocks fastest, so the workgroups that
+  // share a K/V piece run together.
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z, split = 0;
+  if (PREFIX) {
+    const int hblocks = a.hq / kWaves;
+    int t = blockIdx.x;
+    bx = t % a.rowblocks;
+    t /= a.rowblocks;
+    by = t % hblocks;
+    t /= hblocks;
+    split = t % a.nsplit;
+    bz = t / a.nsplit;
+  }
+  const int s = bz;
+  int qbeg, nq;
+  if (PREFIX) {
+    qbeg = min(max(a.cu_q[s], 0), a.members);
+    nq = min(max(a.cu_q[s + 1], qbeg), a.members) - qbeg;
+  } else {
+    qbeg = a.cu_q[s];
+    nq = a.cu_q[s + 1] - qbeg;
+  }
+  // Heaviest (latest) query blocks first.
+  const int q0 = (PREFIX ? bx : (gridDim.x - 1 - bx)) * kBM;
+  if (q0 >= nq) return;
+  const int nrows = min(kBM, nq - q0);
+  // Table row read for the keys: the sequence, or the group's first member.
+  const int trow = PREFIX ? qbeg : s;
+  const int ctx = clamp_ctx(a, trow, PAGED);
+  int kv_beg = 0, kv_end, pos_first = 0;
+  if (PREFIX) {
+    // Shared tokens, rounded down to whole 16-token groups so that the
+    // members' own tokens start on a group boundary.
+    const int P = min(max(a.shared[s], 0), ctx) & ~15;
+    if (by == 0 && split == 0)
+      for (int i = tid; i < nrows; i += kWaves * kWave) {
+        const int m = qbeg + q0 + i;
+        a.plen[m] = min(P, clamp_ctx(a, m, PAGED)) & ~15;
+      }
+    if (P == 0) return;
+    kv_beg = split * a.ksplit;
+    kv_end = min(P, kv_beg + a.ksplit);
+  } else {
+    pos_first = a.q_start[s] + q0;
+    const int pos_last = pos_first + nrows - 1;
+    kv_end = a.causal ? min(ctx, pos_last + 1) : ctx;
+    kv_end = kv_end < 0 ? 0 : kv_end;
+  }
+
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g2 = lane >> 5;
-  const int h = blockIdx.y * kWaves + w;
-  const int kvh = (blockIdx.y * kWaves) / a.group;
+  const int h = by * kWaves + w;
+  const int kvh = (by * kWaves) / a.group;
+  if (PREFIX && kv_beg >= kv_end) {
+    // an empty piece (a group with fewer shared tokens than the launch's
+    // longest): record "no keys" for its rows
+    if (l32 < nrows && g2 == 0) {
+      const int64_t idx =
+          ((int64_t)split * a.members + qbeg + q0 + l32) * a.hq + h;
+      a.pml[2 * idx] = -INFINITY;
+      a.pml[2 * idx + 1] = 0.f;
+    }
+    return;
+  }
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query l32,
   // d = 16 ks + 8 g2 + e.
@@ -149,7 +214,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
     int base;
     if (PAGED) {
       base = min(g0, (kv_end - 1) & ~15);
-      int b = a.bt[(int64_t)s * a.bt_stride + base / a.block_size];
+      int b = a.bt[(int64_t)trow * a.bt_stride + base / a.block_size];
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
       grp_row = (int64_t)b * a.hkv * a.block_size + head_row0 +
                 base % a.block_size;
@@ -256,11 +321,13 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
     }
   };
 
+  const int j_beg = kv_beg / kBN;  // kv_beg is a multiple of kBN
   const int n_tiles = (kv_end + kBN - 1) / kBN;
   // Tiles below n_full need no mask: every key is in the context and at or
   // before the first query of the block.
   int n_full = kv_end / kBN;
-  if (a.causal) n_full = min(n_full, (pos_first + 1) / kBN);
+  if (!PREFIX && a.causal) n_full = min(n_full, (pos_first + 1) / kBN);
+  n_full = max(n_full, j_beg);
   // Two loops (unmasked tiles, then the boundary tiles) so that the
   // accumulators never pass through a join inside the loop. Each iteration:
   // wait for this tile's loads, barrier (they are visible and every wave is
@@ -274,11 +341,32 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
       tile(buf, j, masked);
     }
   };
-  if (n_tiles > 0) load_tile(0, 0);
-  run_tiles(0, n_full, std::false_type{});
+  if (n_tiles > j_beg) load_tile(j_beg & 1, j_beg);
+  run_tiles(j_beg, n_full, std::false_type{});
   run_tiles(n_full, n_tiles, std::true_type{});
 
   l_part += __shfl_xor(l_part, 32);
+  if (PREFIX) {
+    if (l32 < nrows) {
+      // unnormalised partial; O^T: lane holds row l32, d = 32 db + 8 a4 +
+      // 4 g2 + (0..3)
+      const int64_t idx =
+          ((int64_t)split * a.members + qbeg + q0 + l32) * a.hq + h;
+      float* po = a.po + idx * kD + 4 * g2;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * a4) =
+              f32x4{oacc[db][4 * a4], oacc[db][4 * a4 + 1],
+                    oacc[db][4 * a4 + 2], oacc[db][4 * a4 + 3]};
+      if (g2 == 0) {
+        a.pml[2 * idx] = m_run;
+        a.pml[2 * idx + 1] = l_part;
+      }
+    }
+    return;
+  }
   if (l32 < nrows) {
     const float inv = l_part > 0.f ? 1.f / l_part : 0.f;
     // O^T: lane holds query l32, d = 32 db + 8 (r / 4) + 4 g2 + r % 4.
@@ -389,9 +477,9 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
   if (fast) {
     dim3 grid((a.max_q_len + kBM - 1) / kBM, a.hq / kWaves, a.num_seqs);
     if (paged)
-      prefill_mfma_kernel<true><<<grid, kWaves * kWave, 0, st>>>(a);
+      prefill_mfma_kernel<true, false><<<grid, kWaves * kWave, 0, st>>>(a);
     else
-      prefill_mfma_kernel<false><<<grid, kWaves * kWave, 0, st>>>(a);
+      prefill_mfma_kernel<false, false><<<grid, kWaves * kWave, 0, st>>>(a);
     KVP_LAUNCH_CHECK(name);
     return KV_OK;
   }
@@ -418,6 +506,41 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
 }
 
 }  // namespace
+
+kv_status kvp_prefix_partials(const KvpPrefixJob& j, hipStream_t st) {
+  PrefillArgs a = {};
+  a.q = j.q;
+  a.k = j.k;
+  a.v = j.v;
+  a.bt = j.bt;
+  a.bt_stride = j.bt_stride;
+  a.num_blocks = j.num_blocks;
+  a.block_size = j.block_size;
+  a.ctx = j.ctx;
+  a.cu_q = j.group_starts;
+  a.num_seqs = j.num_groups;
+  a.hq = j.hq;
+  a.hkv = j.hkv;
+  a.group = j.hq / j.hkv;
+  a.head_dim = kD;
+  a.scale_log2 = j.scale_log2;
+  a.causal = 0;
+  a.shared = j.shared_lens;
+  a.plen = j.plen;
+  a.po = j.po;
+  a.pml = j.pml;
+  a.members = j.members;
+  a.nsplit = j.nsplit;
+  a.ksplit = j.ksplit;
+  a.rowblocks = (j.max_group_size + kBM - 1) / kBM;
+  const int64_t n = (int64_t)a.rowblocks * (a.hq / kWaves) * a.nsplit *
+                    j.num_groups;
+  if (n > INT32_MAX)
+    return kvp_fail(KV_EUNSUPPORTED, "shared-prefix decode: too many groups");
+  prefill_mfma_kernel<true, true><<<(unsigned)n, kWaves * kWave, 0, st>>>(a);
+  KVP_LAUNCH_CHECK("paged_attn_decode_shared_prefix");
+  return KV_OK;
+}
 
 extern "C" kv_status paged_attn_prefill(
     void* out, const void* q, const int32_t* cu_q_lens,

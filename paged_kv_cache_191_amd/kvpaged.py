@@ -67,6 +67,12 @@ SIGNATURES = {
                                  _SZ, _P]),
     "contig_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32,
                                   _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
+    "kv_decode_shared_prefix_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32,
+                                                      _I32, _I32]),
+    "paged_attn_decode_shared_prefix": (_I32, [_P, _P, _P, _P, _I32, _P, _I32,
+                                               _P, _I32, _I32, _I32, _I32,
+                                               _I32, _I32, _P, _P, _I32, _I32,
+                                               _I32, _F, _I32, _P, _SZ, _P]),
     "paged_attn_prefill": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _P,
                                   _I32, _P, _I32, _I32, _I32, _I32, _I32, _F,
                                   _I32, _I32, _P]),
@@ -352,6 +358,55 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         int(max_context), S, hq, hkv, d, bs, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "paged_attn_decode")
+
+
+def kv_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads,
+                                            num_kv_heads, head_dim,
+                                            max_context, max_shared_len) -> int:
+    return int(lib().kv_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context,
+        max_shared_len))
+
+
+def decode_shared_prefix_workspace(num_seqs, num_q_heads, num_kv_heads,
+                                   head_dim, max_context, max_shared_len,
+                                   device="cuda"):
+    """A device buffer of kv_decode_shared_prefix_workspace_bytes."""
+    torch = _torch()
+    n = kv_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context,
+        max_shared_len)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def paged_attn_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
+                                    context_lens, max_context: int,
+                                    group_starts, shared_lens,
+                                    max_group_size: int, max_shared_len: int,
+                                    scale: float, workspace=None,
+                                    stream=None) -> None:
+    """group_starts: device int32 [G + 1]; shared_lens: device int32 [G]."""
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    G = shared_lens.shape[0]
+    if group_starts.shape[0] != G + 1:
+        raise ValueError("group_starts must have num_groups + 1 entries")
+    if workspace is None:
+        workspace = decode_shared_prefix_workspace(S, hq, hkv, d, max_context,
+                                                   max_shared_len, q.device)
+    st = lib().paged_attn_decode_shared_prefix(
+        _dev(out, "out", q.dtype), _dev(q, "q"),
+        _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        nb, _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context), S, hq, hkv, d, bs,
+        _dev(group_starts, "group_starts", torch.int32),
+        _dev(shared_lens, "shared_lens", torch.int32), G,
+        int(max_group_size), int(max_shared_len), float(scale),
+        _dtype_code(q), _dev(workspace, "workspace"), workspace.numel(),
+        _stream(stream))
+    _check(st, "paged_attn_decode_shared_prefix")
 
 
 def contig_attn_decode(out, q, k, v, context_lens, max_context: int,
