@@ -112,6 +112,19 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float v) {
   return static_cast<bf16>(v);
 }
 
+// Workgroup order for the 8 XCDs of MI355X: consecutive workgroup ids are
+// dispatched round-robin over the XCDs, and each XCD has its own L2. This
+// maps dispatch id `id` (of n) to a logical index such that XCD x runs the
+// contiguous logical range x*n/8 .. (x+1)*n/8 - 1 in order, so workgroups
+// that are neighbours in logical order (and read the same K/V) share an L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_order(int id, int n) {
+  const int per = n / kXcds, rem = n % kXcds;
+  const int x = id % kXcds, slot = id / kXcds;
+  const int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return base + slot;
+}
+
 }  // namespace kvp
 
 #define KVP_LAUNCH_CHECK(what)                                              \

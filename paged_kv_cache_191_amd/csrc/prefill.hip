@@ -112,22 +112,40 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 template <bool PAGED, bool PREFIX>
 __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
     PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 sk[2][kBN * kD];
-  __shared__ __attribute__((aligned(16))) bf16 sv[2][kBN * kD];
+  // Double-buffered K/V tiles as four separate LDS objects, with the
+  // buffer of each tile fixed at compile time: the compiler can then see
+  // that reads of one buffer do not alias the asynchronous loads into the
+  // other and does not wait for those loads before computing.
+  __shared__ __attribute__((aligned(16))) bf16 sk0[kBN * kD];
+  __shared__ __attribute__((aligned(16))) bf16 sk1[kBN * kD];
+  __shared__ __attribute__((aligned(16))) bf16 sv0[kBN * kD];
+  __shared__ __attribute__((aligned(16))) bf16 sv1[kBN * kD];
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
   // PREFIX: one linear grid, query blocks fastest, so the workgroups that
   // share a K/V piece run together.
-  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z, split = 0;
+  // Workgroups are taken in XCD order (xcd_order): the query blocks of one
+  // (sequence, head block), which stream the same K/V tiles, run together
+  // on one XCD and share its L2.
+  int bx, by, bz, split = 0;
   if (PREFIX) {
     const int hblocks = a.hq / kWaves;
-    int t = blockIdx.x;
+    int t = xcd_order(blockIdx.x, gridDim.x);
     bx = t % a.rowblocks;
     t /= a.rowblocks;
     by = t % hblocks;
     t /= hblocks;
     split = t % a.nsplit;
     bz = t / a.nsplit;
+  } else {
+    const int t = xcd_order(
+        blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+        gridDim.x * gridDim.y * gridDim.z);
+    bx = t % gridDim.x;
+    by = (t / gridDim.x) % gridDim.y;
+    bz = t / (gridDim.x * gridDim.y);
   }
   const int s = bz;
   int qbeg, nq;
@@ -205,16 +223,33 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
   // instruction, straight from global memory into LDS (lane i of an
   // instruction fills 16-byte LDS unit i). Keys past the context re-read
   // the last valid key (finite data; their scores are masked).
+  const int n_tiles_all = (kv_end + kBN - 1) / kBN;
   const int ld_row = lane >> 4;           // row within the 4-row group
   const int ld_pc = lane & 15;            // physical 16-byte chunk
   const int64_t head_row0 = (int64_t)kvh * (PAGED ? a.block_size : a.seq_stride);
-  auto load_tile = [&](int buf, int j) {
+  // Physical block of this wave's 16 keys of tile j (paged), read one tile
+  // ahead of its use so that the table read's latency is hidden.
+  auto group_base = [&](int j) __attribute__((always_inline)) {
+    return min(j * kBN + 16 * w, (kv_end - 1) & ~15);
+  };
+  // The table is read through the constant address space (it is not
+  // written during the kernel) so that the read is a scalar load, whose
+  // wait does not also wait for the tile loads in flight.
+  typedef __attribute__((address_space(4))) const int32_t* cptr_t;
+  auto table_block = [&](int j) __attribute__((always_inline)) {
+    if (!PAGED) return 0;
+    j = min(j, n_tiles_all - 1);
+    return ((cptr_t)a.bt)[(int64_t)trow * a.bt_stride +
+                          group_base(j) / a.block_size];
+  };
+  auto load_tile = [&](auto buf, int j, int b) __attribute__((always_inline)) {
+    bf16* skb = decltype(buf)::value ? sk1 : sk0;
+    bf16* svb = decltype(buf)::value ? sv1 : sv0;
     const int g0 = j * kBN + 16 * w;      // first key of this wave's group
     int64_t grp_row;                       // head row of key `base`
     int base;
     if (PAGED) {
-      base = min(g0, (kv_end - 1) & ~15);
-      int b = a.bt[(int64_t)trow * a.bt_stride + base / a.block_size];
+      base = group_base(j);
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
       grp_row = (int64_t)b * a.hkv * a.block_size + head_row0 +
                 base % a.block_size;
@@ -231,18 +266,19 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
       const int vc = ld_pc ^ ((0xAC60 >> (4 * (row & 3))) & 15);
       __builtin_amdgcn_global_load_lds(
           (gptr_t)((const bf16*)a.k + hrow * kD + 8 * kc),
-          (lptr_t)(&sk[buf][(16 * w + 4 * n) * kD]), 16, 0, 0);
+          (lptr_t)(&skb[(16 * w + 4 * n) * kD]), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(
           (gptr_t)((const bf16*)a.v + hrow * kD + 8 * vc),
-          (lptr_t)(&sv[buf][(16 * w + 4 * n) * kD]), 16, 0, 0);
+          (lptr_t)(&svb[(16 * w + 4 * n) * kD]), 16, 0, 0);
     }
   };
 
   // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto tile = [&](int buf, int j, auto masked) {
+  auto tile = [&](auto buf, int j, auto masked)
+      __attribute__((always_inline)) {
     constexpr bool MASK = decltype(masked)::value;
-    const bf16* K_ = sk[buf];
-    const bf16* V_ = sv[buf];
+    const bf16* K_ = decltype(buf)::value ? sk1 : sk0;
+    const bf16* V_ = decltype(buf)::value ? sv1 : sv0;
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -322,26 +358,46 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
   };
 
   const int j_beg = kv_beg / kBN;  // kv_beg is a multiple of kBN
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  const int n_tiles = n_tiles_all;
   // Tiles below n_full need no mask: every key is in the context and at or
   // before the first query of the block.
   int n_full = kv_end / kBN;
   if (!PREFIX && a.causal) n_full = min(n_full, (pos_first + 1) / kBN);
   n_full = max(n_full, j_beg);
   // Two loops (unmasked tiles, then the boundary tiles) so that the
-  // accumulators never pass through a join inside the loop. Each iteration:
-  // wait for this tile's loads, barrier (they are visible and every wave is
-  // done with the other buffer), start the next tile's loads, compute.
-  auto run_tiles = [&](int j0, int j1, auto masked) {
-    for (int j = j0; j < j1; ++j) {
-      const int buf = j & 1;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (j + 1 < n_tiles) load_tile(buf ^ 1, j + 1);
-      tile(buf, j, masked);
+  // accumulators never pass through a join inside the loop. Tile j lives in
+  // buffer j & 1; each loop is unrolled by two so that the buffer of every
+  // step is static. A step waits for its tile's loads, meets the barrier
+  // (they are visible and every wave is done with the other buffer),
+  // starts the next tile's loads, then computes.
+  int next_block = 0;  // table entry of the next tile to load
+  auto step = [&](auto buf, int j, auto masked)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < n_tiles) {
+      if constexpr (decltype(buf)::value) load_tile(B0{}, j + 1, next_block);
+      else load_tile(B1{}, j + 1, next_block);
     }
+    next_block = table_block(j + 2);
+    tile(buf, j, masked);
   };
-  if (n_tiles > j_beg) load_tile(j_beg & 1, j_beg);
+  auto run_tiles = [&](int j0, int j1, auto masked)
+      __attribute__((always_inline)) {
+    int j = j0;
+    if ((j & 1) && j < j1) step(B1{}, j++, masked);
+    for (; j + 1 < j1; j += 2) {
+      step(B0{}, j, masked);
+      step(B1{}, j + 1, masked);
+    }
+    if (j < j1) step(B0{}, j, masked);
+  };
+  if (n_tiles > j_beg) {
+    const int b0 = table_block(j_beg);
+    if (j_beg & 1) load_tile(B1{}, j_beg, b0);
+    else load_tile(B0{}, j_beg, b0);
+    next_block = table_block(j_beg + 1);
+  }
   run_tiles(j_beg, n_full, std::false_type{});
   run_tiles(n_full, n_tiles, std::true_type{});
 
@@ -476,6 +532,8 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
                     a.group % kWaves == 0 && (!paged || a.block_size % 16 == 0);
   if (fast) {
     dim3 grid((a.max_q_len + kBM - 1) / kBM, a.hq / kWaves, a.num_seqs);
+    if ((int64_t)grid.x * grid.y * grid.z > INT32_MAX)
+      return kvp_fail(KV_EUNSUPPORTED, "%s: too many query blocks", name);
     if (paged)
       prefill_mfma_kernel<true, false><<<grid, kWaves * kWave, 0, st>>>(a);
     else
