@@ -441,6 +441,463 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two-group ("ping-pong") variant of the MFMA path. A workgroup of 8 waves
+// owns 64 query rows x 4 query heads of one KV head: waves 0-3 (group 0)
+// take rows 0-31, waves 4-7 (group 1) rows 32-63, one head per wave, and
+// both groups read the same K/V tiles from LDS. A SIMD runs the matrix
+// unit and the vector ALU at the same time only for different waves, so
+// the groups are kept half a step apart by workgroup barriers: in each
+// phase one group issues its MFMA block (PV of the previous tile, QK of the
+// next) while the other runs the softmax of its current tile. Per tile t:
+//   phase A(t): group 0 softmax(t)           group 1 PV(t-1), QK(t)
+//   phase B(t): group 0 PV(t), QK(t+1)       group 1 softmax(t)
+// K tiles are loaded two tiles ahead and V tiles one tile ahead (issued at
+// the start of B phases), into static double buffers.
+// ---------------------------------------------------------------------------
+constexpr int kPPWaves = 8;
+constexpr int kPPRows = 64;
+
+// Barrier between phases. wait_vm: first wait for this wave's tile loads
+// and LDS reads (at the end of A phases: the next phase reads the loaded
+// tiles, and loads into the buffers read so far start after it). B phases
+// end without a wait: no LDS buffer is rewritten before the next A phase
+// ends. The scheduling barriers and empty asm statements keep the compiler
+// from moving instructions or memory accesses across the barrier.
+__device__ __forceinline__ void phase_barrier(bool wait_vm) {
+  if (wait_vm) __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt: 0
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool PAGED, bool PREFIX>
+__global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
+    PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 sk0[kBN * kD];
+  __shared__ __attribute__((aligned(16))) bf16 sk1[kBN * kD];
+  __shared__ __attribute__((aligned(16))) bf16 sv0[kBN * kD];
+  __shared__ __attribute__((aligned(16))) bf16 sv1[kBN * kD];
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using NoMask = std::false_type;
+  using Mask = std::true_type;
+
+  const int tid = threadIdx.x;
+  const int hblocks = a.hq / 4;
+  int bx, by, bz, split = 0;
+  if (PREFIX) {
+    int t = xcd_order(blockIdx.x, gridDim.x);
+    bx = t % a.rowblocks;
+    t /= a.rowblocks;
+    by = t % hblocks;
+    t /= hblocks;
+    split = t % a.nsplit;
+    bz = t / a.nsplit;
+  } else {
+    const int t = xcd_order(
+        blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+        gridDim.x * gridDim.y * gridDim.z);
+    bx = t % gridDim.x;
+    by = (t / gridDim.x) % gridDim.y;
+    bz = t / (gridDim.x * gridDim.y);
+  }
+  const int s = bz;
+  int qbeg, nq;
+  if (PREFIX) {
+    qbeg = min(max(a.cu_q[s], 0), a.members);
+    nq = min(max(a.cu_q[s + 1], qbeg), a.members) - qbeg;
+  } else {
+    qbeg = a.cu_q[s];
+    nq = a.cu_q[s + 1] - qbeg;
+  }
+  const int q0 = (PREFIX ? bx : (gridDim.x - 1 - bx)) * kPPRows;
+  if (q0 >= nq) return;
+  const int nrows = min(kPPRows, nq - q0);
+  const int trow = PREFIX ? qbeg : s;
+  const int ctx = clamp_ctx(a, trow, PAGED);
+  int kv_beg = 0, kv_end, pos_first = 0;
+  if (PREFIX) {
+    const int P = min(max(a.shared[s], 0), ctx) & ~15;
+    if (by == 0 && split == 0)
+      for (int i = tid; i < nrows; i += kPPWaves * kWave) {
+        const int m = qbeg + q0 + i;
+        a.plen[m] = min(P, clamp_ctx(a, m, PAGED)) & ~15;
+      }
+    if (P == 0) return;
+    kv_beg = split * a.ksplit;
+    kv_end = min(P, kv_beg + a.ksplit);
+  } else {
+    pos_first = a.q_start[s] + q0;
+    const int pos_last = pos_first + nrows - 1;
+    kv_end = a.causal ? min(ctx, pos_last + 1) : ctx;
+    kv_end = kv_end < 0 ? 0 : kv_end;
+  }
+
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g2 = lane >> 5;
+  const int h = by * 4 + (w & 3);
+  const int kvh = (by * 4) / a.group;
+  const int row0 = q0 + 32 * grp;  // first query row of this group
+  if (PREFIX && kv_beg >= kv_end) {
+    if (row0 + l32 < nrows + q0 && g2 == 0) {
+      const int64_t idx =
+          ((int64_t)split * a.members + qbeg + row0 + l32) * a.hq + h;
+      a.pml[2 * idx] = -INFINITY;
+      a.pml[2 * idx + 1] = 0.f;
+    }
+    return;
+  }
+  if (kv_end <= kv_beg) {
+    // no key at all (empty context): zero rows
+    if (!PREFIX && row0 + l32 < q0 + nrows) {
+      bf16* op = (bf16*)a.out + ((int64_t)(qbeg + row0 + l32) * a.hq + h) * kD +
+                 64 * g2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st16(op + 8 * i, u32x4{0, 0, 0, 0});
+    }
+    return;
+  }
+
+  // Q^T (B operand of S^T = K Q^T): lane holds query l32 of its group,
+  // d = 16 ks + 8 g2 + e. Rows past the block repeat its last row.
+  bf16x8 qop[8];
+  {
+    const int qr = qbeg + min(row0 + l32, q0 + nrows - 1);
+    const bf16* qp = (const bf16*)a.q + ((int64_t)qr * a.hq + h) * kD + 8 * g2;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(ld16(qp + 16 * ks));
+  }
+  const int my_pos = pos_first + 32 * grp + l32;
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x16 sacc[2];
+  u32x4 pk[4];  // P^T of the last softmax, packed for the PV MFMAs
+
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  const int j_beg = kv_beg / kBN;
+  // Tiles below n_full need no mask for this group's rows.
+  int n_full = kv_end / kBN;
+  if (!PREFIX && a.causal) n_full = min(n_full, (pos_first + 32 * grp + 1) / kBN);
+  n_full = max(n_full, j_beg);
+
+  // ---- tile loads: wave w moves keys 8w..8w+7 of a tile (2 instructions
+  // of 4 rows per tensor); table entries are read one step ahead.
+  const int ld_row = lane >> 4;
+  const int ld_pc = lane & 15;
+  const int64_t head_row0 =
+      (int64_t)kvh * (PAGED ? a.block_size : a.seq_stride);
+  typedef __attribute__((address_space(4))) const int32_t* cptr_t;
+  auto group_base = [&](int j) __attribute__((always_inline)) {
+    return min((j * kBN + 8 * w) & ~15, (kv_end - 1) & ~15);
+  };
+  auto table_block = [&](int j) __attribute__((always_inline)) {
+    if (!PAGED) return 0;
+    j = min(j, n_tiles - 1);
+    return ((cptr_t)a.bt)[(int64_t)trow * a.bt_stride +
+                          group_base(j) / a.block_size];
+  };
+  // Per-lane parts of the load addresses: the 16-byte chunk each lane moves
+  // (swizzled), as a byte offset inside a head row.
+  int chunk_off[2][2];  // [K/V][n]
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int row = 8 * w + 4 * n + ld_row;
+    chunk_off[0][n] = 16 * (ld_pc ^ (row & 15));
+    chunk_off[1][n] = 16 * (ld_pc ^ ((0xAC60 >> (4 * (row & 3))) & 15));
+  }
+  auto load = [&](auto is_v, auto buf, int j, int b)
+      __attribute__((always_inline)) {
+    constexpr bool V = decltype(is_v)::value;
+    bf16* dst = V ? (decltype(buf)::value ? sv1 : sv0)
+                  : (decltype(buf)::value ? sk1 : sk0);
+    int64_t grp_row;
+    int base;
+    if (PAGED) {
+      base = group_base(j);
+      b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+      grp_row = (int64_t)b * a.hkv * a.block_size + head_row0 +
+                base % a.block_size;
+    } else {
+      base = 0;
+      grp_row = (int64_t)s * a.hkv * a.seq_stride + head_row0;
+    }
+    // wave-uniform byte address of head row `base`, plus a 32-bit per-lane
+    // offset (row within the 16-key group, and the chunk)
+    const char* gbase = (const char*)(V ? a.v : a.k) + grp_row * (kD * 2);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int key = min(j * kBN + 8 * w + 4 * n + ld_row, kv_end - 1);
+      const int off = (key - base) * (kD * 2) + chunk_off[V ? 1 : 0][n];
+      __builtin_amdgcn_global_load_lds((gptr_t)(gbase + off),
+                                       (lptr_t)(&dst[(8 * w + 4 * n) * kD]),
+                                       16, 0, 0);
+    }
+  };
+  using KT = std::false_type;
+  using VT = std::true_type;
+
+  // ---- MFMA blocks
+  // The scheduler is asked to keep each LDS read two steps ahead of its
+  // MFMA (short read-ahead keeps register use down).
+  auto qk = [&](auto buf) __attribute__((always_inline)) {
+    const bf16* K_ = decltype(buf)::value ? sk1 : sk0;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 ka = as_bf16x8(
+            ld16(&K_[k_elem(32 * kb + l32, 16 * ks + 8 * g2)]));
+        sacc[kb] = mfma32(ka, qop[ks], sacc[kb]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int trs = lane & 15;
+  const int trd = 16 * ((lane >> 4) & 1) + 4 * (trs & 3);
+  auto pv = [&](auto buf) __attribute__((always_inline)) {
+    const bf16* V_ = decltype(buf)::value ? sv1 : sv0;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 pop = as_bf16x8(pk[kk]);
+      const int r0 = 16 * kk + 4 * g2 + (trs >> 2);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u32x2 lo = lds_read_tr16(&V_[v_elem(r0, 32 * db + trd)]);
+        const u32x2 hi = lds_read_tr16(&V_[v_elem(r0 + 8, 32 * db + trd)]);
+        const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        oacc[db] = mfma32(va, pop, oacc[db]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // ---- softmax of tile j (vector ALU): masks, lazy rescale, P^T packed.
+  auto softmax = [&](int j, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(masked)::value;
+    const int tile0 = j * kBN;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (MASK) {
+          const int key = tile0 + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+          const bool dead = key >= kv_end || (a.causal && key > my_pos);
+          sacc[kb][r] = dead ? -INFINITY : sacc[kb][r];
+        }
+        mx = fmaxf(mx, sacc[kb][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    }
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(sacc[kb][r], a.scale_log2,
+                                                 -m_ref));
+        sacc[kb][r] = p;
+        psum += p;
+      }
+    l_part += psum;
+    // P^T: lane holds query l32; k-slot e of MFMA kk <-> key
+    // 16 kk + 8 (e / 4) + 4 g2 + e % 4 of the tile.
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int kb = kk >> 1;
+      const int rb = 8 * (kk & 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pk[kk][e] = pack_bf16(sacc[kb][rb + 2 * e], sacc[kb][rb + 2 * e + 1]);
+    }
+    // Pin the results here: the softmax must finish in its own phase, not
+    // sink into the next MFMA block of this wave.
+    asm volatile("" : "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]), "+v"(pk[3]),
+                 "+v"(l_part), "+v"(m_run));
+  };
+
+  // ---- loads issued at the start of phase B(t): K(t+2) into buffer t&1,
+  // V(t+1) into buffer (t+1)&1 (both freed by the end of phase A(t)).
+  int kblk_next = 0, kblk_next2 = 0;  // table entries of tiles t+1, t+2
+  auto issue_loads = [&](auto par, int t) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    if (t + 2 < n_tiles) {
+      if constexpr (PAR) load(KT{}, B1{}, t + 2, kblk_next2);
+      else load(KT{}, B0{}, t + 2, kblk_next2);
+    }
+    if (t + 1 < n_tiles) {
+      if constexpr (PAR) load(VT{}, B0{}, t + 1, kblk_next);
+      else load(VT{}, B1{}, t + 1, kblk_next);
+    }
+    kblk_next = kblk_next2;
+    kblk_next2 = table_block(t + 3);
+  };
+
+  // ---- prologue: K(j_beg) (and, at the start of the first phase, K(j_beg+1)
+  // and V(j_beg)).
+  {
+    const int b0 = table_block(j_beg);
+    if (j_beg & 1) load(KT{}, B1{}, j_beg, b0);
+    else load(KT{}, B0{}, j_beg, b0);
+    kblk_next = b0;  // V(j_beg) uses the same entry
+    kblk_next2 = table_block(j_beg + 1);
+  }
+  phase_barrier(true);
+  // first phase ("B(j_beg - 1)"): loads K(j_beg+1), V(j_beg); group 0
+  // computes QK(j_beg); group 1 waits.
+  {
+    const int t = j_beg - 1;
+    if (j_beg + 1 < n_tiles) {
+      if ((j_beg + 1) & 1) load(KT{}, B1{}, j_beg + 1, kblk_next2);
+      else load(KT{}, B0{}, j_beg + 1, kblk_next2);
+    }
+    if (j_beg & 1) load(VT{}, B1{}, j_beg, kblk_next);
+    else load(VT{}, B0{}, j_beg, kblk_next);
+    kblk_next = kblk_next2;
+    kblk_next2 = table_block(t + 3);
+    if (grp == 0) {
+      if (j_beg & 1) qk(B1{});
+      else qk(B0{});
+    }
+  }
+  phase_barrier(false);
+
+  if (grp == 0) {
+    // A(t): softmax(t); B(t): loads, PV(t) from V[t&1], QK(t+1) from K[(t+1)&1]
+    auto iter = [&](auto par, int t, auto masked) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par)::value;
+      softmax(t, masked);
+      phase_barrier(true);
+      // The loads go after this block's V reads: the compiler makes a
+      // transposed LDS read wait for every LDS load in flight.
+      if constexpr (PAR) pv(B1{}); else pv(B0{});
+      issue_loads(par, t);
+      if (t + 1 < n_tiles) {
+        if constexpr (PAR) qk(B0{}); else qk(B1{});
+      }
+      phase_barrier(false);
+    };
+    auto run = [&](int t0, int t1, auto masked) __attribute__((always_inline)) {
+      int t = t0;
+      if ((t & 1) && t < t1) iter(B1{}, t++, masked);
+      for (; t + 1 < t1; t += 2) {
+        iter(B0{}, t, masked);
+        iter(B1{}, t + 1, masked);
+      }
+      if (t < t1) iter(B0{}, t, masked);
+    };
+    run(j_beg, n_full, NoMask{});
+    run(n_full, n_tiles, Mask{});
+  } else {
+    // A(t): PV(t-1) from V[(t-1)&1], QK(t) from K[t&1]; B(t): loads, softmax(t)
+    auto iter = [&](auto par, int t, auto masked, auto with_pv)
+        __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par)::value;
+      if constexpr (decltype(with_pv)::value) {
+        if constexpr (PAR) pv(B0{}); else pv(B1{});
+      }
+      if constexpr (PAR) qk(B1{}); else qk(B0{});
+      phase_barrier(true);
+      issue_loads(par, t);
+      softmax(t, masked);
+      phase_barrier(false);
+    };
+    auto run = [&](int t0, int t1, auto masked) __attribute__((always_inline)) {
+      int t = t0;
+      if (t == j_beg && t < t1) {  // first tile: no PV yet
+        if (t & 1) iter(B1{}, t, masked, std::false_type{});
+        else iter(B0{}, t, masked, std::false_type{});
+        ++t;
+      }
+      if ((t & 1) && t < t1) iter(B1{}, t++, masked, std::true_type{});
+      for (; t + 1 < t1; t += 2) {
+        iter(B0{}, t, masked, std::true_type{});
+        iter(B1{}, t + 1, masked, std::true_type{});
+      }
+      if (t < t1) iter(B0{}, t, masked, std::true_type{});
+    };
+    run(j_beg, n_full, NoMask{});
+    run(n_full, n_tiles, Mask{});
+    // last phase: PV(n_tiles - 1)
+    if ((n_tiles - 1) & 1) pv(B1{});
+    else pv(B0{});
+  }
+
+  // ---- outputs of this group's rows
+  l_part += __shfl_xor(l_part, 32);
+  const bool row_ok = row0 + l32 < q0 + nrows;
+  if (PREFIX) {
+    if (row_ok) {
+      const int64_t idx =
+          ((int64_t)split * a.members + qbeg + row0 + l32) * a.hq + h;
+      float* po = a.po + idx * kD + 4 * g2;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * a4) =
+              f32x4{oacc[db][4 * a4], oacc[db][4 * a4 + 1],
+                    oacc[db][4 * a4 + 2], oacc[db][4 * a4 + 3]};
+      if (g2 == 0) {
+        a.pml[2 * idx] = m_run;
+        a.pml[2 * idx + 1] = l_part;
+      }
+    }
+    return;
+  }
+  if (row_ok) {
+    const float inv = l_part > 0.f ? 1.f / l_part : 0.f;
+    bf16* op = (bf16*)a.out + ((int64_t)(qbeg + row0 + l32) * a.hq + h) * kD +
+               4 * g2;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        u32x2 v2;
+        v2[0] = pack_bf16(oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv);
+        v2[1] =
+            pack_bf16(oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * a4) = v2;
+      }
+  }
+}
+
 // Generic path: one wave per (query head, query row, sequence).
 template <typename T, bool PAGED>
 __global__ __launch_bounds__(kWave) void prefill_generic_kernel(PrefillArgs a) {
@@ -531,13 +988,13 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
   const bool fast = dtype == KV_BF16 && a.head_dim == kD &&
                     a.group % kWaves == 0 && (!paged || a.block_size % 16 == 0);
   if (fast) {
-    dim3 grid((a.max_q_len + kBM - 1) / kBM, a.hq / kWaves, a.num_seqs);
+    dim3 grid((a.max_q_len + kPPRows - 1) / kPPRows, a.hq / 4, a.num_seqs);
     if ((int64_t)grid.x * grid.y * grid.z > INT32_MAX)
       return kvp_fail(KV_EUNSUPPORTED, "%s: too many query blocks", name);
     if (paged)
-      prefill_mfma_kernel<true, false><<<grid, kWaves * kWave, 0, st>>>(a);
+      prefill_pp_kernel<true, false><<<grid, kPPWaves * kWave, 0, st>>>(a);
     else
-      prefill_mfma_kernel<false, false><<<grid, kWaves * kWave, 0, st>>>(a);
+      prefill_pp_kernel<false, false><<<grid, kPPWaves * kWave, 0, st>>>(a);
     KVP_LAUNCH_CHECK(name);
     return KV_OK;
   }
@@ -590,12 +1047,12 @@ kv_status kvp_prefix_partials(const KvpPrefixJob& j, hipStream_t st) {
   a.members = j.members;
   a.nsplit = j.nsplit;
   a.ksplit = j.ksplit;
-  a.rowblocks = (j.max_group_size + kBM - 1) / kBM;
-  const int64_t n = (int64_t)a.rowblocks * (a.hq / kWaves) * a.nsplit *
+  a.rowblocks = (j.max_group_size + kPPRows - 1) / kPPRows;
+  const int64_t n = (int64_t)a.rowblocks * (a.hq / 4) * a.nsplit *
                     j.num_groups;
   if (n > INT32_MAX)
     return kvp_fail(KV_EUNSUPPORTED, "shared-prefix decode: too many groups");
-  prefill_mfma_kernel<true, true><<<(unsigned)n, kWaves * kWave, 0, st>>>(a);
+  prefill_pp_kernel<true, true><<<(unsigned)n, kPPWaves * kWave, 0, st>>>(a);
   KVP_LAUNCH_CHECK("paged_attn_decode_shared_prefix");
   return KV_OK;
 }
