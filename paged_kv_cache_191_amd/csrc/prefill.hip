@@ -8,21 +8,21 @@
 // only the tile loader's row addressing different.
 //
 // Fast path (bf16, head_dim 128, group % 4 == 0, block_size % 16 == 0):
-//   * A workgroup of 4 waves owns 32 query rows of one sequence and 4 query
+//   * A workgroup of 8 waves owns 64 query rows of one sequence and 4 query
 //     heads of one KV head (grouped-query packing: the K/V tile in LDS serves
-//     all four heads). Each wave owns one head.
-//   * Keys advance in tiles of 64. The whole workgroup loads a tile with
-//     16-byte loads (16 lanes per 256-byte token row), gathering rows through
-//     the block table (4 consecutive keys share a block), into a double
-//     buffer in LDS: K row-major, V transposed (V^T) with a column order that
-//     matches the order in which S^T leaves P in registers. The next tile's
-//     global loads are in flight while the current tile is computed.
+//     all four heads and all 64 rows). Each wave owns one head and 32 rows.
+//   * Keys advance in tiles of 64, gathered through the block table (16
+//     consecutive keys share a block) with 16-byte direct global-to-LDS
+//     loads into double buffers: unpadded 256-byte rows, XOR-swizzled so
+//     that the MFMA operand reads hit distinct banks.
 //   * Per tile a wave computes S^T = K Q^T (keys x queries) with
 //     v_mfma_f32_32x32x16_bf16, an online softmax in the log2 domain (one
-//     query per lane column), and O^T += V^T P^T with the same MFMA; P stays
-//     in the lanes that computed it.
-//   * Causal and context masks are selects (-inf scores, zero V rows), only
-//     in the tiles that need them.
+//     query per lane column), and O^T += V^T P^T with the same MFMA (V^T
+//     through transposing LDS reads); P stays in the lanes that computed it.
+//   * The two halves of the workgroup alternate between MFMA and softmax
+//     work (see prefill_pp_kernel).
+//   * Causal and context masks are selects (-inf scores), only in the tiles
+//     that need them.
 // Generic path (other dtypes/shapes): one wave per (query row, head).
 //
 // The same tile loop also serves decode with a shared prefix: the queries
@@ -41,9 +41,7 @@ namespace {
 using namespace kvp;
 
 constexpr int kD = 128;
-constexpr int kBM = 32;            // query rows per workgroup
 constexpr int kBN = 64;            // keys per tile
-constexpr int kWaves = 4;          // = query heads per workgroup
 
 struct PrefillArgs {
   void* out;
@@ -74,7 +72,7 @@ struct PrefillArgs {
   int32_t members;
   int32_t nsplit;
   int32_t ksplit;         // keys per piece (multiple of 64)
-  int32_t rowblocks;      // query blocks of kBM members per group
+  int32_t rowblocks;      // query blocks of 64 members per group
 };
 
 __device__ __forceinline__ int clamp_ctx(const PrefillArgs& a, int s,
@@ -106,340 +104,6 @@ __device__ __forceinline__ int v_elem(int row, int d) {
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
-
-// PREFIX: the shared-prefix partials described at the top of this file
-// (paged only). Otherwise chunked prefill writing normalised outputs.
-template <bool PAGED, bool PREFIX>
-__global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(
-    PrefillArgs a) {
-  // Double-buffered K/V tiles as four separate LDS objects, with the
-  // buffer of each tile fixed at compile time: the compiler can then see
-  // that reads of one buffer do not alias the asynchronous loads into the
-  // other and does not wait for those loads before computing.
-  __shared__ __attribute__((aligned(16))) bf16 sk0[kBN * kD];
-  __shared__ __attribute__((aligned(16))) bf16 sk1[kBN * kD];
-  __shared__ __attribute__((aligned(16))) bf16 sv0[kBN * kD];
-  __shared__ __attribute__((aligned(16))) bf16 sv1[kBN * kD];
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-
-  const int tid = threadIdx.x;
-  // PREFIX: one linear grid, query blocks fastest, so the workgroups that
-  // share a K/V piece run together.
-  // Workgroups are taken in XCD order (xcd_order): the query blocks of one
-  // (sequence, head block), which stream the same K/V tiles, run together
-  // on one XCD and share its L2.
-  int bx, by, bz, split = 0;
-  if (PREFIX) {
-    const int hblocks = a.hq / kWaves;
-    int t = xcd_order(blockIdx.x, gridDim.x);
-    bx = t % a.rowblocks;
-    t /= a.rowblocks;
-    by = t % hblocks;
-    t /= hblocks;
-    split = t % a.nsplit;
-    bz = t / a.nsplit;
-  } else {
-    const int t = xcd_order(
-        blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
-        gridDim.x * gridDim.y * gridDim.z);
-    bx = t % gridDim.x;
-    by = (t / gridDim.x) % gridDim.y;
-    bz = t / (gridDim.x * gridDim.y);
-  }
-  const int s = bz;
-  int qbeg, nq;
-  if (PREFIX) {
-    qbeg = min(max(a.cu_q[s], 0), a.members);
-    nq = min(max(a.cu_q[s + 1], qbeg), a.members) - qbeg;
-  } else {
-    qbeg = a.cu_q[s];
-    nq = a.cu_q[s + 1] - qbeg;
-  }
-  // Heaviest (latest) query blocks first.
-  const int q0 = (PREFIX ? bx : (gridDim.x - 1 - bx)) * kBM;
-  if (q0 >= nq) return;
-  const int nrows = min(kBM, nq - q0);
-  // Table row read for the keys: the sequence, or the group's first member.
-  const int trow = PREFIX ? qbeg : s;
-  const int ctx = clamp_ctx(a, trow, PAGED);
-  int kv_beg = 0, kv_end, pos_first = 0;
-  if (PREFIX) {
-    // Shared tokens, rounded down to whole 16-token groups so that the
-    // members' own tokens start on a group boundary.
-    const int P = min(max(a.shared[s], 0), ctx) & ~15;
-    if (by == 0 && split == 0)
-      for (int i = tid; i < nrows; i += kWaves * kWave) {
-        const int m = qbeg + q0 + i;
-        a.plen[m] = min(P, clamp_ctx(a, m, PAGED)) & ~15;
-      }
-    if (P == 0) return;
-    kv_beg = split * a.ksplit;
-    kv_end = min(P, kv_beg + a.ksplit);
-  } else {
-    pos_first = a.q_start[s] + q0;
-    const int pos_last = pos_first + nrows - 1;
-    kv_end = a.causal ? min(ctx, pos_last + 1) : ctx;
-    kv_end = kv_end < 0 ? 0 : kv_end;
-  }
-
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int g2 = lane >> 5;
-  const int h = by * kWaves + w;
-  const int kvh = (by * kWaves) / a.group;
-  if (PREFIX && kv_beg >= kv_end) {
-    // an empty piece (a group with fewer shared tokens than the launch's
-    // longest): record "no keys" for its rows
-    if (l32 < nrows && g2 == 0) {
-      const int64_t idx =
-          ((int64_t)split * a.members + qbeg + q0 + l32) * a.hq + h;
-      a.pml[2 * idx] = -INFINITY;
-      a.pml[2 * idx + 1] = 0.f;
-    }
-    return;
-  }
-
-  // Q^T as the B operand of S^T = K Q^T: lane holds query l32,
-  // d = 16 ks + 8 g2 + e.
-  bf16x8 qop[8];
-  {
-    const int qr = qbeg + q0 + min(l32, nrows - 1);
-    const bf16* qp = (const bf16*)a.q + ((int64_t)qr * a.hq + h) * kD + 8 * g2;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(ld16(qp + 16 * ks));
-  }
-  const int my_pos = pos_first + l32;
-
-  f32x16 oacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY, l_part = 0.f;
-
-  // Tile loader: wave w moves keys 16w..16w+15 of the tile, four rows per
-  // instruction, straight from global memory into LDS (lane i of an
-  // instruction fills 16-byte LDS unit i). Keys past the context re-read
-  // the last valid key (finite data; their scores are masked).
-  const int n_tiles_all = (kv_end + kBN - 1) / kBN;
-  const int ld_row = lane >> 4;           // row within the 4-row group
-  const int ld_pc = lane & 15;            // physical 16-byte chunk
-  const int64_t head_row0 = (int64_t)kvh * (PAGED ? a.block_size : a.seq_stride);
-  // Physical block of this wave's 16 keys of tile j (paged), read one tile
-  // ahead of its use so that the table read's latency is hidden.
-  auto group_base = [&](int j) __attribute__((always_inline)) {
-    return min(j * kBN + 16 * w, (kv_end - 1) & ~15);
-  };
-  // The table is read through the constant address space (it is not
-  // written during the kernel) so that the read is a scalar load, whose
-  // wait does not also wait for the tile loads in flight.
-  typedef __attribute__((address_space(4))) const int32_t* cptr_t;
-  auto table_block = [&](int j) __attribute__((always_inline)) {
-    if (!PAGED) return 0;
-    j = min(j, n_tiles_all - 1);
-    return ((cptr_t)a.bt)[(int64_t)trow * a.bt_stride +
-                          group_base(j) / a.block_size];
-  };
-  auto load_tile = [&](auto buf, int j, int b) __attribute__((always_inline)) {
-    bf16* skb = decltype(buf)::value ? sk1 : sk0;
-    bf16* svb = decltype(buf)::value ? sv1 : sv0;
-    const int g0 = j * kBN + 16 * w;      // first key of this wave's group
-    int64_t grp_row;                       // head row of key `base`
-    int base;
-    if (PAGED) {
-      base = group_base(j);
-      b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      grp_row = (int64_t)b * a.hkv * a.block_size + head_row0 +
-                base % a.block_size;
-    } else {
-      base = 0;
-      grp_row = (int64_t)s * a.hkv * a.seq_stride + head_row0;
-    }
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int row = 16 * w + 4 * n + ld_row;               // tile row
-      const int key = min(g0 + 4 * n + ld_row, kv_end - 1);
-      const int64_t hrow = grp_row + (key - base);
-      const int kc = ld_pc ^ (row & 15);
-      const int vc = ld_pc ^ ((0xAC60 >> (4 * (row & 3))) & 15);
-      __builtin_amdgcn_global_load_lds(
-          (gptr_t)((const bf16*)a.k + hrow * kD + 8 * kc),
-          (lptr_t)(&skb[(16 * w + 4 * n) * kD]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (gptr_t)((const bf16*)a.v + hrow * kD + 8 * vc),
-          (lptr_t)(&svb[(16 * w + 4 * n) * kD]), 16, 0, 0);
-    }
-  };
-
-  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto tile = [&](auto buf, int j, auto masked)
-      __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(masked)::value;
-    const bf16* K_ = decltype(buf)::value ? sk1 : sk0;
-    const bf16* V_ = decltype(buf)::value ? sv1 : sv0;
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 ka = as_bf16x8(
-            ld16(&K_[k_elem(32 * kb + l32, 16 * ks + 8 * g2)]));
-        sacc[kb] = mfma32(ka, qop[ks], sacc[kb]);
-      }
-    }
-    // Raw scores; keys past the context or after the query -> -inf.
-    const int tile0 = j * kBN;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (MASK) {
-          const int key = tile0 + 32 * kb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-          const bool dead = key >= kv_end || (a.causal && key > my_pos);
-          sacc[kb][r] = dead ? -INFINITY : sacc[kb][r];
-        }
-        mx = fmaxf(mx, sacc[kb][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-    // Lazy rescaling (log2 domain): the reference max moves only when a
-    // score exceeds it by more than 2^8; the final division by the sum
-    // makes the result independent of the reference. A row with no visible
-    // key yet keeps m = -inf and p = 0.
-    if (__any(mx > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-    }
-    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[kb][r], a.scale_log2,
-                                                 -m_ref));
-        sacc[kb][r] = p;
-        psum += p;
-      }
-    l_part += psum;
-
-    // O^T += V^T P^T, 16 keys per MFMA. P^T (B operand): lane holds query
-    // l32, k-slot e <-> key 16 kk + 8 (e / 4) + 4 g2 + e % 4 of the tile,
-    // which is where S^T left it. V^T (A operand): two transpose reads give
-    // lane l (d = 32 db + l % 32) the same 8 keys.
-    const int trs = lane & 15;
-    const int trd = 16 * ((lane >> 4) & 1) + 4 * (trs & 3);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int kb = kk >> 1;
-      const int rb = 8 * (kk & 1);
-      u32x4 pb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pb[e] = pack_bf16(sacc[kb][rb + 2 * e], sacc[kb][rb + 2 * e + 1]);
-      const bf16x8 pop = as_bf16x8(pb);
-      const int r0 = 16 * kk + 4 * g2 + (trs >> 2);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const u32x2 lo = lds_read_tr16(&V_[v_elem(r0, 32 * db + trd)]);
-        const u32x2 hi = lds_read_tr16(&V_[v_elem(r0 + 8, 32 * db + trd)]);
-        const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        oacc[db] = mfma32(va, pop, oacc[db]);
-      }
-    }
-  };
-
-  const int j_beg = kv_beg / kBN;  // kv_beg is a multiple of kBN
-  const int n_tiles = n_tiles_all;
-  // Tiles below n_full need no mask: every key is in the context and at or
-  // before the first query of the block.
-  int n_full = kv_end / kBN;
-  if (!PREFIX && a.causal) n_full = min(n_full, (pos_first + 1) / kBN);
-  n_full = max(n_full, j_beg);
-  // Two loops (unmasked tiles, then the boundary tiles) so that the
-  // accumulators never pass through a join inside the loop. Tile j lives in
-  // buffer j & 1; each loop is unrolled by two so that the buffer of every
-  // step is static. A step waits for its tile's loads, meets the barrier
-  // (they are visible and every wave is done with the other buffer),
-  // starts the next tile's loads, then computes.
-  int next_block = 0;  // table entry of the next tile to load
-  auto step = [&](auto buf, int j, auto masked)
-      __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j + 1 < n_tiles) {
-      if constexpr (decltype(buf)::value) load_tile(B0{}, j + 1, next_block);
-      else load_tile(B1{}, j + 1, next_block);
-    }
-    next_block = table_block(j + 2);
-    tile(buf, j, masked);
-  };
-  auto run_tiles = [&](int j0, int j1, auto masked)
-      __attribute__((always_inline)) {
-    int j = j0;
-    if ((j & 1) && j < j1) step(B1{}, j++, masked);
-    for (; j + 1 < j1; j += 2) {
-      step(B0{}, j, masked);
-      step(B1{}, j + 1, masked);
-    }
-    if (j < j1) step(B0{}, j, masked);
-  };
-  if (n_tiles > j_beg) {
-    const int b0 = table_block(j_beg);
-    if (j_beg & 1) load_tile(B1{}, j_beg, b0);
-    else load_tile(B0{}, j_beg, b0);
-    next_block = table_block(j_beg + 1);
-  }
-  run_tiles(j_beg, n_full, std::false_type{});
-  run_tiles(n_full, n_tiles, std::true_type{});
-
-  l_part += __shfl_xor(l_part, 32);
-  if (PREFIX) {
-    if (l32 < nrows) {
-      // unnormalised partial; O^T: lane holds row l32, d = 32 db + 8 a4 +
-      // 4 g2 + (0..3)
-      const int64_t idx =
-          ((int64_t)split * a.members + qbeg + q0 + l32) * a.hq + h;
-      float* po = a.po + idx * kD + 4 * g2;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-          *reinterpret_cast<f32x4*>(po + 32 * db + 8 * a4) =
-              f32x4{oacc[db][4 * a4], oacc[db][4 * a4 + 1],
-                    oacc[db][4 * a4 + 2], oacc[db][4 * a4 + 3]};
-      if (g2 == 0) {
-        a.pml[2 * idx] = m_run;
-        a.pml[2 * idx + 1] = l_part;
-      }
-    }
-    return;
-  }
-  if (l32 < nrows) {
-    const float inv = l_part > 0.f ? 1.f / l_part : 0.f;
-    // O^T: lane holds query l32, d = 32 db + 8 (r / 4) + 4 g2 + r % 4.
-    bf16* op = (bf16*)a.out + ((int64_t)(qbeg + q0 + l32) * a.hq + h) * kD +
-               4 * g2;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        u32x2 v2;
-        v2[0] = pack_bf16(oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv);
-        v2[1] =
-            pack_bf16(oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * a4) = v2;
-      }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Two-group ("ping-pong") variant of the MFMA path. A workgroup of 8 waves
@@ -986,7 +650,7 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
     return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
   a.group = a.hq / a.hkv;
   const bool fast = dtype == KV_BF16 && a.head_dim == kD &&
-                    a.group % kWaves == 0 && (!paged || a.block_size % 16 == 0);
+                    a.group % 4 == 0 && (!paged || a.block_size % 16 == 0);
   if (fast) {
     dim3 grid((a.max_q_len + kPPRows - 1) / kPPRows, a.hq / 4, a.num_seqs);
     if ((int64_t)grid.x * grid.y * grid.z > INT32_MAX)
