@@ -277,33 +277,54 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
         b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
         row_lane = (b * a.hkv + g) * a.block_size + gpos % a.block_size;
       }
-      // Head row of token `off` of half hf of this wave's j-th tile here.
-      auto row_of = [&](int j, int hf, int off) -> int64_t {
+      // Addresses: a wave-uniform pointer to the head row of the first
+      // token of the 16-token group of half hf of this wave's j-th tile
+      // (groups past the context are replaced by the last context group),
+      // plus a 32-bit per-lane byte offset: row `off` of the group, in
+      // 0..15 (clamped to the context's last row for the contiguous
+      // layout), and the lane's 16-byte chunk.
+      auto half_start = [&](int j, int hf) -> int {
+        return min(t_al + kTile * (kb0 + w + kWaves * j) + 16 * hf,
+                   last_grp_pos);
+      };
+      auto half_ptr = [&](const bf16* base, int j, int hf) -> const char* {
+        int64_t row;
         if (PAGED)
-          return (int64_t)__builtin_amdgcn_readlane(row_lane, 2 * j + hf) +
-                 off;
-        const int k = kb0 + w + kWaves * j;
-        const int p = min(t_al + kTile * k + 16 * hf + off, hi - 1);
-        return seq_row0 + p;
+          row = __builtin_amdgcn_readlane(row_lane, 2 * j + hf);
+        else
+          row = seq_row0 + half_start(j, hf);
+        return (const char*)(base + row * kD);
+      };
+      auto lane_off = [&](int j, int hf, int off, int chunk) -> uint32_t {
+        const int r = PAGED ? off : min(off, hi - 1 - half_start(j, hf));
+        return (uint32_t)(r * (kD * 2) + 16 * chunk);
       };
       const int k_end = min(n_tiles, kb0 + kWaves * (kGroupsPerLoad / 2));
       for (int j = 0; kb0 + w + kWaves * j < k_end; ++j) {
         const int t = t_al + kTile * (kb0 + w + kWaves * j);
         // K: A operand of S^T (token r16 of each half, d = 32 i + 8 grp + e)
-        // K: A operand of S^T (token r16 of each half, d = 32 i + 8 grp + e)
         u32x4 kr[2][4];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const bf16* kp = kbase + row_of(j, hf, r16) * kD + 8 * grp;
+          const char* kp = half_ptr(kbase, j, hf);
+          const uint32_t ko = lane_off(j, hf, r16, grp);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) kr[hf][i] = ld16_stream(kp + 32 * i);
+          for (int i = 0; i < 4; ++i)
+            kr[hf][i] = ld16_stream(kp + ko + 64 * i);
         }
         // V: rows tau(grp, e) = 16 (e / 4) + 4 grp + e % 4, d-chunk r16
         u32x4 vr[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vr[e] = ld16_stream(vbase + row_of(j, e >> 2, 4 * grp + (e & 3)) * kD +
-                              8 * r16);
+        for (int hf = 0; hf < 2; ++hf) {
+          const char* vp = half_ptr(vbase, j, hf);
+#pragma unroll
+          for (int e = 4 * hf; e < 4 * hf + 4; ++e)
+            vr[e] = ld16_stream(vp + lane_off(j, hf, 4 * grp + (e & 3), r16));
+        }
+        // All 16 loads of the tile are issued before the first MFMA waits
+        // for any of them (the scheduler would otherwise start on the K half
+        // and issue the V loads late, halving the bytes in flight).
+        __builtin_amdgcn_sched_barrier(0);
 
         f32x4 sc[2];
 #pragma unroll
