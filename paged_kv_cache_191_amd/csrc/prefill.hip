@@ -42,6 +42,10 @@ using namespace kvp;
 
 constexpr int kD = 128;
 constexpr int kBN = 64;            // keys per tile
+// LDS reads issued ahead of the first MFMA of a QK / PV block (deeper
+// read-ahead measured no faster and costs registers)
+constexpr int kQkAhead = 2;
+constexpr int kPvAhead = 2;
 
 struct PrefillArgs {
   void* out;
@@ -55,6 +59,7 @@ struct PrefillArgs {
   int32_t bt_stride;
   int32_t num_blocks;
   int32_t block_size;
+  int32_t bs_shift;       // log2(block_size) when it is a power of two, else -1
   int32_t seq_stride;
   const int32_t* ctx;
   int32_t num_seqs;
@@ -262,6 +267,16 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
   const int64_t head_row0 =
       (int64_t)kvh * (PAGED ? a.block_size : a.seq_stride);
   typedef __attribute__((address_space(4))) const int32_t* cptr_t;
+  // block index and offset of a key position (shift and mask for the usual
+  // power-of-two block sizes)
+  auto blk_of = [&](int x) __attribute__((always_inline)) {
+    if (__builtin_expect(a.bs_shift >= 0, 1)) return x >> a.bs_shift;
+    return x / a.block_size;
+  };
+  auto off_in_blk = [&](int x) __attribute__((always_inline)) {
+    if (__builtin_expect(a.bs_shift >= 0, 1)) return x & (a.block_size - 1);
+    return x % a.block_size;
+  };
   auto group_base = [&](int j) __attribute__((always_inline)) {
     return min((j * kBN + 8 * w) & ~15, (kv_end - 1) & ~15);
   };
@@ -269,7 +284,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     if (!PAGED) return 0;
     j = min(j, n_tiles - 1);
     return ((cptr_t)a.bt)[(int64_t)trow * a.bt_stride +
-                          group_base(j) / a.block_size];
+                          blk_of(group_base(j))];
   };
   // Per-lane parts of the load addresses: the 16-byte chunk each lane moves
   // (swizzled), as a byte offset inside a head row.
@@ -291,7 +306,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
       base = group_base(j);
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
       grp_row = (int64_t)b * a.hkv * a.block_size + head_row0 +
-                base % a.block_size;
+                off_in_blk(base);
     } else {
       base = 0;
       grp_row = (int64_t)s * a.hkv * a.seq_stride + head_row0;
@@ -328,13 +343,13 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
         sacc[kb] = mfma32(ka, qop[ks], sacc[kb]);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 14; ++i) {
+    for (int i = 0; i < 16 - kQkAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   const int trs = lane & 15;
@@ -354,13 +369,13 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
         oacc[db] = mfma32(va, pop, oacc[db]);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 14; ++i) {
+    for (int i = 0; i < 16 - kPvAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kPvAhead, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   // ---- softmax of tile j (vector ALU): masks, lazy rescale, P^T packed.
@@ -649,6 +664,9 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
       (paged && !a.bt))
     return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
   a.group = a.hq / a.hkv;
+  a.bs_shift = (a.block_size > 0 && (a.block_size & (a.block_size - 1)) == 0)
+                   ? __builtin_ctz((unsigned)a.block_size)
+                   : -1;
   const bool fast = dtype == KV_BF16 && a.head_dim == kD &&
                     a.group % 4 == 0 && (!paged || a.block_size % 16 == 0);
   if (fast) {
@@ -695,6 +713,9 @@ kv_status kvp_prefix_partials(const KvpPrefixJob& j, hipStream_t st) {
   a.bt_stride = j.bt_stride;
   a.num_blocks = j.num_blocks;
   a.block_size = j.block_size;
+  a.bs_shift = (j.block_size > 0 && (j.block_size & (j.block_size - 1)) == 0)
+                   ? __builtin_ctz((unsigned)j.block_size)
+                   : -1;
   a.ctx = j.ctx;
   a.cu_q = j.group_starts;
   a.num_seqs = j.num_groups;
