@@ -736,7 +736,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": recorded_traffic(wd.name),
-            "kernel": ("paged_attn_decode_shared_prefix (prefill_mfma_kernel"
+            "kernel": ("paged_attn_decode_shared_prefix (prefill_pp_kernel"
                        "<true,true> + decode_sk_kernel + decode_combine_kernel)"
                        if plain else "paged_attn_decode (decode_sk_kernel + "
                        "decode_combine_kernel)"),
