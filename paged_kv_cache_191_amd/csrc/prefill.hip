@@ -121,8 +121,10 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // next) while the other runs the softmax of its current tile. Per tile t:
 //   phase A(t): group 0 softmax(t)           group 1 PV(t-1), QK(t)
 //   phase B(t): group 0 PV(t), QK(t+1)       group 1 softmax(t)
-// K tiles are loaded two tiles ahead and V tiles one tile ahead (issued at
-// the start of B phases), into static double buffers.
+// K tiles are loaded two tiles ahead and V tiles one tile ahead into static
+// double buffers. Group 0 issues all of a tile's loads, one every second
+// MFMA of its QK block in B phases, so that the requests reach the memory
+// pipeline spread out while the other group's softmax runs undisturbed.
 // ---------------------------------------------------------------------------
 constexpr int kPPWaves = 8;
 constexpr int kPPRows = 64;
@@ -142,7 +144,7 @@ __device__ __forceinline__ void phase_barrier(bool wait_vm) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool PAGED, bool PREFIX>
+template <bool PAGED, bool PREFIX, bool POW2>
 __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sk0[kBN * kD];
@@ -268,26 +270,28 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
       (int64_t)kvh * (PAGED ? a.block_size : a.seq_stride);
   typedef __attribute__((address_space(4))) const int32_t* cptr_t;
   // block index and offset of a key position (shift and mask for the usual
-  // power-of-two block sizes)
+  // power-of-two block sizes: no branch inside the tile loop)
   auto blk_of = [&](int x) __attribute__((always_inline)) {
-    if (__builtin_expect(a.bs_shift >= 0, 1)) return x >> a.bs_shift;
-    return x / a.block_size;
+    if constexpr (POW2) return x >> a.bs_shift;
+    else return x / a.block_size;
   };
   auto off_in_blk = [&](int x) __attribute__((always_inline)) {
-    if (__builtin_expect(a.bs_shift >= 0, 1)) return x & (a.block_size - 1);
-    return x % a.block_size;
+    if constexpr (POW2) return x & (a.block_size - 1);
+    else return x % a.block_size;
   };
-  auto group_base = [&](int j) __attribute__((always_inline)) {
-    return min((j * kBN + 8 * w) & ~15, (kv_end - 1) & ~15);
+  // Key slot `slot` (0..7) of a tile: keys 8 slot .. 8 slot + 7.
+  auto group_base = [&](int j, int slot) __attribute__((always_inline)) {
+    return min((j * kBN + 8 * slot) & ~15, (kv_end - 1) & ~15);
   };
-  auto table_block = [&](int j) __attribute__((always_inline)) {
+  auto table_block = [&](int j, int slot) __attribute__((always_inline)) {
     if (!PAGED) return 0;
     j = min(j, n_tiles - 1);
     return ((cptr_t)a.bt)[(int64_t)trow * a.bt_stride +
-                          blk_of(group_base(j))];
+                          blk_of(group_base(j, slot))];
   };
   // Per-lane parts of the load addresses: the 16-byte chunk each lane moves
-  // (swizzled), as a byte offset inside a head row.
+  // (swizzled), as a byte offset inside a head row. The swizzle depends on
+  // the row modulo 16, the same for slots w and w + 4.
   int chunk_off[2][2];  // [K/V][n]
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
@@ -295,7 +299,9 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     chunk_off[0][n] = 16 * (ld_pc ^ (row & 15));
     chunk_off[1][n] = 16 * (ld_pc ^ ((0xAC60 >> (4 * (row & 3))) & 15));
   }
-  auto load = [&](auto is_v, auto buf, int j, int b)
+  // One 16-byte-per-lane load: rows 8 slot + 4 n .. + 3 of tile j (block
+  // table entry b) into buffer `buf`.
+  auto load1 = [&](auto is_v, auto buf, int j, int b, int slot, int n)
       __attribute__((always_inline)) {
     constexpr bool V = decltype(is_v)::value;
     bf16* dst = V ? (decltype(buf)::value ? sv1 : sv0)
@@ -303,7 +309,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     int64_t grp_row;
     int base;
     if (PAGED) {
-      base = group_base(j);
+      base = group_base(j, slot);
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
       grp_row = (int64_t)b * a.hkv * a.block_size + head_row0 +
                 off_in_blk(base);
@@ -314,14 +320,29 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     // wave-uniform byte address of head row `base`, plus a 32-bit per-lane
     // offset (row within the 16-key group, and the chunk)
     const char* gbase = (const char*)(V ? a.v : a.k) + grp_row * (kD * 2);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int key = min(j * kBN + 8 * w + 4 * n + ld_row, kv_end - 1);
-      const int off = (key - base) * (kD * 2) + chunk_off[V ? 1 : 0][n];
-      __builtin_amdgcn_global_load_lds((gptr_t)(gbase + off),
-                                       (lptr_t)(&dst[(8 * w + 4 * n) * kD]),
-                                       16, 0, 0);
-    }
+    const int key = min(j * kBN + 8 * slot + 4 * n + ld_row, kv_end - 1);
+    const uint32_t off =
+        (uint32_t)((key - base) * (kD * 2) + chunk_off[V ? 1 : 0][n]);
+    const uint32_t lds =
+        (uint32_t)(uintptr_t)(lptr_t)(&dst[(8 * slot + 4 * n) * kD]);
+    // Issued as inline assembly: the compiler then keeps its own LDS read
+    // counters exact (it treats a direct-to-LDS load as an unordered LDS
+    // event and would drain every LDS read behind it). Completion is
+    // awaited explicitly: every phase that follows a load phase ends with
+    // s_waitcnt 0 before the barrier (phase_barrier(true)).
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %2"
+        :
+        : "v"(off), "s"(lds), "s"(gbase)
+        : "m0");
+  };
+  // All eight waves: each moves its own slot w.
+  auto load = [&](auto is_v, auto buf, int j, int b)
+      __attribute__((always_inline)) {
+    load1(is_v, buf, j, b, w, 0);
+    load1(is_v, buf, j, b, w, 1);
   };
   using KT = std::false_type;
   using VT = std::true_type;
@@ -351,6 +372,52 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // QK(t+1) of group 0 in phase B(t), with the tile loads of the whole
+  // workgroup interleaved (one every second MFMA): K(t+2) into the K buffer
+  // of parity t, V(t+1) into the V buffer of parity t+1, slots w and w + 4.
+  // Tiles past the last are clamped to it (the buffers written are free).
+  int kb_v[2] = {0, 0}, kb_k[2] = {0, 0};  // table entries, V(t+1), K(t+2)
+  auto qk_ld = [&](auto par, int t) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    const bf16* K_ = PAR ? sk0 : sk1;  // K(t+1)
+    const int jk = min(t + 2, n_tiles - 1);
+    const int jv = t + 1;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 ka = as_bf16x8(
+            ld16(&K_[k_elem(32 * kb + l32, 16 * ks + 8 * g2)]));
+        sacc[kb] = mfma32(ka, qop[ks], sacc[kb]);
+        const int i = 8 * kb + ks;
+        if (i & 1) {
+          const int k = i >> 1;  // load k of 8
+          const int sl = (k & 2) ? 1 : 0;
+          const int n = k & 1;
+          if (k < 4) load1(KT{}, std::integral_constant<int, PAR>{}, jk,
+                           kb_k[sl], w + 4 * sl, n);
+          else load1(VT{}, std::integral_constant<int, 1 - PAR>{}, jv,
+                     kb_v[sl], w + 4 * sl, n);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 16 - kQkAhead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      kb_v[sl] = kb_k[sl];
+      kb_k[sl] = table_block(t + 3, w + 4 * sl);
+    }
   };
   const int trs = lane & 15;
   const int trd = 16 * ((lane >> 4) & 1) + 4 * (trs & 3);
@@ -431,45 +498,29 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
                  "+v"(l_part), "+v"(m_run));
   };
 
-  // ---- loads issued at the start of phase B(t): K(t+2) into buffer t&1,
-  // V(t+1) into buffer (t+1)&1 (both freed by the end of phase A(t)).
-  int kblk_next = 0, kblk_next2 = 0;  // table entries of tiles t+1, t+2
-  auto issue_loads = [&](auto par, int t) __attribute__((always_inline)) {
-    constexpr int PAR = decltype(par)::value;
-    if (t + 2 < n_tiles) {
-      if constexpr (PAR) load(KT{}, B1{}, t + 2, kblk_next2);
-      else load(KT{}, B0{}, t + 2, kblk_next2);
-    }
-    if (t + 1 < n_tiles) {
-      if constexpr (PAR) load(VT{}, B0{}, t + 1, kblk_next);
-      else load(VT{}, B1{}, t + 1, kblk_next);
-    }
-    kblk_next = kblk_next2;
-    kblk_next2 = table_block(t + 3);
-  };
-
   // ---- prologue: K(j_beg) (and, at the start of the first phase, K(j_beg+1)
-  // and V(j_beg)).
+  // and V(j_beg)), one slot per wave.
   {
-    const int b0 = table_block(j_beg);
+    const int b0 = table_block(j_beg, w);
     if (j_beg & 1) load(KT{}, B1{}, j_beg, b0);
     else load(KT{}, B0{}, j_beg, b0);
-    kblk_next = b0;  // V(j_beg) uses the same entry
-    kblk_next2 = table_block(j_beg + 1);
-  }
-  phase_barrier(true);
-  // first phase ("B(j_beg - 1)"): loads K(j_beg+1), V(j_beg); group 0
-  // computes QK(j_beg); group 1 waits.
-  {
-    const int t = j_beg - 1;
-    if (j_beg + 1 < n_tiles) {
-      if ((j_beg + 1) & 1) load(KT{}, B1{}, j_beg + 1, kblk_next2);
-      else load(KT{}, B0{}, j_beg + 1, kblk_next2);
+    if (grp == 0) {
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        kb_v[sl] = table_block(j_beg + 1, w + 4 * sl);
+        kb_k[sl] = table_block(j_beg + 2, w + 4 * sl);
+      }
     }
-    if (j_beg & 1) load(VT{}, B1{}, j_beg, kblk_next);
-    else load(VT{}, B0{}, j_beg, kblk_next);
-    kblk_next = kblk_next2;
-    kblk_next2 = table_block(t + 3);
+    phase_barrier(true);
+    // first phase ("B(j_beg - 1)"): loads K(j_beg+1), V(j_beg); group 0
+    // computes QK(j_beg); group 1 waits.
+    if (j_beg + 1 < n_tiles) {
+      const int b1 = table_block(j_beg + 1, w);
+      if ((j_beg + 1) & 1) load(KT{}, B1{}, j_beg + 1, b1);
+      else load(KT{}, B0{}, j_beg + 1, b1);
+    }
+    if (j_beg & 1) load(VT{}, B1{}, j_beg, b0);
+    else load(VT{}, B0{}, j_beg, b0);
     if (grp == 0) {
       if (j_beg & 1) qk(B1{});
       else qk(B0{});
@@ -478,18 +529,16 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
   phase_barrier(false);
 
   if (grp == 0) {
-    // A(t): softmax(t); B(t): loads, PV(t) from V[t&1], QK(t+1) from K[(t+1)&1]
+    // A(t): softmax(t); B(t): PV(t) from V[t&1], QK(t+1) from K[(t+1)&1]
+    // with the loads of K(t+2) and V(t+1) interleaved
     auto iter = [&](auto par, int t, auto masked) __attribute__((always_inline)) {
       constexpr int PAR = decltype(par)::value;
       softmax(t, masked);
       phase_barrier(true);
-      // The loads go after this block's V reads: the compiler makes a
-      // transposed LDS read wait for every LDS load in flight.
+      // The loads go after this block's V reads, so that they have the whole
+      // next phase to land.
       if constexpr (PAR) pv(B1{}); else pv(B0{});
-      issue_loads(par, t);
-      if (t + 1 < n_tiles) {
-        if constexpr (PAR) qk(B0{}); else qk(B1{});
-      }
+      if (t + 1 < n_tiles) qk_ld(par, t);
       phase_barrier(false);
     };
     auto run = [&](int t0, int t1, auto masked) __attribute__((always_inline)) {
@@ -504,7 +553,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     run(j_beg, n_full, NoMask{});
     run(n_full, n_tiles, Mask{});
   } else {
-    // A(t): PV(t-1) from V[(t-1)&1], QK(t) from K[t&1]; B(t): loads, softmax(t)
+    // A(t): PV(t-1) from V[(t-1)&1], QK(t) from K[t&1]; B(t): softmax(t)
     auto iter = [&](auto par, int t, auto masked, auto with_pv)
         __attribute__((always_inline)) {
       constexpr int PAR = decltype(par)::value;
@@ -513,7 +562,6 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
       }
       if constexpr (PAR) qk(B1{}); else qk(B0{});
       phase_barrier(true);
-      issue_loads(par, t);
       softmax(t, masked);
       phase_barrier(false);
     };
@@ -673,10 +721,12 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
     dim3 grid((a.max_q_len + kPPRows - 1) / kPPRows, a.hq / 4, a.num_seqs);
     if ((int64_t)grid.x * grid.y * grid.z > INT32_MAX)
       return kvp_fail(KV_EUNSUPPORTED, "%s: too many query blocks", name);
-    if (paged)
-      prefill_pp_kernel<true, false><<<grid, kPPWaves * kWave, 0, st>>>(a);
+    if (!paged)
+      prefill_pp_kernel<false, false, false><<<grid, kPPWaves * kWave, 0, st>>>(a);
+    else if (a.bs_shift >= 0)
+      prefill_pp_kernel<true, false, true><<<grid, kPPWaves * kWave, 0, st>>>(a);
     else
-      prefill_pp_kernel<false, false><<<grid, kPPWaves * kWave, 0, st>>>(a);
+      prefill_pp_kernel<true, false, false><<<grid, kPPWaves * kWave, 0, st>>>(a);
     KVP_LAUNCH_CHECK(name);
     return KV_OK;
   }
@@ -737,7 +787,10 @@ kv_status kvp_prefix_partials(const KvpPrefixJob& j, hipStream_t st) {
                     j.num_groups;
   if (n > INT32_MAX)
     return kvp_fail(KV_EUNSUPPORTED, "shared-prefix decode: too many groups");
-  prefill_pp_kernel<true, true><<<(unsigned)n, kPPWaves * kWave, 0, st>>>(a);
+  if (a.bs_shift >= 0)
+    prefill_pp_kernel<true, true, true><<<(unsigned)n, kPPWaves * kWave, 0, st>>>(a);
+  else
+    prefill_pp_kernel<true, true, false><<<(unsigned)n, kPPWaves * kWave, 0, st>>>(a);
   KVP_LAUNCH_CHECK("paged_attn_decode_shared_prefix");
   return KV_OK;
 }
