@@ -107,6 +107,28 @@ __device__ __forceinline__ int v_elem(int row, int d) {
   return row * kD + ((((d >> 3) ^ swz)) << 3) + (d & 7);
 }
 
+// Lanes l and l ^ 32 combined without LDS: v_permlane32_swap exchanges the
+// upper half-wave of one operand with the lower half-wave of the other, so
+// with both operands v each lane receives {own value, partner's value} in
+// some order; a symmetric operation of the pair gives the combined value.
+// Issued as inline assembly: the optimizer folds a symmetric operation of
+// the builtin's two results to its first result. The s_nop covers the wait
+// states between a VALU write and the swap's read of that register.
+struct f32pair { float a, b; };
+__device__ __forceinline__ f32pair halves_pair(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return {a, b};
+}
+__device__ __forceinline__ float halves_max(float v) {
+  const f32pair r = halves_pair(v);
+  return fmaxf(r.a, r.b);
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const f32pair r = halves_pair(v);
+  return r.a + r.b;
+}
+
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
@@ -350,7 +372,33 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
   // ---- MFMA blocks
   // The scheduler is asked to keep each LDS read two steps ahead of its
   // MFMA (short read-ahead keeps register use down).
-  auto qk = [&](auto buf) __attribute__((always_inline)) {
+  // Tile loads of phase B(t), slot w or w + 4 for group 0, w - 4 or w for
+  // group 1 (sl = 0, 1), rows 4 n ..: group 0 moves K(t+2) into the K buffer
+  // of parity t, one load every fourth MFMA of its QK block; group 1 moves
+  // V(t+1) into the V buffer of parity t + 1 before its softmax. A K tile
+  // past the last is clamped to it (the buffer written is free).
+  int kb_next[2] = {0, 0};  // table entries: K(t+2) (group 0), V(t+1) (group 1)
+  const int slot0 = grp == 0 ? w : w - 4;
+  auto tile_load = [&](auto par, int sl, int n, int t)
+      __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    if (grp == 0)
+      load1(KT{}, std::integral_constant<int, PAR>{}, min(t + 2, n_tiles - 1),
+            kb_next[sl], slot0 + 4 * sl, n);
+    else
+      load1(VT{}, std::integral_constant<int, 1 - PAR>{}, t + 1, kb_next[sl],
+            slot0 + 4 * sl, n);
+  };
+  // table entries of the next phase B's loads (tile t + 3 or t + 2)
+  auto next_entries = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+      kb_next[sl] = table_block(t + (grp == 0 ? 3 : 2), slot0 + 4 * sl);
+  };
+  // QK of K buffer `buf`; with LD, group 0's loads of phase B(t) interleaved.
+  auto qk = [&](auto buf, auto ld, auto par, int t)
+      __attribute__((always_inline)) {
+    constexpr bool LD = decltype(ld)::value;
     const bf16* K_ = decltype(buf)::value ? sk1 : sk0;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -362,6 +410,8 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
         const bf16x8 ka = as_bf16x8(
             ld16(&K_[k_elem(32 * kb + l32, 16 * ks + 8 * g2)]));
         sacc[kb] = mfma32(ka, qop[ks], sacc[kb]);
+        const int i = 8 * kb + ks;
+        if (LD && (i & 3) == 3) tile_load(par, i >> 3, (i >> 2) & 1, t);
       }
     }
     __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
@@ -372,52 +422,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
     __builtin_amdgcn_sched_barrier(0);
-  };
-  // QK(t+1) of group 0 in phase B(t), with the tile loads of the whole
-  // workgroup interleaved (one every second MFMA): K(t+2) into the K buffer
-  // of parity t, V(t+1) into the V buffer of parity t+1, slots w and w + 4.
-  // Tiles past the last are clamped to it (the buffers written are free).
-  int kb_v[2] = {0, 0}, kb_k[2] = {0, 0};  // table entries, V(t+1), K(t+2)
-  auto qk_ld = [&](auto par, int t) __attribute__((always_inline)) {
-    constexpr int PAR = decltype(par)::value;
-    const bf16* K_ = PAR ? sk0 : sk1;  // K(t+1)
-    const int jk = min(t + 2, n_tiles - 1);
-    const int jv = t + 1;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 ka = as_bf16x8(
-            ld16(&K_[k_elem(32 * kb + l32, 16 * ks + 8 * g2)]));
-        sacc[kb] = mfma32(ka, qop[ks], sacc[kb]);
-        const int i = 8 * kb + ks;
-        if (i & 1) {
-          const int k = i >> 1;  // load k of 8
-          const int sl = (k & 2) ? 1 : 0;
-          const int n = k & 1;
-          if (k < 4) load1(KT{}, std::integral_constant<int, PAR>{}, jk,
-                           kb_k[sl], w + 4 * sl, n);
-          else load1(VT{}, std::integral_constant<int, 1 - PAR>{}, jv,
-                     kb_v[sl], w + 4 * sl, n);
-        }
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < 16 - kQkAhead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      kb_v[sl] = kb_k[sl];
-      kb_k[sl] = table_block(t + 3, w + 4 * sl);
-    }
+    if (LD) next_entries(t);
   };
   const int trs = lane & 15;
   const int trd = 16 * ((lane >> 4) & 1) + 4 * (trs & 3);
@@ -445,6 +450,8 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, kPvAhead, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
+  using NoLd = std::false_type;
+  using Ld = std::true_type;
   // ---- softmax of tile j (vector ALU): masks, lazy rescale, P^T packed.
   auto softmax = [&](int j, auto masked) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(masked)::value;
@@ -461,7 +468,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
         }
         mx = fmaxf(mx, sacc[kb][r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    mx = halves_max(mx) * a.scale_log2;
     if (__any(mx > m_run + 8.f)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
@@ -471,27 +478,26 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
     }
     const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[kb][r], a.scale_log2,
-                                                 -m_ref));
-        sacc[kb][r] = p;
-        psum += p;
-      }
-    l_part += psum;
+      for (int r = 0; r < 16; ++r)
+        sacc[kb][r] = fast_exp2(__builtin_fmaf(sacc[kb][r], a.scale_log2,
+                                               -m_ref));
     // P^T: lane holds query l32; k-slot e of MFMA kk <-> key
     // 16 kk + 8 (e / 4) + 4 g2 + e % 4 of the tile.
+    float psum = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int kb = kk >> 1;
       const int rb = 8 * (kk & 1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e) {
         pk[kk][e] = pack_bf16(sacc[kb][rb + 2 * e], sacc[kb][rb + 2 * e + 1]);
+        psum += sacc[kb][rb + 2 * e] + sacc[kb][rb + 2 * e + 1];
+      }
     }
+    l_part += psum;
     // Pin the results here: the softmax must finish in its own phase, not
     // sink into the next MFMA block of this wave.
     asm volatile("" : "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]), "+v"(pk[3]),
@@ -504,13 +510,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     const int b0 = table_block(j_beg, w);
     if (j_beg & 1) load(KT{}, B1{}, j_beg, b0);
     else load(KT{}, B0{}, j_beg, b0);
-    if (grp == 0) {
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        kb_v[sl] = table_block(j_beg + 1, w + 4 * sl);
-        kb_k[sl] = table_block(j_beg + 2, w + 4 * sl);
-      }
-    }
+    next_entries(j_beg - 1);
     phase_barrier(true);
     // first phase ("B(j_beg - 1)"): loads K(j_beg+1), V(j_beg); group 0
     // computes QK(j_beg); group 1 waits.
@@ -522,23 +522,23 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     if (j_beg & 1) load(VT{}, B1{}, j_beg, b0);
     else load(VT{}, B0{}, j_beg, b0);
     if (grp == 0) {
-      if (j_beg & 1) qk(B1{});
-      else qk(B0{});
+      if (j_beg & 1) qk(B1{}, NoLd{}, B0{}, 0);
+      else qk(B0{}, NoLd{}, B0{}, 0);
     }
   }
   phase_barrier(false);
 
   if (grp == 0) {
     // A(t): softmax(t); B(t): PV(t) from V[t&1], QK(t+1) from K[(t+1)&1]
-    // with the loads of K(t+2) and V(t+1) interleaved
+    // with the loads of K(t+2) interleaved
     auto iter = [&](auto par, int t, auto masked) __attribute__((always_inline)) {
       constexpr int PAR = decltype(par)::value;
       softmax(t, masked);
       phase_barrier(true);
-      // The loads go after this block's V reads, so that they have the whole
-      // next phase to land.
       if constexpr (PAR) pv(B1{}); else pv(B0{});
-      if (t + 1 < n_tiles) qk_ld(par, t);
+      if (t + 1 < n_tiles) {
+        if constexpr (PAR) qk(B0{}, Ld{}, par, t); else qk(B1{}, Ld{}, par, t);
+      }
       phase_barrier(false);
     };
     auto run = [&](int t0, int t1, auto masked) __attribute__((always_inline)) {
@@ -553,15 +553,21 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     run(j_beg, n_full, NoMask{});
     run(n_full, n_tiles, Mask{});
   } else {
-    // A(t): PV(t-1) from V[(t-1)&1], QK(t) from K[t&1]; B(t): softmax(t)
+    // A(t): PV(t-1) from V[(t-1)&1], QK(t) from K[t&1]; B(t): loads of
+    // V(t+1), softmax(t)
     auto iter = [&](auto par, int t, auto masked, auto with_pv)
         __attribute__((always_inline)) {
       constexpr int PAR = decltype(par)::value;
       if constexpr (decltype(with_pv)::value) {
         if constexpr (PAR) pv(B0{}); else pv(B1{});
       }
-      if constexpr (PAR) qk(B1{}); else qk(B0{});
+      if constexpr (PAR) qk(B1{}, NoLd{}, par, t); else qk(B0{}, NoLd{}, par, t);
       phase_barrier(true);
+      if (t + 1 < n_tiles) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tile_load(par, k >> 1, k & 1, t);
+        next_entries(t);
+      }
       softmax(t, masked);
       phase_barrier(false);
     };
@@ -587,7 +593,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
   }
 
   // ---- outputs of this group's rows
-  l_part += __shfl_xor(l_part, 32);
+  l_part = halves_sum(l_part);
   const bool row_ok = row0 + l32 < q0 + nrows;
   if (PREFIX) {
     if (row_ok) {
