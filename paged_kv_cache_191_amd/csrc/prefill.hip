@@ -323,28 +323,33 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
   }
   // One 16-byte-per-lane load: rows 8 slot + 4 n .. + 3 of tile j (block
   // table entry b) into buffer `buf`.
+  // Wave-uniform address parts: this head's first row in each tensor, and
+  // the bytes of one block (all heads) of a tensor.
+  const int64_t head_row_seq =
+      PAGED ? head_row0 : (int64_t)s * a.hkv * a.seq_stride + head_row0;
+  const char* k_head = (const char*)a.k + head_row_seq * (kD * 2);
+  const char* v_head = (const char*)a.v + head_row_seq * (kD * 2);
+  const uint64_t blk_bytes = (uint64_t)a.hkv * a.block_size * (kD * 2);
   auto load1 = [&](auto is_v, auto buf, int j, int b, int slot, int n)
       __attribute__((always_inline)) {
     constexpr bool V = decltype(is_v)::value;
     bf16* dst = V ? (decltype(buf)::value ? sv1 : sv0)
                   : (decltype(buf)::value ? sk1 : sk0);
-    int64_t grp_row;
-    int base;
+    // wave-uniform byte address of head row `base` (the first row of the
+    // 16-key group), plus a 32-bit per-lane offset: row within the group
+    // (keys past the context re-read the last one) and 16-byte chunk
+    const char* gbase = V ? v_head : k_head;
+    int base = 0;
     if (PAGED) {
       base = group_base(j, slot);
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      grp_row = (int64_t)b * a.hkv * a.block_size + head_row0 +
-                off_in_blk(base);
-    } else {
-      base = 0;
-      grp_row = (int64_t)s * a.hkv * a.seq_stride + head_row0;
+      gbase += (uint64_t)(uint32_t)b * blk_bytes +
+               (uint32_t)off_in_blk(base) * (kD * 2);
     }
-    // wave-uniform byte address of head row `base`, plus a 32-bit per-lane
-    // offset (row within the 16-key group, and the chunk)
-    const char* gbase = (const char*)(V ? a.v : a.k) + grp_row * (kD * 2);
-    const int key = min(j * kBN + 8 * slot + 4 * n + ld_row, kv_end - 1);
-    const uint32_t off =
-        (uint32_t)((key - base) * (kD * 2) + chunk_off[V ? 1 : 0][n]);
+    const int u = j * kBN + 8 * slot + 4 * n - base;
+    const int lim = kv_end - 1 - base;
+    const uint32_t off = (uint32_t)(min(u + ld_row, lim) * (kD * 2) +
+                                    chunk_off[V ? 1 : 0][n]);
     const uint32_t lds =
         (uint32_t)(uintptr_t)(lptr_t)(&dst[(8 * slot + 4 * n) * kD]);
     // Issued as inline assembly: the compiler then keeps its own LDS read
