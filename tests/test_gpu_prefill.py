@@ -67,7 +67,7 @@ def _run_prefill(inp, layout, nat, kc, vc, rows, cu, start, ctx, causal=True):
 
 
 @pytest.mark.parametrize("B,layout", [(16, "paged"), (64, "paged"),
-                                      (16, "contig")])
+                                      (48, "paged"), (16, "contig")])
 def test_chunked_prefill_small(B, layout):
     # Yi-6B head shape, two ragged sequences, chunks that span several
     # 32-query blocks and 64-key tiles with ragged tails.

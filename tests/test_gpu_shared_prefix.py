@@ -127,7 +127,8 @@ MIXED = [
 ]
 
 
-@pytest.mark.parametrize("B,hq,hkv", [(16, 8, 2), (32, 32, 8), (16, 16, 4)])
+@pytest.mark.parametrize("B,hq,hkv", [(16, 8, 2), (32, 32, 8), (16, 16, 4),
+                                      (48, 8, 2)])
 def test_mixed_groups(B, hq, hkv):
     b = build_groups(MIXED, B, hq, hkv, seed=11 + B + hq)
     scale = 1.0 / np.sqrt(128)
