@@ -281,6 +281,61 @@ kv_status contig_attn_prefill(void* out, const void* q,
                               int32_t head_dim, float scale, int32_t causal,
                               kv_dtype dtype, void* stream);
 
+/* ---------------------------------------------------------------------
+ * Contiguous KV cache on demand-mapped virtual memory ["Makale Bülteni —
+ * vAttention", section "İddia ve Gerçeklik: vAttention"]: a virtually
+ * contiguous buffer is reserved for every sequence's maximum context at
+ * creation (no physical memory); physical pages are created and mapped
+ * into it only as sequences grow, so the contiguous kernels above
+ * (contig_attn_decode, contig_attn_prefill, kv_reshape_and_cache with
+ * slot = s * max_context + position) run on it unchanged.
+ *   Layout: K and V each [max_seqs, Hkv, max_context, D] of `dtype`
+ *   (seq_stride = max_context). The unit of mapping is a page of
+ *   page_tokens rows of one (sequence, KV head) in one tensor: a sequence
+ *   of L tokens holds 2 * Hkv * ceil(L / page_tokens) pages.
+ *   page_tokens: a multiple of 16 that divides max_context, whose pages
+ *   (page_tokens * D * sizeof(dtype) bytes) are a multiple of the device's
+ *   mapping granularity (kv_vcache_granularity).
+ * Host functions; they run HIP virtual-memory calls (hipMemAddressReserve,
+ * hipMemCreate, hipMemMap, hipMemSetAccess, hipMemUnmap) on the device that
+ * is current at kv_vcache_create, and launch no kernel. A kernel may read
+ * or write only tokens [0, L) of a sequence reserved up to L: other
+ * addresses of the range are unmapped. Released pages keep their physical
+ * memory in the cache's pool and are mapped again before new pages are
+ * created; kv_vcache_destroy frees everything. Before a release or destroy
+ * the caller must have synchronized the work that reads those pages.
+ * Errors: KV_EINVAL (arguments), KV_ENOMEM (device memory), KV_EHIP (other
+ * HIP failures); a failed reserve leaves the mapping unchanged. One host
+ * thread per cache. */
+typedef struct kv_vcache kv_vcache;
+
+/* Minimum mapping granularity of the current device, in bytes. */
+kv_status kv_vcache_granularity(size_t* bytes);
+
+kv_status kv_vcache_create(int32_t max_seqs, int32_t max_context,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           kv_dtype dtype, int32_t page_tokens,
+                           kv_vcache** out);
+void kv_vcache_destroy(kv_vcache* cache);
+
+/* Device base addresses of the K and V ranges. */
+kv_status kv_vcache_ptrs(const kv_vcache* cache, void** k, void** v);
+
+/* Map pages so that tokens [0, num_tokens) of sequence seq are backed;
+ * *pages_mapped (may be NULL) = pages this call mapped. Never unmaps. */
+kv_status kv_vcache_reserve(kv_vcache* cache, int32_t seq, int32_t num_tokens,
+                            int32_t* pages_mapped);
+
+/* Unmap all pages of sequence seq (their memory stays in the pool). */
+kv_status kv_vcache_release(kv_vcache* cache, int32_t seq);
+
+/* Pages mapped per region of sequence seq (-1 on a bad argument). */
+int32_t kv_vcache_seq_pages(const kv_vcache* cache, int32_t seq);
+
+/* Physical bytes mapped now / held (mapped + pooled); -1 if cache is NULL. */
+int64_t kv_vcache_mapped_bytes(const kv_vcache* cache);
+int64_t kv_vcache_held_bytes(const kv_vcache* cache);
+
 #ifdef __cplusplus
 }
 #endif

@@ -357,6 +357,9 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
     // event and would drain every LDS read behind it). Completion is
     // awaited explicitly: every phase that follows a load phase ends with
     // s_waitcnt 0 before the barrier (phase_barrier(true)).
+    // m0 is named as clobbered; no other code of this kernel uses m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
     asm volatile(
         "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
@@ -364,6 +367,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
         :
         : "v"(off), "s"(lds), "s"(gbase)
         : "m0");
+#pragma clang diagnostic pop
   };
   // All eight waves: each moves its own slot w.
   auto load = [&](auto is_v, auto buf, int j, int b)

@@ -79,6 +79,16 @@ SIGNATURES = {
     "contig_attn_prefill": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _P,
                                    _I32, _I32, _I32, _I32, _F, _I32, _I32,
                                    _P]),
+    "kv_vcache_granularity": (_I32, [ctypes.POINTER(_SZ)]),
+    "kv_vcache_create": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32,
+                                ctypes.POINTER(_P)]),
+    "kv_vcache_destroy": (None, [_P]),
+    "kv_vcache_ptrs": (_I32, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
+    "kv_vcache_reserve": (_I32, [_P, _I32, _I32, _PI32]),
+    "kv_vcache_release": (_I32, [_P, _I32]),
+    "kv_vcache_seq_pages": (_I32, [_P, _I32]),
+    "kv_vcache_mapped_bytes": (_I64, [_P]),
+    "kv_vcache_held_bytes": (_I64, [_P]),
 }
 
 _lib = None
@@ -461,3 +471,100 @@ def contig_attn_prefill(out, q, cu_q_lens, q_start_pos, max_q_len: int, k, v,
         _dev(context_lens, "context_lens", torch.int32), S, hq, hkv, d,
         float(scale), 1 if causal else 0, _dtype_code(q), _stream(stream))
     _check(st, "contig_attn_prefill")
+
+
+# ------------------------------------------- demand-mapped contiguous cache --
+class DeviceView:
+    """A device range owned by the library (the K or V range of a VCache),
+    with the attributes the wrappers above read from a tensor: shape, dtype,
+    is_cuda, is_contiguous(), data_ptr(), numel()."""
+
+    is_cuda = True
+
+    def __init__(self, ptr: int, shape, dtype):
+        self._ptr = int(ptr)
+        self.shape = tuple(int(x) for x in shape)
+        self.dtype = dtype
+
+    def is_contiguous(self) -> bool:
+        return True
+
+    def data_ptr(self) -> int:
+        return self._ptr
+
+    def numel(self) -> int:
+        return int(np.prod(self.shape))
+
+
+def kv_vcache_granularity() -> int:
+    g = _SZ(0)
+    _check(lib().kv_vcache_granularity(ctypes.byref(g)),
+           "kv_vcache_granularity")
+    return int(g.value)
+
+
+class VCache:
+    """Contiguous K/V [max_seqs, Hkv, max_context, D] on virtual memory whose
+    pages are mapped as sequences grow (kv_vcache_* in kvpaged.h). `k` and
+    `v` are DeviceViews for contig_attn_decode / contig_attn_prefill /
+    kv_reshape_and_cache; only tokens reserved for a sequence may be read or
+    written. Call close() (after synchronizing the work that reads it)."""
+
+    def __init__(self, max_seqs: int, max_context: int, num_kv_heads: int,
+                 head_dim: int, dtype, page_tokens: int):
+        torch = _torch()
+        code = KV_BF16 if dtype == torch.bfloat16 else (
+            KV_F32 if dtype == torch.float32 else None)
+        if code is None:
+            raise TypeError(f"unsupported dtype {dtype}")
+        h = _P()
+        _check(lib().kv_vcache_create(max_seqs, max_context, num_kv_heads,
+                                      head_dim, code, page_tokens,
+                                      ctypes.byref(h)), "kv_vcache_create")
+        self._h = h
+        k, v = _P(), _P()
+        _check(lib().kv_vcache_ptrs(h, ctypes.byref(k), ctypes.byref(v)),
+               "kv_vcache_ptrs")
+        shape = (max_seqs, num_kv_heads, max_context, head_dim)
+        self.k = DeviceView(k.value, shape, dtype)
+        self.v = DeviceView(v.value, shape, dtype)
+        self.page_tokens = page_tokens
+        self.max_context = max_context
+
+    def _handle(self):
+        if self._h is None:
+            raise ValueError("VCache is closed")
+        return self._h
+
+    def reserve(self, seq: int, num_tokens: int) -> int:
+        n = ctypes.c_int32(0)
+        _check(lib().kv_vcache_reserve(self._handle(), int(seq),
+                                       int(num_tokens), ctypes.byref(n)),
+               "kv_vcache_reserve")
+        return int(n.value)
+
+    def release(self, seq: int) -> None:
+        _check(lib().kv_vcache_release(self._handle(), int(seq)),
+               "kv_vcache_release")
+
+    def seq_pages(self, seq: int) -> int:
+        return int(lib().kv_vcache_seq_pages(self._handle(), int(seq)))
+
+    @property
+    def mapped_bytes(self) -> int:
+        return int(lib().kv_vcache_mapped_bytes(self._handle()))
+
+    @property
+    def held_bytes(self) -> int:
+        return int(lib().kv_vcache_held_bytes(self._handle()))
+
+    def close(self) -> None:
+        if self._h is not None:
+            lib().kv_vcache_destroy(self._h)
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
