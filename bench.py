@@ -69,6 +69,13 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# page of the demand-mapped contiguous cache in the prefill pass, in tokens
+# of one head (--vmm-page-tokens)
+VMM_PREFILL_PAGE_TOKENS = 1024
+# pages one process maps at most in a decode run (each page is one device
+# allocation; larger pages are used when the contexts would need more)
+VMM_MAX_PAGES = 16384
+
 TRAFFIC_PROFILES = {
     "llama3_8b_decode": os.path.join(ROOT, "profiles",
                                      "hbm_traffic_decode_llama3_8b.txt"),
@@ -141,7 +148,8 @@ class DecodeReplica:
     the others take shared references to its blocks (fork)."""
 
     def __init__(self, inp, k_dev, v_dev, new_k, new_v, paged: bool,
-                 steps: int, device, shared_op: bool = False):
+                 steps: int, device, shared_op: bool = False,
+                 vmm_page_tokens: int = 0):
         import torch
         from paged_kv_cache_191_amd import kvpaged as kv
         from paged_kv_cache_191_amd import workloads as W
@@ -153,6 +161,10 @@ class DecodeReplica:
         S, B = w.num_seqs, w.block_size
         ctx = W.context_lengths(inp).astype(np.int64)
         self.lmax = int(ctx.max()) + steps + 1
+        # demand-mapped contiguous cache: Lmax in whole pages
+        self.vmm = vmm_page_tokens if not paged else 0
+        if self.vmm:
+            self.lmax = -(-self.lmax // self.vmm) * self.vmm
         self.cap = -(-self.lmax // B)
         n_pool = len(inp.free_order)
         # pinned host staging: [slots int64 S | lens int32 S | table int32 S*cap]
@@ -203,6 +215,28 @@ class DecodeReplica:
             for s in range(S):
                 first = int(self.h_lens[s])
                 write(s, first, int(ctx[s]) - 1 - first)
+        elif self.vmm:
+            # pages mapped as each sequence's context is written
+            self.vc = kv.VCache(S, self.lmax, w.num_kv_heads, w.head_dim,
+                                tdt, self.vmm)
+            self.k, self.v = self.vc.k, self.vc.v
+            self.map_s = 0.0
+            self.map_pages = 0
+            for s in range(S):
+                n = int(ctx[s]) - 1
+                t0 = time.perf_counter()
+                self.map_pages += self.vc.reserve(s, n)
+                self.map_s += time.perf_counter() - t0
+                rows = torch.from_numpy(W.logical_rows(inp, s)[:n]).to(device)
+                slots = torch.arange(s * self.lmax, s * self.lmax + n,
+                                     dtype=torch.int64, device=device)
+                kv.kv_reshape_and_cache(k_dev[rows], v_dev[rows], slots,
+                                        self.k, self.v)
+                self.h_lens[s] = n
+            self.mapped_tok = np.array(
+                [self.vc.seq_pages(s) * self.vmm for s in range(S)])
+            self.step_map_s = []
+            self.step_map_pages = []
         else:
             self.k = torch.empty((S, w.num_kv_heads, self.lmax, w.head_dim),
                                  dtype=tdt, device=device)
@@ -246,6 +280,19 @@ class DecodeReplica:
             self.h_slots[:] = np.arange(S, dtype=np.int64) * self.lmax + \
                 self.h_lens
             self.h_lens += 1
+            if self.vmm:
+                # map a page for the sequences whose new token starts one
+                t0 = time.perf_counter()
+                n = 0
+                for s in np.nonzero(self.h_lens > self.mapped_tok)[0]:
+                    n += self.vc.reserve(int(s), int(self.h_lens[s]))
+                    self.mapped_tok[s] = self.vc.seq_pages(int(s)) * self.vmm
+                self.step_map_s.append(time.perf_counter() - t0)
+                self.step_map_pages.append(n)
+
+    def close(self) -> None:
+        if self.vmm:
+            self.vc.close()
 
     def device_step(self, ev=None) -> None:
         kv = self.kv
@@ -285,13 +332,14 @@ def new_token_kv(w, device):
 
 
 def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
-               device, shared_op: bool = False):
+               device, shared_op: bool = False, vmm_page_tokens: int = 0):
     import torch
     w = inp.workload
     new_k, new_v = new_token_kv(w, device)
     k_dev, v_dev = inp.k.to(device), inp.v.to(device)
     reps_ = [DecodeReplica(inp, k_dev, v_dev, new_k, new_v, paged,
-                           steps + warmup, device, shared_op)
+                           steps + warmup, device, shared_op,
+                           vmm_page_tokens)
              for _ in range(reps)]
     del k_dev, v_dev
     for i in range(warmup):
@@ -334,6 +382,35 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     # the new rows: K and V, read once and written once
     tok_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2 * 2
     res["reshape_and_cache_GBps"] = tok_bytes / (rc["median"] * 1e-3) / 1e9
+    if vmm_page_tokens and not paged:
+        P = vmm_page_tokens
+        r0 = reps_[0]
+        page_bytes = P * w.head_dim * 2
+        used = float(r0.h_lens.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+        mapped = r0.vc.mapped_bytes
+        # the same contexts in 64 KiB and 2 MiB pages
+
+        def mapped_with(page_b):
+            tok = page_b // (w.head_dim * 2)
+            return float(np.sum(-(-r0.h_lens // tok))) * \
+                w.num_kv_heads * 2 * page_b
+        step_s = [x for r in reps_ for x in r.step_map_s]
+        step_pages = [x for r in reps_ for x in r.step_map_pages]
+        res["vmm"] = {
+            "page_tokens": P, "page_bytes": page_bytes,
+            "fill_map_us_per_page": 1e6 * sum(r.map_s for r in reps_) /
+            max(1, sum(r.map_pages for r in reps_)),
+            "fill_pages_per_replica": r0.map_pages,
+            "step_pages_mapped_mean": float(np.mean(step_pages)),
+            "step_map_host_us_mean": 1e6 * float(np.mean(step_s)),
+            "step_map_host_us_max": 1e6 * float(np.max(step_s)),
+            "mapped_bytes": mapped, "used_bytes": used,
+            "waste": 1.0 - used / mapped,
+            "waste_64KiB_pages": 1.0 - used / mapped_with(64 << 10),
+            "waste_2MiB_pages": 1.0 - used / mapped_with(2 << 20),
+        }
+    for r in reps_:
+        r.close()
     del reps_
     torch.cuda.empty_cache()
     return res
@@ -432,10 +509,18 @@ def prefill_pass(inp, layout: str, device):
     q_dev = inp.q.to(device)
     k_dev = inp.k.to(device)
     v_dev = inp.v.to(device)
+    vcache = None
+    map_s, map_pages = [], []
     if layout == "contig":
         kc = torch.empty((S, w.num_kv_heads, N, w.head_dim), dtype=tdt,
                          device=device)
         vc = torch.empty_like(kc)
+    elif layout == "vattn":
+        # contiguous layout on demand-mapped memory: pages are mapped as
+        # each chunk's rows are written
+        vcache = kv.VCache(S, N, w.num_kv_heads, w.head_dim, tdt,
+                           VMM_PREFILL_PAGE_TOKENS)
+        kc, vc = vcache.k, vcache.v
     else:
         n_pool = len(inp.free_order)
         kc = torch.empty((n_pool, w.num_kv_heads, B, w.head_dim), dtype=tdt,
@@ -450,11 +535,22 @@ def prefill_pass(inp, layout: str, device):
     def one_pass(timed: bool):
         nonlocal flops_total
         pool = kv.KVPool(len(inp.free_order), B, inp.free_order) \
-            if layout != "contig" else None
+            if layout == "paged" else None
         table = np.full((S, cap), -1, dtype=np.int32)
         lens = np.zeros(S, dtype=np.int32)
+        if vcache is not None:
+            # start from unmapped sequences; pages come back from the pool
+            torch.cuda.synchronize()
+            for s in range(S):
+                vcache.release(s)
+        t_map, n_map = 0.0, 0
         for c0 in range(0, N, C):
             n_new = np.full(S, C, dtype=np.int32)
+            if vcache is not None:
+                t0 = time.perf_counter()
+                for s in range(S):
+                    n_map += vcache.reserve(s, c0 + C)
+                t_map += time.perf_counter() - t0
             if pool is not None:
                 slots, _ = pool.seq_append(table, lens, n_new)
             else:
@@ -476,7 +572,7 @@ def prefill_pass(inp, layout: str, device):
             ev[0].record()
             kv.kv_reshape_and_cache(k_new, v_new, d_slots, kc, vc)
             ev[1].record()
-            if layout == "contig":
+            if layout != "paged":
                 kv.contig_attn_prefill(out, q, cu, start, C, kc, vc, ctx,
                                        scale, True)
             else:
@@ -489,6 +585,9 @@ def prefill_pass(inp, layout: str, device):
                 pairs = S * (C * c0 + C * (C + 1) // 2)
                 flops_total += 4.0 * w.head_dim * w.num_q_heads * pairs
         torch.cuda.synchronize()
+        if timed:
+            map_s.append(t_map)
+            map_pages.append(n_map)
 
     one_pass(False)
     t0 = time.perf_counter()
@@ -498,14 +597,22 @@ def prefill_pass(inp, layout: str, device):
     rc_ms = [e[0].elapsed_time(e[1]) for e in times]
     # new rows per chunk: K and V, read once and written once
     rc_bytes = S * C * w.num_kv_heads * w.head_dim * 2 * 2 * 2
+    res = {"attn_ms": attn_ms, "pass_wall_ms": 1e3 * wall,
+           "TFLOPs": flops_total / (attn_ms * 1e-3) / 1e12,
+           "tflop": flops_total / 1e12,
+           "reshape_and_cache_us_median": 1e3 * float(np.median(rc_ms)),
+           "reshape_and_cache_GBps": rc_bytes / (float(np.median(rc_ms)) *
+                                                 1e-3) / 1e9}
+    if vcache is not None:
+        res["vmm_page_tokens"] = VMM_PREFILL_PAGE_TOKENS
+        res["vmm_pages_mapped_per_pass"] = map_pages[0]
+        res["vmm_map_host_ms_per_pass"] = 1e3 * map_s[0]
+        res["vmm_map_us_per_page"] = 1e6 * map_s[0] / max(1, map_pages[0])
+        torch.cuda.synchronize()
+        vcache.close()
     del kc, vc, q_dev, k_dev, v_dev, out
     torch.cuda.empty_cache()
-    return {"attn_ms": attn_ms, "pass_wall_ms": 1e3 * wall,
-            "TFLOPs": flops_total / (attn_ms * 1e-3) / 1e12,
-            "tflop": flops_total / 1e12,
-            "reshape_and_cache_us_median": 1e3 * float(np.median(rc_ms)),
-            "reshape_and_cache_GBps": rc_bytes / (float(np.median(rc_ms)) *
-                                                  1e-3) / 1e9}
+    return res
 
 
 def memory_waste(inp, lmax_reserved: int) -> dict:
@@ -618,8 +725,16 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode steps (prefill / profiling runs); "
                          "no bench line is printed")
-    ap.add_argument("--prefill-layouts", default="paged_b16,paged_b64,contig")
+    ap.add_argument("--prefill-layouts",
+                    default="paged_b16,paged_b64,contig,contig_vmm")
     ap.add_argument("--no-contig", action="store_true")
+    ap.add_argument("--no-vmm", action="store_true",
+                    help="skip the contiguous decode on demand-mapped memory")
+    ap.add_argument("--vmm-page-tokens", type=int, default=1024,
+                    help="page of the demand-mapped cache, in tokens of one "
+                         "head (1024 x 128 bf16 values = 256 KiB; one "
+                         "allocation per page, and a process holds some "
+                         "tens of thousands at most)")
     ap.add_argument("--no-cow", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -627,6 +742,8 @@ def main() -> int:
                     help="also run one plain 1 GiB device copy (reference "
                          "kernel for hardware traffic counters)")
     args = ap.parse_args()
+    global VMM_PREFILL_PAGE_TOKENS
+    VMM_PREFILL_PAGE_TOKENS = args.vmm_page_tokens
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not "
               "supported (decode and prefill shard by sequence or head with "
@@ -650,7 +767,7 @@ def main() -> int:
     default_workload = args.workload == "llama3_8b_decode"
     headroom = wd.num_seqs * (-(-(args.steps + args.warmup) // wd.block_size)
                               + 1)
-    paged = contig = inp = cow = plain = None
+    paged = contig = inp = cow = plain = vattn = None
     if not args.no_decode:
         log(f"drawing {wd.name}")
         inp = W.draw(wd, lambda L: pool_blocks(kv, wd, L, headroom))
@@ -666,6 +783,21 @@ def main() -> int:
             log("contiguous decode steps")
             contig = run_decode(inp, False, args.steps, args.warmup,
                                 args.replicas, device)
+            if not args.no_vmm and wd.kind != "prefix":
+                log("contiguous decode steps on demand-mapped memory")
+                ctx = W.context_lengths(inp)
+                pt = args.vmm_page_tokens
+                while args.replicas * 2 * wd.num_kv_heads * int(
+                        np.sum(-(-(ctx + args.steps + args.warmup) // pt))) \
+                        > VMM_MAX_PAGES:
+                    pt *= 2
+                try:
+                    vattn = run_decode(inp, False, args.steps, args.warmup,
+                                       args.replicas, device,
+                                       vmm_page_tokens=pt)
+                except kv.KVError as e:
+                    log(f"demand-mapped decode failed: {e}")
+                    vattn = {"error": str(e)}
         if wd.kind == "prefix" and not args.no_cow:
             log("copy-on-write step")
             cow = run_cow(wd, args.steps, args.warmup, device)
@@ -676,18 +808,19 @@ def main() -> int:
         wanted = args.prefill_layouts.split(",")
         for name, layout in (("yi6b_chunked_prefill_b16", "paged_b16"),
                              ("yi6b_chunked_prefill_b64", "paged_b64"),
-                             ("yi6b_chunked_prefill_b16", "contig")):
+                             ("yi6b_chunked_prefill_b16", "contig"),
+                             ("yi6b_chunked_prefill_b16", "contig_vmm")):
             if layout not in wanted:
                 continue
             wp = W.WORKLOADS[name]
             log(f"prefill {layout}")
             pin = W.draw(wp, lambda L: pool_blocks(kv, wp, L))
-            r = prefill_pass(pin, "contig" if layout == "contig" else "paged",
-                             device)
+            r = prefill_pass(pin, {"contig": "contig", "contig_vmm": "vattn"}
+                             .get(layout, "paged"), device)
             r["frac_of_peak"] = r["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
             prefill[layout] = r
         if "contig" in prefill:
-            for b in ("paged_b16", "paged_b64"):
+            for b in ("paged_b16", "paged_b64", "contig_vmm"):
                 if b in prefill:
                     prefill[b]["overhead_vs_contig"] = (
                         prefill[b]["attn_ms"] / prefill["contig"]["attn_ms"]
@@ -753,6 +886,15 @@ def main() -> int:
         line["decode_contig"] = {k: round(v, 4) for k, v in contig.items()}
         line["decode_paged_vs_contig_overhead"] = round(
             paged["decode_op_ms_mean"] / contig["decode_op_ms_mean"] - 1.0, 4)
+    if vattn and "error" in vattn:
+        line["decode_contig_demand_mapped"] = vattn
+    elif vattn:
+        line["decode_contig_demand_mapped"] = {
+            k: ({kk: round(vv, 4) for kk, vv in v.items()}
+                if isinstance(v, dict) else round(v, 4))
+            for k, v in vattn.items()}
+        line["decode_paged_vs_demand_mapped_overhead"] = round(
+            paged["decode_op_ms_mean"] / vattn["decode_op_ms_mean"] - 1.0, 4)
     if cow:
         line["copy_on_write"] = {k: round(v, 4) for k, v in cow.items()}
     if prefill:

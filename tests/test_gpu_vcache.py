@@ -111,11 +111,11 @@ def test_grow_release_and_reuse():
                       O.decode_logical(q.float().cpu().numpy(), ks, vs, SCALE))
         assert err <= TOL
         # release sequence 0; its pages go to the pool and back into use
-        held = vc.held_bytes
+        held, mapped = vc.held_bytes, vc.mapped_bytes
         vc.release(0)
         assert vc.seq_pages(0) == 0
         assert vc.held_bytes == held
-        assert vc.mapped_bytes == held - 2 * HKV * 3 * P * D * 2
+        assert vc.mapped_bytes == mapped - 2 * HKV * 3 * P * D * 2
         k0, v0 = _bf16(rng, (200, HKV, D)), _bf16(rng, (200, HKV, D))
         assert vc.reserve(0, 200) == 2 * HKV * 2
         _write(vc, 0, 0, k0, v0)
