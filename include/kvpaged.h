@@ -282,6 +282,58 @@ kv_status contig_attn_prefill(void* out, const void* q,
                               kv_dtype dtype, void* stream);
 
 /* ---------------------------------------------------------------------
+ * Prefix cache over a block pool ["PagedAttention Nedir?" (bitcanli.com),
+ * section "Prefix Sharing Nasıl Çalışır?"]: the K/V of a prompt's leading
+ * tokens is reused only for an equal token sequence under the same model
+ * context, found by keys that cover a block's contents and the context
+ * before it, while the blocks are still cached. Host functions; no GPU.
+ *   Key of full block i of a prompt (kv_prefix_block_key): FNV-1a-64 over
+ *   the little-endian bytes of (key of block i-1, 0 for the first; salt;
+ *   the block's block_size token ids as int32). The salt identifies the
+ *   model / adapter context. Only full blocks are keyed.
+ *   An entry keeps its block id, parent key and tokens; a key matches only
+ *   if they are equal (a hash collision is a miss, never a wrong reuse).
+ *   Blocks a lookup or insert passes are stamped with increasing ticks from
+ *   the chain's last block to its first; eviction frees blocks only the
+ *   cache references (refcount 1), oldest stamp first.
+ * The cache holds one pool reference per cached block; the pool must
+ * outlive it. One host thread per pool. */
+typedef struct kv_prefix_cache kv_prefix_cache;
+
+uint64_t kv_prefix_block_key(uint64_t parent, uint64_t salt,
+                             const int32_t* tokens, int32_t block_size);
+
+kv_status kv_prefix_cache_create(kv_pool* pool, uint64_t salt,
+                                 kv_prefix_cache** out);
+/* Drops the cache's references (blocks only it held return to the pool). */
+void kv_prefix_cache_destroy(kv_prefix_cache* cache);
+
+/* Longest cached run of full blocks at the start of tokens[0, n): their ids
+ * go to out_blocks (room for n / block_size), their count to *num_blocks,
+ * and each gets one more reference for the caller's block table. */
+kv_status kv_prefix_cache_lookup(kv_prefix_cache* cache, const int32_t* tokens,
+                                 int32_t n, int32_t* out_blocks,
+                                 int32_t* num_blocks);
+
+/* blocks[i] holds the K/V of tokens [i*B, (i+1)*B) (the caller's table row,
+ * written). Adds the full blocks not cached yet (one cache reference each),
+ * keeps equal entries, stops at a colliding key; *num_inserted (may be NULL)
+ * = entries added. KV_EINVAL (nothing changed) if a block to add is not
+ * live. */
+kv_status kv_prefix_cache_insert(kv_prefix_cache* cache, const int32_t* tokens,
+                                 int32_t n, const int32_t* blocks,
+                                 int32_t* num_inserted);
+
+/* Free up to n blocks only the cache references, least recently used
+ * first; their ids go to freed (room for n; may be NULL). Returns the count
+ * (-1 on a bad argument). */
+int32_t kv_prefix_cache_evict(kv_prefix_cache* cache, int32_t n,
+                              int32_t* freed);
+
+/* Entries held (-1 if cache is NULL). */
+int32_t kv_prefix_cache_size(const kv_prefix_cache* cache);
+
+/* ---------------------------------------------------------------------
  * Contiguous KV cache on demand-mapped virtual memory ["Makale Bülteni —
  * vAttention", section "İddia ve Gerçeklik: vAttention"]: a virtually
  * contiguous buffer is reserved for every sequence's maximum context at

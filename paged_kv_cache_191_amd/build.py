@@ -12,8 +12,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = ["host.cpp", "vcache.cpp", "cache_ops.hip", "decode.hip",
-           "prefill.hip"]
+SOURCES = ["host.cpp", "prefix_cache.cpp", "vcache.cpp", "cache_ops.hip",
+           "decode.hip", "prefill.hip"]
 LIB = os.path.join(HERE, "libkvpaged.so")
 ARCH = os.environ.get("KVPAGED_ARCH", "gfx950")
 

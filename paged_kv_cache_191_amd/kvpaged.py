@@ -79,6 +79,15 @@ SIGNATURES = {
     "contig_attn_prefill": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _P,
                                    _I32, _I32, _I32, _I32, _F, _I32, _I32,
                                    _P]),
+    "kv_prefix_block_key": (ctypes.c_uint64, [ctypes.c_uint64,
+                                              ctypes.c_uint64, _PI32, _I32]),
+    "kv_prefix_cache_create": (_I32, [_P, ctypes.c_uint64,
+                                      ctypes.POINTER(_P)]),
+    "kv_prefix_cache_destroy": (None, [_P]),
+    "kv_prefix_cache_lookup": (_I32, [_P, _PI32, _I32, _PI32, _PI32]),
+    "kv_prefix_cache_insert": (_I32, [_P, _PI32, _I32, _PI32, _PI32]),
+    "kv_prefix_cache_evict": (_I32, [_P, _I32, _PI32]),
+    "kv_prefix_cache_size": (_I32, [_P]),
     "kv_vcache_granularity": (_I32, [ctypes.POINTER(_SZ)]),
     "kv_vcache_create": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32,
                                 ctypes.POINTER(_P)]),
@@ -271,6 +280,70 @@ def kv_slot_mapping(block_tables: np.ndarray, seq_ids, positions,
                                len(pos), int(block_size), _i64p(out))
     _check(st, "kv_slot_mapping")
     return out[:len(pos)]
+
+
+class PrefixCache:
+    """Owner of a native kv_prefix_cache over a KVPool (kv_prefix_cache_*).
+    The pool must stay open while the cache lives; close() drops the cache's
+    block references."""
+
+    def __init__(self, pool: KVPool, salt: int):
+        self._h = None
+        self.pool = pool
+        h = _P()
+        _check(lib().kv_prefix_cache_create(pool.handle,
+                                            int(salt) & (2**64 - 1),
+                                            ctypes.byref(h)),
+               "kv_prefix_cache_create")
+        self._h = h
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            lib().kv_prefix_cache_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def lookup(self, tokens) -> list:
+        t = _as_i32(tokens)
+        out = np.zeros(max(1, len(t) // self.pool.block_size), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(lib().kv_prefix_cache_lookup(self._h, _i32p(t), len(t),
+                                            _i32p(out), ctypes.byref(n)),
+               "kv_prefix_cache_lookup")
+        return out[:n.value].tolist()
+
+    def insert(self, tokens, blocks) -> int:
+        t = _as_i32(tokens)
+        b = _as_i32(blocks)
+        if len(b) < len(t) // self.pool.block_size:
+            raise ValueError("fewer blocks than full blocks of tokens")
+        n = ctypes.c_int32(0)
+        _check(lib().kv_prefix_cache_insert(self._h, _i32p(t), len(t),
+                                            _i32p(b), ctypes.byref(n)),
+               "kv_prefix_cache_insert")
+        return int(n.value)
+
+    def evict(self, n: int) -> list:
+        out = np.zeros(max(1, int(n)), dtype=np.int32)
+        k = lib().kv_prefix_cache_evict(self._h, int(n), _i32p(out))
+        if k < 0:
+            raise KVError(KV_EINVAL, "kv_prefix_cache_evict")
+        return out[:k].tolist()
+
+    def size(self) -> int:
+        return int(lib().kv_prefix_cache_size(self._h))
+
+
+def kv_prefix_block_key(parent: int, salt: int, tokens) -> int:
+    t = _as_i32(tokens)
+    return int(lib().kv_prefix_block_key(int(parent) & (2**64 - 1),
+                                         int(salt) & (2**64 - 1), _i32p(t),
+                                         len(t)))
 
 
 # --------------------------------------------------------------- device ---
