@@ -416,6 +416,47 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     return res
 
 
+def run_swap(w, device, n_blocks: int = 2048, reps: int = 5):
+    """Swap of n_blocks blocks of the workload's pool shape (K and V) out to a
+    pinned host pool and back in (kv_swap_blocks), timed with events: the
+    PCIe cost of preempting sequences when the device pool is full."""
+    import torch
+    from paged_kv_cache_191_amd import kvpaged as kv
+    shape = (n_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    dk = torch.randn(shape, dtype=torch.float32, device=device).to(
+        torch.bfloat16)
+    dv = torch.randn(shape, dtype=torch.float32, device=device).to(
+        torch.bfloat16)
+    hk = torch.empty(shape, dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty(shape, dtype=torch.bfloat16).pin_memory()
+    perm = np.random.default_rng([w.seed, 60]).permutation(n_blocks)
+    pairs = torch.from_numpy(np.stack([perm, np.arange(n_blocks)], 1).astype(
+        np.int32)).to(device)
+    back = torch.from_numpy(np.stack([np.arange(n_blocks), perm], 1).astype(
+        np.int32)).to(device)
+    t_out, t_in = [], []
+    for i in range(reps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        kv.kv_swap_blocks(dk, dv, hk, hv, pairs)
+        e[1].record()
+        kv.kv_swap_blocks(hk, hv, dk, dv, back)
+        e[2].record()
+        torch.cuda.synchronize()
+        if i:
+            t_out.append(e[0].elapsed_time(e[1]))
+            t_in.append(e[1].elapsed_time(e[2]))
+    nbytes = 2 * dk.numel() * 2
+    res = {"blocks": n_blocks, "bytes": nbytes,
+           "out_ms_median": float(np.median(t_out)),
+           "in_ms_median": float(np.median(t_in))}
+    res["out_GBps"] = nbytes / (res["out_ms_median"] * 1e-3) / 1e9
+    res["in_GBps"] = nbytes / (res["in_ms_median"] * 1e-3) / 1e9
+    del dk, dv, hk, hv
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_cow(w, steps: int, warmup: int, device):
     """Copy-on-write step: 256 sequences forked from a COW_PREFIX-token
     prefix whose last block is half full each append one token; 255 of them
@@ -767,7 +808,7 @@ def main() -> int:
     default_workload = args.workload == "llama3_8b_decode"
     headroom = wd.num_seqs * (-(-(args.steps + args.warmup) // wd.block_size)
                               + 1)
-    paged = contig = inp = cow = plain = vattn = None
+    paged = contig = inp = cow = plain = vattn = swap = None
     if not args.no_decode:
         log(f"drawing {wd.name}")
         inp = W.draw(wd, lambda L: pool_blocks(kv, wd, L, headroom))
@@ -801,6 +842,9 @@ def main() -> int:
         if wd.kind == "prefix" and not args.no_cow:
             log("copy-on-write step")
             cow = run_cow(wd, args.steps, args.warmup, device)
+        if default_workload:
+            log("block swap to pinned host memory and back")
+            swap = run_swap(wd, device)
 
     prefill = None
     if not args.no_prefill and (default_workload or args.no_decode):
@@ -897,6 +941,8 @@ def main() -> int:
             paged["decode_op_ms_mean"] / vattn["decode_op_ms_mean"] - 1.0, 4)
     if cow:
         line["copy_on_write"] = {k: round(v, 4) for k, v in cow.items()}
+    if swap:
+        line["block_swap"] = {k: round(v, 4) for k, v in swap.items()}
     if prefill:
         line["prefill"] = {k: {kk: round(vv, 4) for kk, vv in v.items()}
                            for k, v in prefill.items()}

@@ -281,6 +281,22 @@ kv_status contig_attn_prefill(void* out, const void* q,
                               int32_t head_dim, float scale, int32_t causal,
                               kv_dtype dtype, void* stream);
 
+/* Copy blocks between two pools of the same [blocks, Hkv, block_size, D]
+ * shape: the swap of blocks out to CPU memory when the device pool is full,
+ * and back in ["Makale Bülteni — PagedAttention ve vLLM", section "İddia
+ * ve Gerçeklik"]. pairs: int32 [n, 2] of (block of the source pool
+ * src_k/src_v with src_blocks blocks, block of the destination pool with
+ * dst_blocks blocks); a pair with an id outside its pool is skipped. Each
+ * pool and `pairs` may be device memory or pinned host memory (hipHostMalloc,
+ * e.g. torch's pin_memory) that the device addresses directly; other host
+ * memory -> KV_EINVAL. Destinations must be distinct and must not be read
+ * by another pair. Enqueued on `stream`; allocates nothing. */
+kv_status kv_swap_blocks(const void* src_k, const void* src_v,
+                         int32_t src_blocks, void* dst_k, void* dst_v,
+                         int32_t dst_blocks, const int32_t* pairs, int32_t n,
+                         int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, kv_dtype dtype, void* stream);
+
 /* ---------------------------------------------------------------------
  * Prefix cache over a block pool ["PagedAttention Nedir?" (bitcanli.com),
  * section "Prefix Sharing Nasıl Çalışır?"]: the K/V of a prompt's leading

@@ -162,3 +162,89 @@ extern "C" kv_status kv_copy_blocks(void* k_cache, void* v_cache,
   KVP_LAUNCH_CHECK("kv_copy_blocks");
   return KV_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Copies of whole blocks between two pools of the same shape, either of which
+// may be pinned host memory the device addresses directly: blocks swapped out
+// to CPU memory when the device pool is full, and back in ["Makale Bülteni —
+// PagedAttention ve vLLM", section "İddia ve Gerçeklik"].
+namespace {
+template <typename U>
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const U* __restrict__ sk, const U* __restrict__ sv, U* __restrict__ dk,
+    U* __restrict__ dv, const int32_t* __restrict__ pairs, int32_t n,
+    int32_t src_blocks, int32_t dst_blocks, int64_t units_per_block) {
+  const int64_t total = 2 * units_per_block;
+  for (int32_t p = blockIdx.y; p < n; p += gridDim.y) {
+    const int32_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+    if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) continue;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+      const bool is_v = i >= units_per_block;
+      const int64_t u = is_v ? i - units_per_block : i;
+      (is_v ? dv : dk)[(int64_t)dst * units_per_block + u] =
+          (is_v ? sv : sk)[(int64_t)src * units_per_block + u];
+    }
+  }
+}
+
+// Device address of a pointer the device can use: device memory as is,
+// pinned host memory through its device mapping. NULL otherwise.
+void* device_view(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // pageable host memory: clear the error
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged)
+    return const_cast<void*>(p);
+  if (a.type == hipMemoryTypeHost) return a.devicePointer;
+  return nullptr;
+}
+}  // namespace
+
+extern "C" kv_status kv_swap_blocks(const void* src_k, const void* src_v,
+                                    int32_t src_blocks, void* dst_k,
+                                    void* dst_v, int32_t dst_blocks,
+                                    const int32_t* pairs, int32_t n,
+                                    int32_t block_size, int32_t num_kv_heads,
+                                    int32_t head_dim, kv_dtype dtype,
+                                    void* stream) {
+  if (dtype != KV_F32 && dtype != KV_BF16)
+    return kvp_fail(KV_EINVAL, "kv_swap_blocks: unknown dtype %d", (int)dtype);
+  if (n < 0 || src_blocks < 0 || dst_blocks < 0 || block_size <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0)
+    return kvp_fail(KV_EINVAL, "kv_swap_blocks: bad shape");
+  if (n == 0) return KV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs)
+    return kvp_fail(KV_EINVAL, "kv_swap_blocks: NULL pointer");
+  const void* ptrs[5] = {src_k, src_v, dst_k, dst_v, pairs};
+  void* dev[5];
+  for (int i = 0; i < 5; ++i) {
+    dev[i] = device_view(ptrs[i]);
+    if (!dev[i])
+      return kvp_fail(KV_EINVAL,
+                      "kv_swap_blocks: %s is not device or pinned host memory",
+                      i == 4 ? "pairs" : (i < 2 ? "a source pool" :
+                                          "a destination pool"));
+  }
+  const int64_t block_bytes =
+      (int64_t)block_size * num_kv_heads * head_dim * elem_size(dtype);
+  hipStream_t st = (hipStream_t)stream;
+  const int threads = 256;
+  auto go = [&](auto unit) {
+    using U = decltype(unit);
+    const int64_t units = block_bytes / (int64_t)sizeof(U);
+    const int64_t per_pair = (2 * units + threads - 1) / threads;
+    dim3 grid((unsigned)(per_pair < 1024 ? per_pair : 1024),
+              (unsigned)(n < 65535 ? n : 65535));
+    swap_blocks_kernel<U><<<grid, threads, 0, st>>>(
+        (const U*)dev[0], (const U*)dev[1], (U*)dev[2], (U*)dev[3],
+        (const int32_t*)dev[4], n, src_blocks, dst_blocks, units);
+  };
+  if (block_bytes % 16 == 0) go(u32x4{});
+  else if (block_bytes % 4 == 0) go(uint32_t{});
+  else go(uint16_t{});
+  KVP_LAUNCH_CHECK("kv_swap_blocks");
+  return KV_OK;
+}

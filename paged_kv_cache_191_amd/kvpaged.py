@@ -60,6 +60,8 @@ SIGNATURES = {
                                     _I32, _I32, _I32, _P]),
     "kv_copy_blocks": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                               _I32, _P]),
+    "kv_swap_blocks": (_I32, [_P, _P, _I32, _P, _P, _I32, _P, _I32, _I32,
+                              _I32, _I32, _I32, _P]),
     "kv_decode_chunks": (_I32, [_I32, _I32]),
     "kv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "paged_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
@@ -403,6 +405,30 @@ def kv_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
         _dev(src_dst, "src_dst", torch.int32), src_dst.shape[0], nb, bs, hkv,
         d, _dtype_code(k_cache), _stream(stream))
     _check(st, "kv_copy_blocks")
+
+
+def kv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:
+    """Copy blocks src -> dst between two pools [blocks, Hkv, B, D] (device
+    tensors or pinned host tensors); pairs int32 [n, 2] (device or pinned)."""
+    sb, hkv, bs, d = src_k.shape
+    db = dst_k.shape[0]
+    if tuple(dst_k.shape[1:]) != (hkv, bs, d):
+        raise ValueError("the pools differ in Hkv, block_size or head_dim")
+    for t, name in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"),
+                    (dst_v, "dst_v"), (pairs, "pairs")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for t in (src_v, dst_k, dst_v):
+        if t.dtype != src_k.dtype:
+            raise TypeError("the pools differ in dtype")
+    torch = _torch()
+    if pairs.dtype != torch.int32:
+        raise TypeError("pairs must be int32")
+    st = lib().kv_swap_blocks(src_k.data_ptr(), src_v.data_ptr(), sb,
+                              dst_k.data_ptr(), dst_v.data_ptr(), db,
+                              pairs.data_ptr(), pairs.shape[0], bs, hkv, d,
+                              _dtype_code(src_k), _stream(stream))
+    _check(st, "kv_swap_blocks")
 
 
 def kv_decode_chunks(num_q_heads, num_kv_heads) -> int:
