@@ -17,4 +17,4 @@ against something other than itself (a worked example on the pages, a closed
 form, brute force in exact decimal arithmetic, a library routine, or an
 invariant the pages state). None is "parity unpinned".
 """
-from . import allocator, attention, prefix_cache  # noqa: F401
+from . import allocator, attention, fp8, prefix_cache  # noqa: F401
