@@ -75,6 +75,9 @@ VMM_PREFILL_PAGE_TOKENS = 1024
 # pages one process maps at most in a decode run (each page is one device
 # allocation; larger pages are used when the contexts would need more)
 VMM_MAX_PAGES = 16384
+# per-tensor scale of the fp8 E4M3 caches: N(0, 1) K/V values up to about
+# 5.5 land near the format's largest finite value, 448
+FP8_SCALE = 0.0123
 
 TRAFFIC_PROFILES = {
     "llama3_8b_decode": os.path.join(ROOT, "profiles",
@@ -108,14 +111,16 @@ def recorded_traffic(workload: str = "llama3_8b_decode"):
 
 
 def decode_bytes(ctx: np.ndarray, hq: int, hkv: int, d: int, B: int,
-                 paged: bool, esize: int = 2, shared: int = 0) -> int:
+                 paged: bool, esize: int = 2, shared: int = 0,
+                 kv_esize: int = 0) -> int:
     """Algorithmic bytes of one decode call: K and V of every context token
-    once per KV head, q and o, the block-table entries in use, lengths.
-    ``shared`` leading tokens of every context sit in the same physical
-    blocks for all sequences and count once."""
+    once per KV head (``kv_esize`` bytes per value, default ``esize``), q and
+    o, the block-table entries in use, lengths. ``shared`` leading tokens of
+    every context sit in the same physical blocks for all sequences and count
+    once."""
     toks = int(ctx.sum()) - shared * (len(ctx) - 1) if shared else \
         int(ctx.sum())
-    kvb = toks * hkv * d * 2 * esize
+    kvb = toks * hkv * d * 2 * (kv_esize or esize)
     qo = 2 * len(ctx) * hq * d * esize
     table = int(sum(-(-int(n) // B) for n in ctx)) * 4 if paged else 0
     return kvb + qo + table + 4 * len(ctx)
@@ -149,7 +154,7 @@ class DecodeReplica:
 
     def __init__(self, inp, k_dev, v_dev, new_k, new_v, paged: bool,
                  steps: int, device, shared_op: bool = False,
-                 vmm_page_tokens: int = 0):
+                 vmm_page_tokens: int = 0, fp8: bool = False):
         import torch
         from paged_kv_cache_191_amd import kvpaged as kv
         from paged_kv_cache_191_amd import workloads as W
@@ -182,6 +187,10 @@ class DecodeReplica:
         self.out = torch.empty_like(self.q)
         self.new_k, self.new_v = new_k, new_v
         tdt = inp.k.dtype
+        # fp8 E4M3 caches (paged only), one scale per tensor
+        self.fp8 = fp8 and paged
+        if self.fp8:
+            tdt = torch.uint8
         self.h_table[:] = -1
         self.h_lens[:] = 0
         self.shared = 0
@@ -199,9 +208,14 @@ class DecodeReplica:
                 assert len(pairs) == 0
                 rows = torch.from_numpy(
                     W.logical_rows(inp, s)[first:first + count]).to(device)
-                kv.kv_reshape_and_cache(k_dev[rows], v_dev[rows],
-                                        torch.from_numpy(slots).to(device),
-                                        self.k, self.v)
+                d_slots = torch.from_numpy(slots).to(device)
+                if self.fp8:
+                    kv.kv_reshape_and_cache_fp8(k_dev[rows], v_dev[rows],
+                                                d_slots, self.k, self.v,
+                                                FP8_SCALE, FP8_SCALE)
+                else:
+                    kv.kv_reshape_and_cache(k_dev[rows], v_dev[rows],
+                                            d_slots, self.k, self.v)
 
             P = inp.prefix_rows
             if P:
@@ -300,12 +314,21 @@ class DecodeReplica:
         self.uploaded.record()
         if ev is not None:
             ev[0].record()
-        kv.kv_reshape_and_cache(self.new_k, self.new_v, self.d_slots, self.k,
-                                self.v)
+        if self.fp8:
+            kv.kv_reshape_and_cache_fp8(self.new_k, self.new_v, self.d_slots,
+                                        self.k, self.v, FP8_SCALE, FP8_SCALE)
+        else:
+            kv.kv_reshape_and_cache(self.new_k, self.new_v, self.d_slots,
+                                    self.k, self.v)
         max_ctx = int(self.h_lens.max())
         if ev is not None:
             ev[1].record()
-        if self.shared_op:
+        if self.fp8:
+            kv.paged_attn_decode_fp8(self.out, self.q, self.k, self.v,
+                                     self.d_table, self.d_lens, max_ctx,
+                                     self.scale, FP8_SCALE, FP8_SCALE,
+                                     self.ws)
+        elif self.shared_op:
             kv.paged_attn_decode_shared_prefix(
                 self.out, self.q, self.k, self.v, self.d_table, self.d_lens,
                 max_ctx, self.g_starts, self.g_shared, self.w.num_seqs,
@@ -332,14 +355,15 @@ def new_token_kv(w, device):
 
 
 def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
-               device, shared_op: bool = False, vmm_page_tokens: int = 0):
+               device, shared_op: bool = False, vmm_page_tokens: int = 0,
+               fp8: bool = False):
     import torch
     w = inp.workload
     new_k, new_v = new_token_kv(w, device)
     k_dev, v_dev = inp.k.to(device), inp.v.to(device)
     reps_ = [DecodeReplica(inp, k_dev, v_dev, new_k, new_v, paged,
                            steps + warmup, device, shared_op,
-                           vmm_page_tokens)
+                           vmm_page_tokens, fp8)
              for _ in range(reps)]
     del k_dev, v_dev
     for i in range(warmup):
@@ -356,8 +380,9 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         r.host_append()
         args = (r.h_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
                 w.block_size, paged)
-        total_bytes += decode_bytes(*args, shared=r.shared)
-        logical_bytes += decode_bytes(*args)
+        kv_es = 1 if fp8 else 0
+        total_bytes += decode_bytes(*args, shared=r.shared, kv_esize=kv_es)
+        logical_bytes += decode_bytes(*args, kv_esize=kv_es)
         r.device_step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -379,8 +404,9 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         res["logical_bytes_per_step"] = logical_bytes / steps
         res["decode_op_effective_GBps"] = (logical_bytes / steps) / (
             op["mean"] * 1e-3) / 1e9
-    # the new rows: K and V, read once and written once
-    tok_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2 * 2
+    # the new rows: K and V, read once (bf16) and written once
+    tok_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * (
+        2 + (1 if fp8 else 2))
     res["reshape_and_cache_GBps"] = tok_bytes / (rc["median"] * 1e-3) / 1e9
     if vmm_page_tokens and not paged:
         P = vmm_page_tokens
@@ -776,6 +802,8 @@ def main() -> int:
                          "head (1024 x 128 bf16 values = 256 KiB; one "
                          "allocation per page, and a process holds some "
                          "tens of thousands at most)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the paged decode over fp8 E4M3 caches")
     ap.add_argument("--no-cow", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -808,7 +836,7 @@ def main() -> int:
     default_workload = args.workload == "llama3_8b_decode"
     headroom = wd.num_seqs * (-(-(args.steps + args.warmup) // wd.block_size)
                               + 1)
-    paged = contig = inp = cow = plain = vattn = swap = None
+    paged = contig = inp = cow = plain = vattn = swap = fp8 = None
     if not args.no_decode:
         log(f"drawing {wd.name}")
         inp = W.draw(wd, lambda L: pool_blocks(kv, wd, L, headroom))
@@ -839,6 +867,10 @@ def main() -> int:
                 except kv.KVError as e:
                     log(f"demand-mapped decode failed: {e}")
                     vattn = {"error": str(e)}
+        if not args.no_fp8 and wd.kind != "prefix":
+            log("paged decode steps over fp8 caches")
+            fp8 = run_decode(inp, True, args.steps, args.warmup,
+                             args.replicas, device, fp8=True)
         if wd.kind == "prefix" and not args.no_cow:
             log("copy-on-write step")
             cow = run_cow(wd, args.steps, args.warmup, device)
@@ -939,6 +971,12 @@ def main() -> int:
             for k, v in vattn.items()}
         line["decode_paged_vs_demand_mapped_overhead"] = round(
             paged["decode_op_ms_mean"] / vattn["decode_op_ms_mean"] - 1.0, 4)
+    if fp8:
+        line["decode_paged_fp8"] = {k: round(v, 4) for k, v in fp8.items()}
+        line["decode_paged_fp8"]["frac_of_hbm_peak"] = round(
+            fp8["decode_op_GBps"] / HBM_PEAK_GBPS, 4)
+        line["decode_fp8_speedup_vs_bf16"] = round(
+            paged["decode_op_ms_mean"] / fp8["decode_op_ms_mean"], 4)
     if cow:
         line["copy_on_write"] = {k: round(v, 4) for k, v in cow.items()}
     if swap:

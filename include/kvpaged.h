@@ -298,6 +298,54 @@ kv_status kv_swap_blocks(const void* src_k, const void* src_v,
                          int32_t head_dim, kv_dtype dtype, void* stream);
 
 /* ---------------------------------------------------------------------
+ * FP8 K/V cache. Lower-precision storage of the cache is a separate lever
+ * from paging ["PagedAttention Nedir?" (bitcanli.com), section "KV Cache'i
+ * Sıkıştırıyor mu?"]; FP8 is among the serving stack's quantisation schemes
+ * ["Makale Bülteni — PagedAttention ve vLLM", section "Kod ve Entegrasyon
+ * Haritası"]. Format: OCP E4M3 ("E4M3FN": bias 7, no infinities, largest
+ * finite 448), one byte per value, in the same [blocks, Hkv, block_size, D]
+ * (or [S, Hkv, seq_stride, D]) layout as the bf16 caches. A value x is
+ * stored as E4M3(clamp(x * fl32(1 / scale), -448, 448)): fp32 product with
+ * the reciprocal rounded to fp32, maxNum/minNum clamp (a NaN becomes -448),
+ * round to nearest, ties to even; it reads back as E4M3 value * scale.
+ * One scale per tensor (k_scale for K, v_scale for V), finite and > 0. */
+
+/* kv_reshape_and_cache for an fp8 cache: k, v are bf16 rows [num_tokens,
+ * Hkv, D] (16-byte aligned), the caches hold codes (8-byte aligned);
+ * D % 8 == 0. Slots as in kv_reshape_and_cache. */
+kv_status kv_reshape_and_cache_fp8(const void* k, const void* v,
+                                   const int64_t* slots, int32_t num_tokens,
+                                   void* k_cache, void* v_cache,
+                                   int64_t num_slots, int32_t block_size,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   float k_scale, float v_scale, void* stream);
+
+/* paged_attn_decode / contig_attn_decode over fp8 caches: q and out are
+ * bf16; attention is computed on the dequantised K (k_scale folded into the
+ * softmax scale) and V (v_scale applied to the output). Workspace as for
+ * the bf16 calls (kv_decode_workspace_bytes). Only head_dim 128 and, paged,
+ * block_size a multiple of 16 (else KV_EUNSUPPORTED). */
+kv_status paged_attn_decode_fp8(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, int32_t num_blocks,
+                                const int32_t* block_tables, int32_t bt_stride,
+                                const int32_t* context_lens,
+                                int32_t max_context, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size,
+                                float scale, float k_scale, float v_scale,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+kv_status contig_attn_decode_fp8(void* out, const void* q, const void* k,
+                                 const void* v, int32_t seq_stride,
+                                 const int32_t* context_lens,
+                                 int32_t max_context, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float scale, float k_scale,
+                                 float v_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
  * Prefix cache over a block pool ["PagedAttention Nedir?" (bitcanli.com),
  * section "Prefix Sharing Nasıl Çalışır?"]: the K/V of a prompt's leading
  * tokens is reused only for an equal token sequence under the same model

@@ -74,15 +74,13 @@ def quantize(x, inv_scale: float) -> np.ndarray:
     +-448 (maxNum/minNum), round to nearest, ties to even."""
     prod = np.float32(np.asarray(x, dtype=np.float32)) * np.float32(inv_scale)
     prod = np.fmin(np.fmax(prod, np.float32(-MAX)), np.float32(MAX))
-    flat = prod.reshape(-1)
-    out = np.empty(flat.shape, dtype=np.uint8)
-    cache = {}
-    for i, v in enumerate(flat.tolist()):
-        key = (v, np.signbit(flat[i]))
-        if key not in cache:
-            cache[key] = encode_value(float(flat[i]))
-        out[i] = cache[key]
-    return out.reshape(prod.shape)
+    # each distinct fp32 bit pattern (so -0 and +0 stay apart) is encoded
+    # once by the search above
+    bits, inverse = np.unique(np.ascontiguousarray(prod).view(np.uint32),
+                              return_inverse=True)
+    codes = np.array([encode_value(float(b)) for b in bits.view(np.float32)],
+                     dtype=np.uint8)
+    return codes[inverse.reshape(-1)].reshape(prod.shape)
 
 
 def dequantize(codes, scale: float) -> np.ndarray:

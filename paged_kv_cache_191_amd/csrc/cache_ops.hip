@@ -71,7 +71,94 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 
 size_t elem_size(kv_dtype dt) { return dt == KV_F32 ? 4 : 2; }
 
+// bf16 -> fp8 E4M3 code of x * inv: fp32 product, clamped to the format's
+// finite range with maxNum/minNum (a NaN product becomes -448), then the
+// hardware conversion (round to nearest, ties to even).
+__device__ __forceinline__ float fp8_prep(uint32_t bf16_bits, float inv) {
+  const float x = __builtin_bit_cast(float, bf16_bits << 16) * inv;
+  return fminf(fmaxf(x, -448.f), 448.f);
+}
+
+__device__ __forceinline__ uint32_t fp8_pack4(uint32_t w0, uint32_t w1,
+                                              float inv) {
+  int r = 0;
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prep(w0 & 0xFFFF, inv),
+                                      fp8_prep(w0 >> 16, inv), r, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prep(w1 & 0xFFFF, inv),
+                                      fp8_prep(w1 >> 16, inv), r, true);
+  return (uint32_t)r;
+}
+
+// fp8 variant of scatter_rows_kernel: one item = 8 values of one head row
+// (16 source bytes of bf16 -> 8 cache bytes of codes).
+__global__ __launch_bounds__(256) void scatter_rows_fp8_kernel(
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+    const int64_t* __restrict__ slots, int32_t num_tokens, u32x2* k_cache,
+    u32x2* v_cache, int64_t num_slots, int32_t block_size,
+    int32_t num_kv_heads, int32_t units_per_head, float k_inv, float v_inv) {
+  const int64_t per_token = (int64_t)num_kv_heads * units_per_head;
+  const int64_t per_tensor = (int64_t)num_tokens * per_token;
+  const int64_t total = 2 * per_tensor;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const bool is_v = i >= per_tensor;
+    const int64_t j = is_v ? i - per_tensor : i;
+    const int64_t t = j / per_token;
+    const int64_t r = j - t * per_token;
+    const int64_t h = r / units_per_head;
+    const int64_t u = r - h * units_per_head;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / block_size;
+    const int64_t off = slot - blk * block_size;
+    const u32x4 x = (is_v ? v : k)[t * per_token + r];
+    const float inv = is_v ? v_inv : k_inv;
+    u32x2 c;
+    c[0] = fp8_pack4(x[0], x[1], inv);
+    c[1] = fp8_pack4(x[2], x[3], inv);
+    (is_v ? v_cache : k_cache)
+        [((blk * num_kv_heads + h) * block_size + off) * units_per_head + u] =
+        c;
+  }
+}
+
 }  // namespace
+
+extern "C" kv_status kv_reshape_and_cache_fp8(
+    const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
+    void* k_cache, void* v_cache, int64_t num_slots, int32_t block_size,
+    int32_t num_kv_heads, int32_t head_dim, float k_scale, float v_scale,
+    void* stream) {
+  const char* name = "kv_reshape_and_cache_fp8";
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      head_dim % 8 != 0 || num_slots < 0 || block_size <= 0 ||
+      num_slots % block_size != 0)
+    return kvp_fail(KV_EINVAL, "%s: bad shape (D=%d slots=%lld block_size=%d;"
+                    " D must be a multiple of 8)", name, head_dim,
+                    (long long)num_slots, block_size);
+  if (!(k_scale > 0.f) || !(k_scale < INFINITY) || !(v_scale > 0.f) ||
+      !(v_scale < INFINITY))
+    return kvp_fail(KV_EINVAL, "%s: k_scale and v_scale must be finite and "
+                    "> 0", name);
+  if (num_tokens == 0) return KV_OK;
+  if (!k || !v || !slots || !k_cache || !v_cache)
+    return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
+  if (((uintptr_t)k | (uintptr_t)v) % 16 || ((uintptr_t)k_cache |
+                                              (uintptr_t)v_cache) % 8)
+    return kvp_fail(KV_EINVAL, "%s: k/v must be 16-byte and the caches "
+                    "8-byte aligned", name);
+  const float k_inv = 1.f / k_scale, v_inv = 1.f / v_scale;
+  hipStream_t st = (hipStream_t)stream;
+  const int threads = 256;
+  const int32_t uph = head_dim / 8;
+  const int64_t items = 2 * (int64_t)num_tokens * num_kv_heads * uph;
+  const int64_t g = (items + threads - 1) / threads;
+  scatter_rows_fp8_kernel<<<(int)(g < 65536 ? g : 65536), threads, 0, st>>>(
+      (const u32x4*)k, (const u32x4*)v, slots, num_tokens, (u32x2*)k_cache,
+      (u32x2*)v_cache, num_slots, block_size, num_kv_heads, uph, k_inv, v_inv);
+  KVP_LAUNCH_CHECK(name);
+  return KV_OK;
+}
 
 extern "C" kv_status kv_reshape_and_cache(const void* k, const void* v,
                                           const int64_t* slots,

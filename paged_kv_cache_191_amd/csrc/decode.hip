@@ -87,7 +87,8 @@ struct DecodeArgs {
   int32_t group;        // hq / hkv
   int32_t head_blocks;  // ceil(group / 16)
   int32_t head_dim;
-  float scale_log2;     // scale * log2(e)
+  float scale_log2;     // scale * log2(e) (fp8 K/V: times k_scale)
+  float v_scale;        // fp8 K/V: scale of V (outputs are multiplied by it)
   int32_t n_chunks;     // chunks per (KV head, head block)
   float* ws_o;          // [n_chunks, 2, Hq, D] unnormalised partial outputs
   float* ws_ml;         // [n_chunks, 2, Hq, 2] (reference max, sum)
@@ -155,9 +156,28 @@ __device__ __forceinline__ int chunk_tiles(int total, int n_chunks) {
 // ---------------------------------------------------------------------------
 // MFMA fast path
 // ---------------------------------------------------------------------------
-template <bool PAGED>
+// 8 fp8 E4M3 values (two dwords) -> 8 bf16 (exact: every E4M3 value is a
+// bf16 value).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    r[2 * i] = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+    r[2 * i + 1] = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+  }
+  return r;
+}
+
+// KV8: K/V cache in fp8 E4M3 (one byte per value, converted to bf16 in
+// registers; K's scale is folded into scale_log2, V's applied to outputs).
+template <bool PAGED, bool KV8>
 __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     DecodeArgs a) {
+  constexpr int ES = KV8 ? 1 : 2;  // bytes per K/V value
+  constexpr int KL = KV8 ? 2 : 4;  // 16-byte K loads per token row per tile
+  constexpr int TPI = KV8 ? 2 : 1; // tiles whose loads are issued together
   __shared__ int s_cs[kMaxSeqs + 1];
   __shared__ int s_part[kWaves * kWave];
   __shared__ float sm_o[kWaves][kHeadBlk][kD];
@@ -225,8 +245,8 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   const int h_in_group = hblk * kHeadBlk + r16;
   const bool h_valid = h_in_group < a.group;
   const int nh = min(kHeadBlk, a.group - hblk * kHeadBlk);
-  const bf16* kbase = (const bf16*)a.k;
-  const bf16* vbase = (const bf16*)a.v;
+  const char* kbase = (const char*)a.k;
+  const char* vbase = (const char*)a.v;
 
   for (int pos = c0; pos < c1; ++s) {
     const int seq_lo = s_cs[s];
@@ -242,13 +262,15 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     const int hi = min(P + kTile * hi_t, L);
 
     const int qh = g * a.group + (h_valid ? h_in_group : 0);
-    bf16x8 qop[4];  // Q^T: B operand, head r16, d = 32 i + 8 grp + e
+    // Q^T: B operand, head r16; d = 32 i + 8 grp + e (bf16 K) or
+    // d = 32 grp + 8 i + e (fp8 K), matching the K operands
+    bf16x8 qop[4];
     {
-      const bf16* qp =
-          (const bf16*)a.q + ((int64_t)s * a.hq + qh) * kD + 8 * grp;
+      const bf16* qp = (const bf16*)a.q + ((int64_t)s * a.hq + qh) * kD +
+                       (KV8 ? 32 : 8) * grp;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        u32x4 raw = ld16(qp + 32 * i);
+        u32x4 raw = ld16(qp + (KV8 ? 8 : 32) * i);
         if (!h_valid) raw = u32x4{0, 0, 0, 0};
         qop[i] = as_bf16x8(raw);
       }
@@ -287,52 +309,83 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
         return min(t_al + kTile * (kb0 + w + kWaves * j) + 16 * hf,
                    last_grp_pos);
       };
-      auto half_ptr = [&](const bf16* base, int j, int hf) -> const char* {
+      auto half_ptr = [&](const char* base, int j, int hf) -> const char* {
         int64_t row;
         if (PAGED)
           row = __builtin_amdgcn_readlane(row_lane, 2 * j + hf);
         else
           row = seq_row0 + half_start(j, hf);
-        return (const char*)(base + row * kD);
+        return base + row * (kD * ES);
       };
       auto lane_off = [&](int j, int hf, int off, int chunk) -> uint32_t {
         const int r = PAGED ? off : min(off, hi - 1 - half_start(j, hf));
-        return (uint32_t)(r * (kD * 2) + 16 * chunk);
+        return (uint32_t)(r * (kD * ES) + 8 * ES * chunk);
+      };
+      // 8 consecutive K/V values of a row, as stored; to_bf16 widens them
+      // once they are needed (after every load of the tile is issued)
+      auto ld8v = [&](const char* p) __attribute__((always_inline)) {
+        if constexpr (KV8)
+          return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        else
+          return ld16_stream(p);
+      };
+      using Raw = decltype(ld8v(kbase));
+      auto to_bf16 = [](Raw r) __attribute__((always_inline)) -> u32x4 {
+        if constexpr (KV8)
+          return fp8x8_to_bf16(r);
+        else
+          return r;
       };
       const int k_end = min(n_tiles, kb0 + kWaves * (kGroupsPerLoad / 2));
-      for (int j = 0; kb0 + w + kWaves * j < k_end; ++j) {
-        const int t = t_al + kTile * (kb0 + w + kWaves * j);
-        // K: A operand of S^T (token r16 of each half, d = 32 i + 8 grp + e)
-        u32x4 kr[2][4];
+      // Raw K of a tile: kraw[hf][i] = 16 bytes of token r16 of half hf.
+      //   bf16: i < 4, d = 32 i + 8 grp .. +7 (one MFMA operand each);
+      //   fp8:  i < 2, d = 32 grp + 16 i .. +15 (two MFMA operands each).
+      // Raw V: rows tau(grp, e) = 16 (e / 4) + 4 grp + e % 4, d-chunk r16.
+      auto load_tile = [&](int j, u32x4 (&kraw)[2][KL], Raw (&vraw)[8])
+          __attribute__((always_inline)) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const char* kp = half_ptr(kbase, j, hf);
-          const uint32_t ko = lane_off(j, hf, r16, grp);
+          if constexpr (KV8) {
+            const uint32_t ko = lane_off(j, hf, r16, 4 * grp);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            kr[hf][i] = ld16_stream(kp + ko + 64 * i);
+            for (int i = 0; i < KL; ++i) kraw[hf][i] = ld16_stream(kp + ko + 16 * i);
+          } else {
+            const uint32_t ko = lane_off(j, hf, r16, grp);
+#pragma unroll
+            for (int i = 0; i < KL; ++i) kraw[hf][i] = ld16_stream(kp + ko + 64 * i);
+          }
         }
-        // V: rows tau(grp, e) = 16 (e / 4) + 4 grp + e % 4, d-chunk r16
-        u32x4 vr[8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const char* vp = half_ptr(vbase, j, hf);
 #pragma unroll
           for (int e = 4 * hf; e < 4 * hf + 4; ++e)
-            vr[e] = ld16_stream(vp + lane_off(j, hf, 4 * grp + (e & 3), r16));
+            vraw[e] = ld8v(vp + lane_off(j, hf, 4 * grp + (e & 3), r16));
         }
-        // All 16 loads of the tile are issued before the first MFMA waits
-        // for any of them (the scheduler would otherwise start on the K half
-        // and issue the V loads late, halving the bytes in flight).
-        __builtin_amdgcn_sched_barrier(0);
-
+      };
+      // K operand i (8 bf16) of half hf
+      auto k_op = [&](const u32x4 (&kraw)[2][KL], int hf, int i)
+          __attribute__((always_inline)) -> bf16x8 {
+        if constexpr (KV8) {
+          const u32x4 r = kraw[hf][i >> 1];
+          return as_bf16x8(fp8x8_to_bf16(
+              (i & 1) ? u32x2{r[2], r[3]} : u32x2{r[0], r[1]}));
+        } else {
+          return as_bf16x8(kraw[hf][i]);
+        }
+      };
+      auto compute_tile = [&](int j, const u32x4 (&kraw)[2][KL],
+                              const Raw (&vraw)[8])
+          __attribute__((always_inline)) {
+        const int t = t_al + kTile * (kb0 + w + kWaves * j);
         f32x4 sc[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sc[hf] = mfma16(as_bf16x8(kr[hf][i]), qop[i], sc[hf]);
+            sc[hf] = mfma16(k_op(kraw, hf, i), qop[i], sc[hf]);
         }
 
         const bool full = t + kTile <= hi;
@@ -379,6 +432,9 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
         pb[2] = pack_bf16(p[1][0], p[1][1]);
         pb[3] = pack_bf16(p[1][2], p[1][3]);
         const bf16x8 pop = as_bf16x8(pb);
+        u32x4 vr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vr[e] = to_bf16(vraw[e]);
         if (!full) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -396,6 +452,27 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
             am[q4] = (m & 1) ? pick_hi(vr[2 * q4][wd], vr[2 * q4 + 1][wd])
                              : pick_lo(vr[2 * q4][wd], vr[2 * q4 + 1][wd]);
           o[m] = mfma16(as_bf16x8(am), pop, o[m]);
+        }
+      };
+      // fp8 loads carry half the bytes of bf16 ones, so a wave issues the
+      // loads of two tiles before it computes either (the same bytes in
+      // flight, and the same raw registers, as one bf16 tile).
+      for (int j = 0; kb0 + w + kWaves * j < k_end; j += TPI) {
+        u32x4 kraw[TPI][2][KL];
+        Raw vraw[TPI][8];
+        load_tile(j, kraw[0], vraw[0]);
+        bool two = false;
+        if constexpr (TPI == 2) {
+          two = kb0 + w + kWaves * (j + 1) < k_end;
+          if (two) load_tile(j + 1, kraw[1], vraw[1]);
+        }
+        // All loads of the tile(s) are issued before the first MFMA waits
+        // for any of them (the scheduler would otherwise start on the K half
+        // and issue the V loads late, halving the bytes in flight).
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile(j, kraw[0], vraw[0]);
+        if constexpr (TPI == 2) {
+          if (two) compute_tile(j + 1, kraw[1], vraw[1]);
         }
       }
     }
@@ -445,6 +522,10 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
             acc[4 + jj] += cw * hi4[jj];
           }
         }
+      }
+      if constexpr (KV8) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc[jj] *= a.v_scale;
       }
       const int head = g * a.group + hblk * kHeadBlk + h;
       if (whole && P > 0) {
@@ -681,9 +762,11 @@ bool fast_path_ok(kv_dtype dtype, int head_dim, int block_size, bool paged) {
          (!paged || block_size % 16 == 0);
 }
 
+// kv8: K/V cache in fp8 E4M3 (q and out stay bf16, dtype must be KV_BF16);
+// only the fast path reads it.
 kv_status run_decode(const char* name, bool paged, DecodeArgs a,
                      kv_dtype dtype, void* workspace, size_t ws_bytes,
-                     hipStream_t st) {
+                     hipStream_t st, bool kv8 = false) {
   if (dtype != KV_F32 && dtype != KV_BF16)
     return kvp_fail(KV_EINVAL, "%s: unknown dtype %d", name, (int)dtype);
   if (!(a.scale_log2 > 0.f) || !(a.scale_log2 < INFINITY))
@@ -706,7 +789,13 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
     return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
   a.group = a.hq / a.hkv;
 
-  if (fast_path_ok(dtype, a.head_dim, a.block_size, paged)) {
+  const bool fast = fast_path_ok(dtype, a.head_dim, a.block_size, paged);
+  if (kv8 && !fast)
+    return kvp_fail(KV_EUNSUPPORTED,
+                    "%s: fp8 K/V needs head_dim %d and block_size a multiple "
+                    "of 16 (got D=%d B=%d)", name, kD, a.head_dim,
+                    a.block_size);
+  if (fast) {
     a.head_blocks = (a.group + kHeadBlk - 1) / kHeadBlk;
     a.n_chunks = choose_chunks(a.hkv, a.head_blocks);
     const int per_launch = a.num_seqs < kMaxSeqs ? a.num_seqs : kMaxSeqs;
@@ -738,15 +827,20 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
       if (paged) {
         b.bt = a.bt + (size_t)s0 * a.bt_stride;
       } else {
-        const size_t seq_elems = (size_t)a.hkv * a.seq_stride * kD;
-        b.k = (const bf16*)a.k + (size_t)s0 * seq_elems;
-        b.v = (const bf16*)a.v + (size_t)s0 * seq_elems;
+        const size_t seq_bytes =
+            (size_t)a.hkv * a.seq_stride * kD * (kv8 ? 1 : sizeof(bf16));
+        b.k = (const char*)a.k + (size_t)s0 * seq_bytes;
+        b.v = (const char*)a.v + (size_t)s0 * seq_bytes;
       }
       dim3 grid(a.hkv * a.head_blocks, a.n_chunks);
-      if (paged)
-        decode_sk_kernel<true><<<grid, kWaves * kWave, 0, st>>>(b);
+      if (paged && kv8)
+        decode_sk_kernel<true, true><<<grid, kWaves * kWave, 0, st>>>(b);
+      else if (paged)
+        decode_sk_kernel<true, false><<<grid, kWaves * kWave, 0, st>>>(b);
+      else if (kv8)
+        decode_sk_kernel<false, true><<<grid, kWaves * kWave, 0, st>>>(b);
       else
-        decode_sk_kernel<false><<<grid, kWaves * kWave, 0, st>>>(b);
+        decode_sk_kernel<false, false><<<grid, kWaves * kWave, 0, st>>>(b);
       KVP_LAUNCH_CHECK(name);
       dim3 g2(b.num_seqs, a.hq);
       decode_combine_kernel<<<g2, kCombineThreads, 0, st>>>(b);
@@ -979,6 +1073,69 @@ extern "C" kv_status paged_attn_decode(
   a.scale_log2 = scale * kLog2e;
   return run_decode("paged_attn_decode", true, a, dtype, workspace,
                     workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" kv_status paged_attn_decode_fp8(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+    const int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, float k_scale, float v_scale,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* name = "paged_attn_decode_fp8";
+  if (!(k_scale > 0.f) || !(k_scale < INFINITY) || !(v_scale > 0.f) ||
+      !(v_scale < INFINITY))
+    return kvp_fail(KV_EINVAL, "%s: k_scale and v_scale must be finite and "
+                    "> 0", name);
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.ctx = context_lens;
+  a.max_ctx = max_context;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale_log2 = scale * k_scale * kLog2e;
+  a.v_scale = v_scale;
+  return run_decode(name, true, a, KV_BF16, workspace, workspace_bytes,
+                    (hipStream_t)stream, true);
+}
+
+extern "C" kv_status contig_attn_decode_fp8(
+    void* out, const void* q, const void* k, const void* v, int32_t seq_stride,
+    const int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+    float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  const char* name = "contig_attn_decode_fp8";
+  if (!(k_scale > 0.f) || !(k_scale < INFINITY) || !(v_scale > 0.f) ||
+      !(v_scale < INFINITY))
+    return kvp_fail(KV_EINVAL, "%s: k_scale and v_scale must be finite and "
+                    "> 0", name);
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seq_stride = seq_stride;
+  a.block_size = 16;
+  a.ctx = context_lens;
+  a.max_ctx = max_context;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale_log2 = scale * k_scale * kLog2e;
+  a.v_scale = v_scale;
+  return run_decode(name, false, a, KV_BF16, workspace, workspace_bytes,
+                    (hipStream_t)stream, true);
 }
 
 extern "C" kv_status contig_attn_decode(

@@ -62,6 +62,14 @@ SIGNATURES = {
                               _I32, _P]),
     "kv_swap_blocks": (_I32, [_P, _P, _I32, _P, _P, _I32, _P, _I32, _I32,
                               _I32, _I32, _I32, _P]),
+    "kv_reshape_and_cache_fp8": (_I32, [_P, _P, _P, _I32, _P, _P, _I64, _I32,
+                                        _I32, _I32, _F, _F, _P]),
+    "paged_attn_decode_fp8": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
+                                     _I32, _I32, _I32, _I32, _I32, _F, _F, _F,
+                                     _P, _SZ, _P]),
+    "contig_attn_decode_fp8": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                      _I32, _I32, _I32, _F, _F, _F, _P, _SZ,
+                                      _P]),
     "kv_decode_chunks": (_I32, [_I32, _I32]),
     "kv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "paged_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
@@ -397,6 +405,32 @@ def kv_reshape_and_cache(k, v, slots, k_cache, v_cache, stream=None) -> None:
     _check(st, "kv_reshape_and_cache")
 
 
+def _fp8_cache(t, name):
+    """Device pointer of an fp8 E4M3 cache (torch.uint8 codes or
+    torch.float8_e4m3fn)."""
+    torch = _torch()
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must be uint8 or float8_e4m3fn, got {t.dtype}")
+    return _dev(t, name)
+
+
+def kv_reshape_and_cache_fp8(k, v, slots, k_cache, v_cache, k_scale: float,
+                             v_scale: float, stream=None) -> None:
+    """bf16 rows k, v [T, Hkv, D] -> fp8 E4M3 codes in the caches (layout
+    as kv_reshape_and_cache): code = E4M3(x * fl32(1 / scale))."""
+    torch = _torch()
+    n, hkv, d = k.shape
+    nb, chkv, bs, cd = k_cache.shape
+    if (chkv, cd) != (hkv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches and rows disagree on shape")
+    st = lib().kv_reshape_and_cache_fp8(
+        _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+        _dev(slots, "slots", torch.int64), n, _fp8_cache(k_cache, "k_cache"),
+        _fp8_cache(v_cache, "v_cache"), nb * bs, bs, hkv, d, float(k_scale),
+        float(v_scale), _stream(stream))
+    _check(st, "kv_reshape_and_cache_fp8")
+
+
 def kv_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
     torch = _torch()
     nb, hkv, bs, d = k_cache.shape
@@ -467,6 +501,45 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         int(max_context), S, hq, hkv, d, bs, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "paged_attn_decode")
+
+
+def paged_attn_decode_fp8(out, q, k_cache, v_cache, block_tables,
+                          context_lens, max_context: int, scale: float,
+                          k_scale: float, v_scale: float, workspace=None,
+                          stream=None) -> None:
+    """paged_attn_decode over fp8 E4M3 caches; q, out bf16."""
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    if workspace is None:
+        workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
+    st = lib().paged_attn_decode_fp8(
+        _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+        _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"), nb,
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context), S, hq, hkv, d, bs, float(scale), float(k_scale),
+        float(v_scale), _dev(workspace, "workspace"), workspace.numel(),
+        _stream(stream))
+    _check(st, "paged_attn_decode_fp8")
+
+
+def contig_attn_decode_fp8(out, q, k, v, context_lens, max_context: int,
+                           scale: float, k_scale: float, v_scale: float,
+                           workspace=None, stream=None) -> None:
+    """contig_attn_decode over fp8 E4M3 caches [S, Hkv, Lmax, D]."""
+    torch = _torch()
+    S, hq, d = q.shape
+    _, hkv, lmax, _ = k.shape
+    if workspace is None:
+        workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
+    st = lib().contig_attn_decode_fp8(
+        _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+        _fp8_cache(k, "k"), _fp8_cache(v, "v"), lmax,
+        _dev(context_lens, "context_lens", torch.int32), int(max_context), S,
+        hq, hkv, d, float(scale), float(k_scale), float(v_scale),
+        _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "contig_attn_decode_fp8")
 
 
 def kv_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads,
