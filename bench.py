@@ -2,10 +2,16 @@
 
 A step is one decode step of a batch of sequences, each growing by one token:
   host   kv_seq_append: allocation when a block fills (copy-on-write of a
-         shared, partly filled block), slot mapping;
-  upload one pinned host->device copy of slots, lengths and block table;
-  device kv_reshape_and_cache of the new token's K/V, paged_attn_decode
-         (stream-K partitions + exact merge).
+         shared, partly filled block), slot mapping; the block ids it took
+         go to a pinned int32 [S] buffer;
+  device kv_append_token (the new block ids read from that pinned buffer
+         into the device block table, slot, cache write of the new token's
+         K/V, length + 1; the table and lengths stay on the device),
+         paged_attn_decode (stream-K partitions + exact merge).
+The contiguous layouts take the same kernel with one "block" per sequence.
+The fp8 decode keeps the earlier form (one pinned upload of slots, lengths
+and table, then kv_reshape_and_cache_fp8), since the append kernel writes
+bf16/fp32 rows.
 Four independent replicas of the whole batch (pools, tables, queries) rotate
 so that no step finds its K/V in the 256 MB last-level cache.
 
@@ -63,6 +69,10 @@ METRIC = ("decode KV-read HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA "
 DECODE_WORKLOADS = ("llama3_8b_decode", "yi34b_long_decode",
                     "prefix_share_decode")
 COW_PREFIX = 4104
+# appends timed on their own after the timed decode steps
+APPEND_TIMING_STEPS = 8
+# GPU spin before each of them (about 40 us at 2.4 GHz)
+SPIN_CYCLES = 100_000
 
 
 def log(msg: str) -> None:
@@ -137,6 +147,13 @@ def pool_blocks(kv, w, lengths, headroom: int = 0) -> int:
                   for n in lengths)
         return kv.kv_blocks_needed(P, B) + own + headroom
     return sum(kv.kv_blocks_needed(int(n), B) for n in lengths) + headroom
+
+
+def rounded(d: dict) -> dict:
+    """Numbers to 4 decimals; other values (names, nested dicts) as they
+    are."""
+    return {k: round(v, 4) if isinstance(v, float) else v
+            for k, v in d.items()}
 
 
 def stats_ms(ms) -> dict:
@@ -275,7 +292,21 @@ class DecodeReplica:
         else:
             self.ws = kv.decode_workspace(S, w.num_q_heads, w.num_kv_heads,
                                           w.head_dim, self.lmax, device)
-        # the staging buffer is rewritten only after its last upload is done
+        # Device-resident table and lengths for kv_append_token (not for the
+        # fp8 path, which uploads them every step). Contiguous layouts: one
+        # block per sequence (table[s] = [s], block_size = Lmax).
+        self.append_path = not self.fp8
+        self.h_newb = torch.full((S,), -1, dtype=torch.int32,
+                                 pin_memory=True)
+        if self.append_path:
+            self.d_buf.copy_(self.h_buf)
+            if paged:
+                self.a_table = self.d_table
+            else:
+                self.a_table = torch.arange(S, dtype=torch.int32,
+                                            device=device).view(S, 1)
+        # the pinned buffers are rewritten only after the last GPU work that
+        # read them is done
         self.uploaded = torch.cuda.Event()
         self.uploaded.record()
         self.scale = 1.0 / float(np.sqrt(w.head_dim))
@@ -286,9 +317,15 @@ class DecodeReplica:
         contiguous slot s * Lmax + position."""
         self.uploaded.synchronize()
         if self.paged:
+            S = self.w.num_seqs
+            ar = np.arange(S)
+            idx = self.h_lens // self.w.block_size
+            before = self.h_table[ar, idx]
             slots, pairs = self.pool.seq_append(self.h_table, self.h_lens)
             assert len(pairs) == 0
             self.h_slots[:] = slots
+            after = self.h_table[ar, idx]
+            self.h_newb.numpy()[:] = np.where(after != before, after, -1)
         else:
             S = self.w.num_seqs
             self.h_slots[:] = np.arange(S, dtype=np.int64) * self.lmax + \
@@ -308,21 +345,26 @@ class DecodeReplica:
         if self.vmm:
             self.vc.close()
 
-    def device_step(self, ev=None) -> None:
+    def cache_write(self) -> None:
+        """Device part of the append: the new token's row in the cache (and,
+        on the append path, the table entry and length on the device)."""
         kv = self.kv
-        self.d_buf.copy_(self.h_buf, non_blocking=True)
-        self.uploaded.record()
-        if ev is not None:
-            ev[0].record()
-        if self.fp8:
+        if self.append_path:
+            kv.kv_append_token(self.new_k, self.new_v, self.h_newb,
+                               self.a_table, self.d_lens, self.k, self.v)
+        else:
+            self.d_buf.copy_(self.h_buf, non_blocking=True)
             kv.kv_reshape_and_cache_fp8(self.new_k, self.new_v, self.d_slots,
                                         self.k, self.v, FP8_SCALE, FP8_SCALE)
-        else:
-            kv.kv_reshape_and_cache(self.new_k, self.new_v, self.d_slots,
-                                    self.k, self.v)
+        self.uploaded.record()
+
+    def device_step(self, ev=None) -> None:
+        """Cache write, then the decode op, bracketed by ev[0], ev[1]."""
+        kv = self.kv
+        self.cache_write()
         max_ctx = int(self.h_lens.max())
         if ev is not None:
-            ev[1].record()
+            ev[0].record()
         if self.fp8:
             kv.paged_attn_decode_fp8(self.out, self.q, self.k, self.v,
                                      self.d_table, self.d_lens, max_ctx,
@@ -341,7 +383,7 @@ class DecodeReplica:
             kv.contig_attn_decode(self.out, self.q, self.k, self.v,
                                   self.d_lens, max_ctx, self.scale, self.ws)
         if ev is not None:
-            ev[2].record()
+            ev[1].record()
 
 
 def new_token_kv(w, device):
@@ -362,7 +404,8 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     new_k, new_v = new_token_kv(w, device)
     k_dev, v_dev = inp.k.to(device), inp.v.to(device)
     reps_ = [DecodeReplica(inp, k_dev, v_dev, new_k, new_v, paged,
-                           steps + warmup, device, shared_op,
+                           steps + warmup + APPEND_TIMING_STEPS, device,
+                           shared_op,
                            vmm_page_tokens, fp8)
              for _ in range(reps)]
     del k_dev, v_dev
@@ -371,7 +414,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         r.host_append()
         r.device_step()
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
            for _ in range(steps)]
     total_bytes = logical_bytes = 0
     t0 = time.perf_counter()
@@ -386,8 +429,23 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         r.device_step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    op = stats_ms([b.elapsed_time(c) for _, b, c in evs])
-    rc = stats_ms([a.elapsed_time(b) for a, b, _ in evs])
+    op = stats_ms([a.elapsed_time(b) for a, b in evs])
+    # The cache write alone (append kernel, or upload + fp8 cache write),
+    # timed after the timed steps so that its events stay out of them. A
+    # short spin kernel keeps the GPU busy while the host queues the events
+    # and the write, so the interval is GPU time, not launch latency.
+    rc_ev = []
+    for i in range(APPEND_TIMING_STEPS):
+        r = reps_[i % reps]
+        r.host_append()
+        e = tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+        torch.cuda._sleep(SPIN_CYCLES)
+        e[0].record()
+        r.cache_write()
+        e[1].record()
+        rc_ev.append(e)
+    torch.cuda.synchronize()
+    rc = stats_ms([a.elapsed_time(b) for a, b in rc_ev])
     res = {
         "wall_s": wall,
         "ms_per_step": 1e3 * wall / steps,
@@ -397,7 +455,9 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         "decode_op_ms_p10": op["p10"],
         "decode_op_ms_p90": op["p90"],
         "bytes_per_step": total_bytes / steps,
-        "reshape_and_cache_us_median": 1e3 * rc["median"],
+        "cache_write": "kv_append_token" if not fp8 else
+                       "upload + kv_reshape_and_cache_fp8",
+        "cache_write_us_median": 1e3 * rc["median"],
     }
     res["decode_op_GBps"] = res["bytes_per_step"] / (op["mean"] * 1e-3) / 1e9
     if logical_bytes != total_bytes:
@@ -407,7 +467,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     # the new rows: K and V, read once (bf16) and written once
     tok_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * (
         2 + (1 if fp8 else 2))
-    res["reshape_and_cache_GBps"] = tok_bytes / (rc["median"] * 1e-3) / 1e9
+    res["cache_write_GBps"] = tok_bytes / (rc["median"] * 1e-3) / 1e9
     if vmm_page_tokens and not paged:
         P = vmm_page_tokens
         r0 = reps_[0]
@@ -834,7 +894,8 @@ def main() -> int:
 
     wd = W.WORKLOADS[args.workload]
     default_workload = args.workload == "llama3_8b_decode"
-    headroom = wd.num_seqs * (-(-(args.steps + args.warmup) // wd.block_size)
+    headroom = wd.num_seqs * (-(-(args.steps + args.warmup +
+                                  APPEND_TIMING_STEPS) // wd.block_size)
                               + 1)
     paged = contig = inp = cow = plain = vattn = swap = fp8 = None
     if not args.no_decode:
@@ -935,7 +996,7 @@ def main() -> int:
             "num_seqs": wd.num_seqs, "num_q_heads": wd.num_q_heads,
             "num_kv_heads": wd.num_kv_heads, "head_dim": wd.head_dim,
             "block_size": wd.block_size, "context": ctx_desc[wd.name],
-            "step": "append+upload+reshape_and_cache+" + (
+            "step": "append+kv_append_token+" + (
                 "paged_attn_decode_shared_prefix" if plain else
                 "paged_attn_decode"),
             "replicas": args.replicas,
@@ -952,35 +1013,34 @@ def main() -> int:
             "bytes_per_launch": int(paged["bytes_per_step"]),
             "ms_per_launch": round(paged["decode_op_ms_mean"], 4),
         },
-        "decode_paged": {k: round(v, 4) for k, v in paged.items()},
+        "decode_paged": rounded(paged),
         "memory": memory_waste(inp, lmax_reserved),
     }
     if plain:
-        line["decode_paged_without_sharing"] = {k: round(v, 4)
-                                                for k, v in plain.items()}
+        line["decode_paged_without_sharing"] = rounded(plain)
     if contig:
-        line["decode_contig"] = {k: round(v, 4) for k, v in contig.items()}
+        line["decode_contig"] = rounded(contig)
         line["decode_paged_vs_contig_overhead"] = round(
             paged["decode_op_ms_mean"] / contig["decode_op_ms_mean"] - 1.0, 4)
     if vattn and "error" in vattn:
         line["decode_contig_demand_mapped"] = vattn
     elif vattn:
         line["decode_contig_demand_mapped"] = {
-            k: ({kk: round(vv, 4) for kk, vv in v.items()}
-                if isinstance(v, dict) else round(v, 4))
+            k: (rounded(v) if isinstance(v, dict) else
+                round(v, 4) if isinstance(v, float) else v)
             for k, v in vattn.items()}
         line["decode_paged_vs_demand_mapped_overhead"] = round(
             paged["decode_op_ms_mean"] / vattn["decode_op_ms_mean"] - 1.0, 4)
     if fp8:
-        line["decode_paged_fp8"] = {k: round(v, 4) for k, v in fp8.items()}
+        line["decode_paged_fp8"] = rounded(fp8)
         line["decode_paged_fp8"]["frac_of_hbm_peak"] = round(
             fp8["decode_op_GBps"] / HBM_PEAK_GBPS, 4)
         line["decode_fp8_speedup_vs_bf16"] = round(
             paged["decode_op_ms_mean"] / fp8["decode_op_ms_mean"], 4)
     if cow:
-        line["copy_on_write"] = {k: round(v, 4) for k, v in cow.items()}
+        line["copy_on_write"] = rounded(cow)
     if swap:
-        line["block_swap"] = {k: round(v, 4) for k, v in swap.items()}
+        line["block_swap"] = rounded(swap)
     if prefill:
         line["prefill"] = {k: {kk: round(vv, 4) for kk, vv in v.items()}
                            for k, v in prefill.items()}

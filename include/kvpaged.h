@@ -158,6 +158,39 @@ kv_status kv_reshape_and_cache(const void* k, const void* v,
                                int32_t block_size, int32_t num_kv_heads,
                                int32_t head_dim, kv_dtype dtype, void* stream);
 
+/* Device side of one decode append for a batch, one new token per
+ * sequence, with the block table and the lengths kept in device memory
+ * ["PagedAttention Nedir?" (bitcanli.com), "PagedAttention Nasıl
+ * Çalışır?", steps 2-3: the new token goes into the slot its table assigns,
+ * a block taken from the pool when the last one is full]. For each
+ * sequence s, with L = context_lens[s]:
+ *   1. if new_blocks[s] >= 0, it is stored as block_tables[s][L / B] (the
+ *      block the host allocator took for that logical block: a fresh block
+ *      when L % B == 0, or the copy-on-write target, whose copy must
+ *      already be enqueued on the stream);
+ *   2. k[s, h, :] and v[s, h, :] go to slot
+ *      block_tables[s][L / B] * B + L % B, laid out as kv_reshape_and_cache
+ *      writes it;
+ *   3. context_lens[s] becomes L + 1.
+ * k, v: [num_seqs, Hkv, D] device rows. block_tables (int32 [num_seqs,
+ * bt_stride]) and context_lens (int32 [num_seqs]) are device memory and are
+ * updated in place. new_blocks: int32 [num_seqs], -1 = keep the entry;
+ * device memory or pinned host memory (hipHostMalloc, torch's pin_memory),
+ * which the kernel reads directly, so that a step uploads nothing; other
+ * host memory -> KV_EINVAL. A sequence with L outside [0, bt_stride * B),
+ * or whose block is outside [0, num_blocks), is left unchanged. The
+ * contiguous layout is the case block_size = seq_stride with
+ * block_tables[s][0] = s. The result equals kv_seq_append's table and slots
+ * followed by kv_reshape_and_cache. Enqueued on `stream`; allocates
+ * nothing. */
+kv_status kv_append_token(const void* k, const void* v,
+                          const int32_t* new_blocks, int32_t* block_tables,
+                          int32_t bt_stride, int32_t* context_lens,
+                          int32_t num_seqs, void* k_cache, void* v_cache,
+                          int32_t num_blocks, int32_t block_size,
+                          int32_t num_kv_heads, int32_t head_dim,
+                          kv_dtype dtype, void* stream);
+
 /* Copy-on-write data move: for i < n, block src_dst[2i] -> src_dst[2i+1]
  * of both caches (device int32 pairs). The pairs must be independent: no
  * destination may be another pair's source or destination (the pairs

@@ -69,6 +69,46 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   }
 }
 
+// One workgroup per sequence: the table entry of the new token's logical
+// block (patched first when the host took a new block), its slot, the K and
+// V rows of every head in U-sized units, then the length. Only this
+// workgroup touches row s of the table and context_lens[s].
+template <typename U>
+__global__ __launch_bounds__(256) void append_token_kernel(
+    const U* __restrict__ k, const U* __restrict__ v,
+    const int32_t* new_blocks, int32_t* bt, int32_t bt_stride, int32_t* ctx,
+    U* k_cache, U* v_cache, int32_t num_blocks, int32_t block_size,
+    int32_t num_kv_heads, int32_t units_per_head) {
+  const int s = blockIdx.x;
+  const int L = ctx[s];
+  const int nb = new_blocks[s];
+  const bool ok_pos = L >= 0 && (int64_t)L < (int64_t)bt_stride * block_size;
+  const int idx = ok_pos ? L / block_size : 0;
+  int32_t* entry = bt + (int64_t)s * bt_stride + idx;
+  const int blk = nb >= 0 ? nb : (ok_pos ? *entry : -1);
+  const bool ok = ok_pos && blk >= 0 && blk < num_blocks;
+  if (ok) {
+    const int64_t off = L - (int64_t)idx * block_size;
+    const int64_t per_tensor = (int64_t)num_kv_heads * units_per_head;
+    for (int64_t i = threadIdx.x; i < 2 * per_tensor; i += blockDim.x) {
+      const bool is_v = i >= per_tensor;
+      const int64_t r = is_v ? i - per_tensor : i;
+      const int64_t h = r / units_per_head;
+      const int64_t u = r - h * units_per_head;
+      const U* src = is_v ? v : k;
+      U* dst = is_v ? v_cache : k_cache;
+      dst[(((int64_t)blk * num_kv_heads + h) * block_size + off) *
+              units_per_head + u] = src[(int64_t)s * per_tensor + r];
+    }
+  }
+  // every thread has read ctx[s] and the table entry before they change
+  __syncthreads();
+  if (ok && threadIdx.x == 0) {
+    if (nb >= 0) *entry = nb;
+    ctx[s] = L + 1;
+  }
+}
+
 size_t elem_size(kv_dtype dt) { return dt == KV_F32 ? 4 : 2; }
 
 // bf16 -> fp8 E4M3 code of x * inv: fp32 product, clamped to the format's
@@ -333,5 +373,54 @@ extern "C" kv_status kv_swap_blocks(const void* src_k, const void* src_v,
   else if (block_bytes % 4 == 0) go(uint32_t{});
   else go(uint16_t{});
   KVP_LAUNCH_CHECK("kv_swap_blocks");
+  return KV_OK;
+}
+
+extern "C" kv_status kv_append_token(const void* k, const void* v,
+                                     const int32_t* new_blocks,
+                                     int32_t* block_tables, int32_t bt_stride,
+                                     int32_t* context_lens, int32_t num_seqs,
+                                     void* k_cache, void* v_cache,
+                                     int32_t num_blocks, int32_t block_size,
+                                     int32_t num_kv_heads, int32_t head_dim,
+                                     kv_dtype dtype, void* stream) {
+  const char* name = "kv_append_token";
+  if (dtype != KV_F32 && dtype != KV_BF16)
+    return kvp_fail(KV_EINVAL, "%s: unknown dtype %d", name, (int)dtype);
+  if (num_seqs < 0 || bt_stride <= 0 || num_blocks <= 0 || block_size <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0)
+    return kvp_fail(KV_EINVAL, "%s: bad shape (S=%d stride=%d N=%d B=%d "
+                    "Hkv=%d D=%d)", name, num_seqs, bt_stride, num_blocks,
+                    block_size, num_kv_heads, head_dim);
+  if (num_seqs == 0) return KV_OK;
+  if (!k || !v || !new_blocks || !block_tables || !context_lens || !k_cache ||
+      !v_cache)
+    return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
+  const int32_t* nb = (const int32_t*)device_view(new_blocks);
+  if (!nb)
+    return kvp_fail(KV_EINVAL, "%s: new_blocks is not device or pinned host "
+                    "memory", name);
+  const int64_t head_bytes = (int64_t)head_dim * elem_size(dtype);
+  // the widest unit that divides a head row and every row address
+  const uintptr_t align = (uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache |
+                          (uintptr_t)v_cache | (uintptr_t)head_bytes;
+  hipStream_t st = (hipStream_t)stream;
+  const int threads = 256;
+  if (align % 16 == 0)
+    append_token_kernel<u32x4><<<num_seqs, threads, 0, st>>>(
+        (const u32x4*)k, (const u32x4*)v, nb, block_tables, bt_stride,
+        context_lens, (u32x4*)k_cache, (u32x4*)v_cache, num_blocks,
+        block_size, num_kv_heads, (int32_t)(head_bytes / 16));
+  else if (align % 4 == 0)
+    append_token_kernel<uint32_t><<<num_seqs, threads, 0, st>>>(
+        (const uint32_t*)k, (const uint32_t*)v, nb, block_tables, bt_stride,
+        context_lens, (uint32_t*)k_cache, (uint32_t*)v_cache, num_blocks,
+        block_size, num_kv_heads, (int32_t)(head_bytes / 4));
+  else
+    append_token_kernel<uint16_t><<<num_seqs, threads, 0, st>>>(
+        (const uint16_t*)k, (const uint16_t*)v, nb, block_tables, bt_stride,
+        context_lens, (uint16_t*)k_cache, (uint16_t*)v_cache, num_blocks,
+        block_size, num_kv_heads, (int32_t)(head_bytes / 2));
+  KVP_LAUNCH_CHECK(name);
   return KV_OK;
 }

@@ -60,6 +60,8 @@ SIGNATURES = {
                                     _I32, _I32, _I32, _P]),
     "kv_copy_blocks": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                               _I32, _P]),
+    "kv_append_token": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P,
+                                _I32, _I32, _I32, _I32, _I32, _P]),
     "kv_swap_blocks": (_I32, [_P, _P, _I32, _P, _P, _I32, _P, _I32, _I32,
                               _I32, _I32, _I32, _P]),
     "kv_reshape_and_cache_fp8": (_I32, [_P, _P, _P, _I32, _P, _P, _I64, _I32,
@@ -439,6 +441,35 @@ def kv_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
         _dev(src_dst, "src_dst", torch.int32), src_dst.shape[0], nb, bs, hkv,
         d, _dtype_code(k_cache), _stream(stream))
     _check(st, "kv_copy_blocks")
+
+
+def kv_append_token(k, v, new_blocks, block_tables, context_lens, k_cache,
+                    v_cache, stream=None) -> None:
+    """One decode token per sequence, table and lengths on the device:
+    k, v [S, Hkv, D]; new_blocks int32 [S] (device or pinned host, -1 = keep
+    the entry) is installed at block_tables[s][L / B] first; the rows go to
+    slot block_tables[s][L / B] * B + L % B; context_lens[s] += 1. Caches
+    [blocks, Hkv, block_size, D]."""
+    torch = _torch()
+    S, hkv, d = k.shape
+    nb, chkv, bs, cd = k_cache.shape
+    if (chkv, cd) != (hkv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches and rows disagree on shape")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v differ in shape")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S or \
+            new_blocks.shape[0] != S:
+        raise ValueError("block_tables, context_lens and new_blocks need one "
+                         "row per sequence")
+    if not new_blocks.is_contiguous() or new_blocks.dtype != torch.int32:
+        raise ValueError("new_blocks must be a contiguous int32 tensor")
+    st = lib().kv_append_token(
+        _dev(k, "k"), _dev(v, "v", k.dtype), new_blocks.data_ptr(),
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        S, _dev(k_cache, "k_cache", k.dtype), _dev(v_cache, "v_cache", k.dtype),
+        nb, bs, hkv, d, _dtype_code(k), _stream(stream))
+    _check(st, "kv_append_token")
 
 
 def kv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:
