@@ -8,10 +8,8 @@ A step is one decode step of a batch of sequences, each growing by one token:
          into the device block table, slot, cache write of the new token's
          K/V, length + 1; the table and lengths stay on the device),
          paged_attn_decode (stream-K partitions + exact merge).
-The contiguous layouts take the same kernel with one "block" per sequence.
-The fp8 decode keeps the earlier form (one pinned upload of slots, lengths
-and table, then kv_reshape_and_cache_fp8), since the append kernel writes
-bf16/fp32 rows.
+The contiguous layouts take the same kernel with one "block" per sequence;
+the fp8 decode its fp8 form (kv_append_token_fp8).
 Four independent replicas of the whole batch (pools, tables, queries) rotate
 so that no step finds its K/V in the 256 MB last-level cache.
 
@@ -292,19 +290,17 @@ class DecodeReplica:
         else:
             self.ws = kv.decode_workspace(S, w.num_q_heads, w.num_kv_heads,
                                           w.head_dim, self.lmax, device)
-        # Device-resident table and lengths for kv_append_token (not for the
-        # fp8 path, which uploads them every step). Contiguous layouts: one
-        # block per sequence (table[s] = [s], block_size = Lmax).
-        self.append_path = not self.fp8
+        # Device-resident table and lengths for kv_append_token, uploaded
+        # once here. Contiguous layouts: one block per sequence
+        # (table[s] = [s], block_size = Lmax).
         self.h_newb = torch.full((S,), -1, dtype=torch.int32,
                                  pin_memory=True)
-        if self.append_path:
-            self.d_buf.copy_(self.h_buf)
-            if paged:
-                self.a_table = self.d_table
-            else:
-                self.a_table = torch.arange(S, dtype=torch.int32,
-                                            device=device).view(S, 1)
+        self.d_buf.copy_(self.h_buf)
+        if paged:
+            self.a_table = self.d_table
+        else:
+            self.a_table = torch.arange(S, dtype=torch.int32,
+                                        device=device).view(S, 1)
         # the pinned buffers are rewritten only after the last GPU work that
         # read them is done
         self.uploaded = torch.cuda.Event()
@@ -349,13 +345,13 @@ class DecodeReplica:
         """Device part of the append: the new token's row in the cache (and,
         on the append path, the table entry and length on the device)."""
         kv = self.kv
-        if self.append_path:
+        if self.fp8:
+            kv.kv_append_token_fp8(self.new_k, self.new_v, self.h_newb,
+                                   self.a_table, self.d_lens, self.k, self.v,
+                                   FP8_SCALE, FP8_SCALE)
+        else:
             kv.kv_append_token(self.new_k, self.new_v, self.h_newb,
                                self.a_table, self.d_lens, self.k, self.v)
-        else:
-            self.d_buf.copy_(self.h_buf, non_blocking=True)
-            kv.kv_reshape_and_cache_fp8(self.new_k, self.new_v, self.d_slots,
-                                        self.k, self.v, FP8_SCALE, FP8_SCALE)
         self.uploaded.record()
 
     def device_step(self, ev=None) -> None:
@@ -430,7 +426,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     op = stats_ms([a.elapsed_time(b) for a, b in evs])
-    # The cache write alone (append kernel, or upload + fp8 cache write),
+    # The cache write alone (the append kernel),
     # timed after the timed steps so that its events stay out of them. A
     # short spin kernel keeps the GPU busy while the host queues the events
     # and the write, so the interval is GPU time, not launch latency.
@@ -456,7 +452,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         "decode_op_ms_p90": op["p90"],
         "bytes_per_step": total_bytes / steps,
         "cache_write": "kv_append_token" if not fp8 else
-                       "upload + kv_reshape_and_cache_fp8",
+                       "kv_append_token_fp8",
         "cache_write_us_median": 1e3 * rc["median"],
     }
     res["decode_op_GBps"] = res["bytes_per_step"] / (op["mean"] * 1e-3) / 1e9

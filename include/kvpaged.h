@@ -353,6 +353,19 @@ kv_status kv_reshape_and_cache_fp8(const void* k, const void* v,
                                    int32_t num_kv_heads, int32_t head_dim,
                                    float k_scale, float v_scale, void* stream);
 
+/* kv_append_token for fp8 caches: k, v are bf16 rows [num_seqs, Hkv, D]
+ * (16-byte aligned), the caches hold codes (8-byte aligned), D % 8 == 0;
+ * each value is stored as in kv_reshape_and_cache_fp8. Table, lengths and
+ * new_blocks as in kv_append_token. */
+kv_status kv_append_token_fp8(const void* k, const void* v,
+                              const int32_t* new_blocks,
+                              int32_t* block_tables, int32_t bt_stride,
+                              int32_t* context_lens, int32_t num_seqs,
+                              void* k_cache, void* v_cache,
+                              int32_t num_blocks, int32_t block_size,
+                              int32_t num_kv_heads, int32_t head_dim,
+                              float k_scale, float v_scale, void* stream);
+
 /* paged_attn_decode / contig_attn_decode over fp8 caches: q and out are
  * bf16; attention is computed on the dequantised K (k_scale folded into the
  * softmax scale) and V (v_scale applied to the output). Workspace as for

@@ -71,14 +71,16 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 
 // One workgroup per sequence: the table entry of the new token's logical
 // block (patched first when the host took a new block), its slot, the K and
-// V rows of every head in U-sized units, then the length. Only this
-// workgroup touches row s of the table and context_lens[s].
-template <typename U>
+// V rows of every head in unit-sized pieces, then the length. Only this
+// workgroup touches row s of the table and context_lens[s]. Src/Dst: a unit
+// of the source row and of the cache (the same type, copied; or 8 bf16
+// values -> 8 fp8 E4M3 codes, quantised with 1 / scale by `Conv`).
+template <typename Src, typename Dst, typename Conv>
 __global__ __launch_bounds__(256) void append_token_kernel(
-    const U* __restrict__ k, const U* __restrict__ v,
+    const Src* __restrict__ k, const Src* __restrict__ v,
     const int32_t* new_blocks, int32_t* bt, int32_t bt_stride, int32_t* ctx,
-    U* k_cache, U* v_cache, int32_t num_blocks, int32_t block_size,
-    int32_t num_kv_heads, int32_t units_per_head) {
+    Dst* k_cache, Dst* v_cache, int32_t num_blocks, int32_t block_size,
+    int32_t num_kv_heads, int32_t units_per_head, Conv conv) {
   const int s = blockIdx.x;
   const int L = ctx[s];
   const int nb = new_blocks[s];
@@ -95,10 +97,10 @@ __global__ __launch_bounds__(256) void append_token_kernel(
       const int64_t r = is_v ? i - per_tensor : i;
       const int64_t h = r / units_per_head;
       const int64_t u = r - h * units_per_head;
-      const U* src = is_v ? v : k;
-      U* dst = is_v ? v_cache : k_cache;
+      const Src* src = is_v ? v : k;
+      Dst* dst = is_v ? v_cache : k_cache;
       dst[(((int64_t)blk * num_kv_heads + h) * block_size + off) *
-              units_per_head + u] = src[(int64_t)s * per_tensor + r];
+              units_per_head + u] = conv(src[(int64_t)s * per_tensor + r], is_v);
     }
   }
   // every thread has read ctx[s] and the table entry before they change
@@ -108,6 +110,11 @@ __global__ __launch_bounds__(256) void append_token_kernel(
     ctx[s] = L + 1;
   }
 }
+
+struct CopyUnit {
+  template <typename U>
+  __device__ U operator()(U x, bool) const { return x; }
+};
 
 size_t elem_size(kv_dtype dt) { return dt == KV_F32 ? 4 : 2; }
 
@@ -161,6 +168,18 @@ __global__ __launch_bounds__(256) void scatter_rows_fp8_kernel(
         c;
   }
 }
+
+// 8 bf16 values -> 8 E4M3 codes, K or V scale
+struct Fp8Unit {
+  float k_inv, v_inv;
+  __device__ u32x2 operator()(u32x4 x, bool is_v) const {
+    const float inv = is_v ? v_inv : k_inv;
+    u32x2 c;
+    c[0] = fp8_pack4(x[0], x[1], inv);
+    c[1] = fp8_pack4(x[2], x[3], inv);
+    return c;
+  }
+};
 
 }  // namespace
 
@@ -407,20 +426,56 @@ extern "C" kv_status kv_append_token(const void* k, const void* v,
   hipStream_t st = (hipStream_t)stream;
   const int threads = 256;
   if (align % 16 == 0)
-    append_token_kernel<u32x4><<<num_seqs, threads, 0, st>>>(
+    append_token_kernel<<<num_seqs, threads, 0, st>>>(
         (const u32x4*)k, (const u32x4*)v, nb, block_tables, bt_stride,
         context_lens, (u32x4*)k_cache, (u32x4*)v_cache, num_blocks,
-        block_size, num_kv_heads, (int32_t)(head_bytes / 16));
+        block_size, num_kv_heads, (int32_t)(head_bytes / 16), CopyUnit{});
   else if (align % 4 == 0)
-    append_token_kernel<uint32_t><<<num_seqs, threads, 0, st>>>(
+    append_token_kernel<<<num_seqs, threads, 0, st>>>(
         (const uint32_t*)k, (const uint32_t*)v, nb, block_tables, bt_stride,
         context_lens, (uint32_t*)k_cache, (uint32_t*)v_cache, num_blocks,
-        block_size, num_kv_heads, (int32_t)(head_bytes / 4));
+        block_size, num_kv_heads, (int32_t)(head_bytes / 4), CopyUnit{});
   else
-    append_token_kernel<uint16_t><<<num_seqs, threads, 0, st>>>(
+    append_token_kernel<<<num_seqs, threads, 0, st>>>(
         (const uint16_t*)k, (const uint16_t*)v, nb, block_tables, bt_stride,
         context_lens, (uint16_t*)k_cache, (uint16_t*)v_cache, num_blocks,
-        block_size, num_kv_heads, (int32_t)(head_bytes / 2));
+        block_size, num_kv_heads, (int32_t)(head_bytes / 2), CopyUnit{});
+  KVP_LAUNCH_CHECK(name);
+  return KV_OK;
+}
+
+extern "C" kv_status kv_append_token_fp8(
+    const void* k, const void* v, const int32_t* new_blocks,
+    int32_t* block_tables, int32_t bt_stride, int32_t* context_lens,
+    int32_t num_seqs, void* k_cache, void* v_cache, int32_t num_blocks,
+    int32_t block_size, int32_t num_kv_heads, int32_t head_dim, float k_scale,
+    float v_scale, void* stream) {
+  const char* name = "kv_append_token_fp8";
+  if (num_seqs < 0 || bt_stride <= 0 || num_blocks <= 0 || block_size <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || head_dim % 8 != 0)
+    return kvp_fail(KV_EINVAL, "%s: bad shape (S=%d stride=%d N=%d B=%d "
+                    "Hkv=%d D=%d; D must be a multiple of 8)", name, num_seqs,
+                    bt_stride, num_blocks, block_size, num_kv_heads, head_dim);
+  if (!(k_scale > 0.f) || !(k_scale < INFINITY) || !(v_scale > 0.f) ||
+      !(v_scale < INFINITY))
+    return kvp_fail(KV_EINVAL, "%s: k_scale and v_scale must be finite and "
+                    "> 0", name);
+  if (num_seqs == 0) return KV_OK;
+  if (!k || !v || !new_blocks || !block_tables || !context_lens || !k_cache ||
+      !v_cache)
+    return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
+  if (((uintptr_t)k | (uintptr_t)v) % 16 ||
+      ((uintptr_t)k_cache | (uintptr_t)v_cache) % 8)
+    return kvp_fail(KV_EINVAL, "%s: k/v must be 16-byte and the caches "
+                    "8-byte aligned", name);
+  const int32_t* nb = (const int32_t*)device_view(new_blocks);
+  if (!nb)
+    return kvp_fail(KV_EINVAL, "%s: new_blocks is not device or pinned host "
+                    "memory", name);
+  append_token_kernel<<<num_seqs, 256, 0, (hipStream_t)stream>>>(
+      (const u32x4*)k, (const u32x4*)v, nb, block_tables, bt_stride,
+      context_lens, (u32x2*)k_cache, (u32x2*)v_cache, num_blocks, block_size,
+      num_kv_heads, head_dim / 8, Fp8Unit{1.f / k_scale, 1.f / v_scale});
   KVP_LAUNCH_CHECK(name);
   return KV_OK;
 }

@@ -62,6 +62,8 @@ SIGNATURES = {
                               _I32, _P]),
     "kv_append_token": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P,
                                 _I32, _I32, _I32, _I32, _I32, _P]),
+    "kv_append_token_fp8": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _P,
+                                    _I32, _I32, _I32, _I32, _F, _F, _P]),
     "kv_swap_blocks": (_I32, [_P, _P, _I32, _P, _P, _I32, _P, _I32, _I32,
                               _I32, _I32, _I32, _P]),
     "kv_reshape_and_cache_fp8": (_I32, [_P, _P, _P, _I32, _P, _P, _I64, _I32,
@@ -470,6 +472,33 @@ def kv_append_token(k, v, new_blocks, block_tables, context_lens, k_cache,
         S, _dev(k_cache, "k_cache", k.dtype), _dev(v_cache, "v_cache", k.dtype),
         nb, bs, hkv, d, _dtype_code(k), _stream(stream))
     _check(st, "kv_append_token")
+
+
+def kv_append_token_fp8(k, v, new_blocks, block_tables, context_lens,
+                        k_cache, v_cache, k_scale: float, v_scale: float,
+                        stream=None) -> None:
+    """kv_append_token into fp8 E4M3 caches: bf16 rows k, v [S, Hkv, D]
+    stored as E4M3(x * fl32(1 / scale))."""
+    torch = _torch()
+    S, hkv, d = k.shape
+    nb, chkv, bs, cd = k_cache.shape
+    if (chkv, cd) != (hkv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches and rows disagree on shape")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v differ in shape")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S or \
+            new_blocks.shape[0] != S:
+        raise ValueError("block_tables, context_lens and new_blocks need one "
+                         "row per sequence")
+    if not new_blocks.is_contiguous() or new_blocks.dtype != torch.int32:
+        raise ValueError("new_blocks must be a contiguous int32 tensor")
+    st = lib().kv_append_token_fp8(
+        _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+        new_blocks.data_ptr(), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        S, _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"), nb,
+        bs, hkv, d, float(k_scale), float(v_scale), _stream(stream))
+    _check(st, "kv_append_token_fp8")
 
 
 def kv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:

@@ -201,3 +201,56 @@ def test_append_errors():
                            kc.clone())
     torch.cuda.synchronize()
     assert lens.cpu().tolist() == [0, 0]
+
+
+def test_append_fp8_matches_cache_write_and_codec():
+    # 12 steps of 8 sequences into fp8 caches: kv_append_token_fp8 against
+    # the host slots + kv_reshape_and_cache_fp8, bit for bit, and the codes
+    # against the oracle's codec.
+    from oracle import fp8 as F
+    S, hkv, B, D = 8, 2, 16, 128
+    g = np.random.default_rng(14)
+    lens = g.integers(0, 60, size=S).astype(np.int32)
+    cap = 8
+    n_pool = S * cap
+    pool = kv.KVPool(n_pool, B, g.permutation(n_pool).astype(np.int32))
+    tables = np.full((S, cap), -1, dtype=np.int32)
+    host_lens = np.zeros(S, dtype=np.int32)
+    pool.seq_append(tables, host_lens, lens)          # contexts so far
+    caches = [torch.zeros((n_pool, hkv, B, D), dtype=torch.uint8,
+                          device="cuda") for _ in range(4)]
+    bt_dev = torch.from_numpy(tables.copy()).cuda()
+    lens_dev = torch.from_numpy(host_lens.copy()).cuda()
+    ks, vs = 0.0123, 0.031
+    keep = []
+    written = []
+    for step in range(12):
+        ar = np.arange(S)
+        idx = host_lens // B
+        before = tables[ar, idx].copy()
+        slots, pairs = pool.seq_append(tables, host_lens)
+        assert len(pairs) == 0
+        after = tables[ar, idx]
+        nb = torch.from_numpy(np.where(after != before, after, -1).astype(
+            np.int32)).pin_memory()
+        keep.append(nb)
+        k = (torch.from_numpy(g.standard_normal((S, hkv, D), dtype=np.float32))
+             * 3).to(torch.bfloat16).cuda()
+        v = (torch.from_numpy(g.standard_normal((S, hkv, D), dtype=np.float32))
+             * 3).to(torch.bfloat16).cuda()
+        kv.kv_append_token_fp8(k, v, nb, bt_dev, lens_dev, caches[0],
+                               caches[1], ks, vs)
+        kv.kv_reshape_and_cache_fp8(k, v, torch.from_numpy(slots).cuda(),
+                                    caches[2], caches[3], ks, vs)
+        written.append((slots.copy(), k.cpu(), v.cpu()))
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0], caches[2])
+    assert torch.equal(caches[1], caches[3])
+    assert np.array_equal(bt_dev.cpu().numpy(), tables)
+    assert np.array_equal(lens_dev.cpu().numpy(), host_lens)
+    kc = caches[0].cpu().numpy()
+    for slots, k, v in written[:3]:
+        for s in range(S):
+            blk, off = int(slots[s]) // B, int(slots[s]) % B
+            want_k = F.quantize(k[s].float().numpy(), np.float32(1 / ks))
+            assert np.array_equal(kc[blk, :, off], want_k.reshape(hkv, D))
