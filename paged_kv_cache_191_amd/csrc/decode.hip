@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   constexpr int KL = KV8 ? 2 : 4;  // 16-byte K loads per token row per tile
   constexpr int TPI = KV8 ? 2 : 1; // tiles whose loads are issued together
   __shared__ int s_cs[kMaxSeqs + 1];
-  __shared__ int s_part[kWaves * kWave];
+  __shared__ int s_part[kWaves];
   __shared__ float sm_o[kWaves][kHeadBlk][kD];
   __shared__ float sm_ml[kWaves][kHeadBlk][2];
 
@@ -196,6 +196,9 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   const int S = a.num_seqs;
 
   // --- tile offsets of the sequences (exclusive scan of the tile counts) ---
+  // Thread tid owns sequences [lo, hi): their tile counts go to s_cs, then
+  // the 256 per-thread sums are scanned (shuffles inside each wave, the
+  // four wave totals through LDS) and s_cs is turned into offsets in place.
   {
     const int per = (S + kWaves * kWave - 1) / (kWaves * kWave);
     const int lo = tid * per;
@@ -203,24 +206,27 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     int sum = 0;
     for (int i = lo; i < hi; ++i) {
       const int L = clamp_ctx(a, i, PAGED);
-      sum += tiles_of(L - shared_of(a, i, L));
+      const int n = tiles_of(L - shared_of(a, i, L));
+      s_cs[i] = n;
+      sum += n;
     }
-    s_part[tid] = sum;
+    int inc = sum;  // inclusive scan over the lanes of this wave
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (lane == kWave - 1) s_part[w] = inc;
     __syncthreads();
-    // inclusive Hillis-Steele scan of the 256 partial sums
-    for (int o = 1; o < kWaves * kWave; o <<= 1) {
-      const int add = tid >= o ? s_part[tid - o] : 0;
-      __syncthreads();
-      s_part[tid] += add;
-      __syncthreads();
-    }
-    int run = s_part[tid] - sum;
+    int base = 0;  // tiles of the waves before this one
+    for (int ww = 0; ww < w; ++ww) base += s_part[ww];
+    int run = base + inc - sum;
     for (int i = lo; i < hi; ++i) {
+      const int n = s_cs[i];
       s_cs[i] = run;
-      const int L = clamp_ctx(a, i, PAGED);
-      run += tiles_of(L - shared_of(a, i, L));
+      run += n;
     }
-    if (tid == kWaves * kWave - 1) s_cs[S] = s_part[tid];
+    if (tid == kWaves * kWave - 1) s_cs[S] = base + inc;
     __syncthreads();
   }
   const int total = s_cs[S];

@@ -264,6 +264,24 @@ def test_decode_physical_permutation_is_bit_identical():
     assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
 
 
+@pytest.mark.parametrize("S", [700, 4100])
+def test_decode_many_sequences(S):
+    # More sequences than the 256 threads of the tile-offset scan (several
+    # per thread), and more than one launch's 4096; short contexts, with
+    # empty ones among them.
+    w = W.WORKLOADS["llama3_8b_decode"].replace(
+        num_seqs=S, num_q_heads=8, num_kv_heads=2, length_range=(0, 48),
+        name=f"many_seqs_{S}")
+    inp = _draw(w)
+    ctx = W.context_lengths(inp)
+    assert (ctx == 0).any()
+    cap = H.tables_capacity(int(max(ctx.max(), 1)), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    outs, want = _decode_both(inp, nat, orc, ctx)
+    _check(outs, want, w)
+
+
 @pytest.mark.parametrize("variant", ["g20_d128", "d64_bf16", "empty_and_one"])
 def test_decode_edge_shapes(variant):
     base = W.WORKLOADS["llama3_8b_decode"]
