@@ -90,6 +90,10 @@ FP8_SCALE = 0.0123
 TRAFFIC_PROFILES = {
     "llama3_8b_decode": os.path.join(ROOT, "profiles",
                                      "hbm_traffic_decode_llama3_8b.txt"),
+    "yi34b_long_decode": os.path.join(ROOT, "profiles",
+                                      "hbm_traffic_decode_yi34b.txt"),
+    "prefix_share_decode": os.path.join(ROOT, "profiles",
+                                        "hbm_traffic_decode_prefix_share.txt"),
 }
 
 
