@@ -191,17 +191,17 @@ class DecodeReplica:
             self.lmax = -(-self.lmax // self.vmm) * self.vmm
         self.cap = -(-self.lmax // B)
         n_pool = len(inp.free_order)
-        # pinned host staging: [slots int64 S | lens int32 S | table int32 S*cap]
-        nbytes = 8 * S + 4 * S + 4 * S * self.cap
+        # host mirror of [lens int32 S | table int32 S*cap], uploaded once
+        # after the set-up writes; the device copy is then kept current by
+        # the append kernel
+        nbytes = 4 * S + 4 * S * self.cap
         self.h_buf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
         self.d_buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         hb = self.h_buf.numpy()
-        self.h_slots = hb[:8 * S].view(np.int64)
-        self.h_lens = hb[8 * S:12 * S].view(np.int32)
-        self.h_table = hb[12 * S:].view(np.int32).reshape(S, self.cap)
-        self.d_slots = self.d_buf[:8 * S].view(torch.int64)
-        self.d_lens = self.d_buf[8 * S:12 * S].view(torch.int32)
-        self.d_table = self.d_buf[12 * S:].view(torch.int32).view(S, self.cap)
+        self.h_lens = hb[:4 * S].view(np.int32)
+        self.h_table = hb[4 * S:].view(np.int32).reshape(S, self.cap)
+        self.d_lens = self.d_buf[:4 * S].view(torch.int32)
+        self.d_table = self.d_buf[4 * S:].view(torch.int32).view(S, self.cap)
         self.q = inp.q.to(device)
         self.out = torch.empty_like(self.q)
         self.new_k, self.new_v = new_k, new_v
@@ -313,23 +313,22 @@ class DecodeReplica:
         torch.cuda.synchronize()
 
     def host_append(self) -> None:
-        """Host part of a step: allocation and slot mapping (paged), or the
-        contiguous slot s * Lmax + position."""
+        """Host part of a step. Paged: kv_seq_append (allocation, slot
+        mapping) on the host mirror, and the block ids it took (-1 where the
+        entry did not change) into the pinned buffer the append kernel
+        reads. Contiguous: the host lengths advance (and, demand-mapped, the
+        pages a new token needs are mapped)."""
         self.uploaded.synchronize()
         if self.paged:
             S = self.w.num_seqs
             ar = np.arange(S)
             idx = self.h_lens // self.w.block_size
             before = self.h_table[ar, idx]
-            slots, pairs = self.pool.seq_append(self.h_table, self.h_lens)
+            _, pairs = self.pool.seq_append(self.h_table, self.h_lens)
             assert len(pairs) == 0
-            self.h_slots[:] = slots
             after = self.h_table[ar, idx]
             self.h_newb.numpy()[:] = np.where(after != before, after, -1)
         else:
-            S = self.w.num_seqs
-            self.h_slots[:] = np.arange(S, dtype=np.int64) * self.lmax + \
-                self.h_lens
             self.h_lens += 1
             if self.vmm:
                 # map a page for the sequences whose new token starts one
