@@ -467,8 +467,11 @@ int32_t kv_prefix_cache_size(const kv_prefix_cache* cache);
  * created; kv_vcache_destroy frees everything. Before a release or destroy
  * the caller must have synchronized the work that reads those pages.
  * Errors: KV_EINVAL (arguments), KV_ENOMEM (device memory), KV_EHIP (other
- * HIP failures); a failed reserve leaves the mapping unchanged. One host
- * thread per cache. */
+ * HIP failures); a failed reserve leaves the mapping unchanged. The calls
+ * on a cache come from one host thread; the cache's own mapping thread
+ * serves kv_vcache_prefetch requests (the newsletter's mapping ahead of
+ * need, off the critical path). One mutex guards the cache, so a call that
+ * arrives while that thread runs a request waits for the request. */
 typedef struct kv_vcache kv_vcache;
 
 /* Minimum mapping granularity of the current device, in bytes. */
@@ -488,7 +491,22 @@ kv_status kv_vcache_ptrs(const kv_vcache* cache, void** k, void** v);
 kv_status kv_vcache_reserve(kv_vcache* cache, int32_t seq, int32_t num_tokens,
                             int32_t* pages_mapped);
 
-/* Unmap all pages of sequence seq (their memory stays in the pool). */
+/* Queue a request that tokens [0, num_tokens) of sequence seq be backed,
+ * for the cache's mapping thread (started by the first request), and
+ * return at once. A later kv_vcache_reserve over the same tokens then finds
+ * the pages mapped, or waits for the request being served. Argument errors
+ * are returned here; failures of the mapping itself are reported by
+ * kv_vcache_sync (and the pages stay unmapped, so a later reserve maps them
+ * or reports its own error). */
+kv_status kv_vcache_prefetch(kv_vcache* cache, int32_t seq,
+                             int32_t num_tokens);
+
+/* Wait until every queued request has been served; return (and clear) the
+ * first failure any of them met since the last sync. */
+kv_status kv_vcache_sync(kv_vcache* cache);
+
+/* Unmap all pages of sequence seq (their memory stays in the pool); queued
+ * requests for seq are dropped. */
 kv_status kv_vcache_release(kv_vcache* cache, int32_t seq);
 
 /* Pages mapped per region of sequence seq (-1 on a bad argument). */

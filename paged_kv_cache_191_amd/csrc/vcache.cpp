@@ -14,10 +14,23 @@
 // contiguous layout with seq_stride = max_context). The unit of mapping is a
 // page of page_tokens rows of one (sequence, KV head) in one tensor, so
 // a sequence of L tokens holds 2 * Hkv * ceil(L / page_tokens) pages.
+//
+// The same section has vAttention run the mapping calls ahead of need, off
+// the critical path. kv_vcache_prefetch queues such a request for the
+// cache's own mapping thread (started by the first request); a reserve that
+// finds the pages mapped returns at once, and one that needs a page being
+// mapped waits for it. All state is guarded by one mutex, held by whichever
+// thread runs the mapping calls.
 
 #include <hip/hip_runtime.h>
 
+#include <condition_variable>
+#include <deque>
+#include <mutex>
 #include <new>
+#include <string>
+#include <thread>
+#include <utility>
 #include <vector>
 
 #include "kvpaged_internal.h"
@@ -37,6 +50,15 @@ struct kv_vcache {
   std::vector<hipMemGenericAllocationHandle_t> pool;  // created, not mapped
   int64_t mapped_pages = 0;
   int64_t created_pages = 0;
+  // mapping thread
+  mutable std::mutex mu;           // guards every field of the cache
+  std::condition_variable cv;      // a request queued, or one served
+  std::deque<std::pair<int32_t, int32_t>> queue;  // (seq, tokens) to back
+  std::thread worker;
+  bool stop = false;
+  bool busy = false;               // the thread is serving a request
+  kv_status async_status = KV_OK;  // first failure of a request since sync
+  std::string async_msg;
 };
 
 namespace {
@@ -160,6 +182,13 @@ extern "C" kv_status kv_vcache_create(int32_t max_seqs, int32_t max_context,
 
 extern "C" void kv_vcache_destroy(kv_vcache* c) {
   if (!c) return;
+  {
+    std::lock_guard<std::mutex> lk(c->mu);
+    c->stop = true;
+    c->queue.clear();
+  }
+  c->cv.notify_all();
+  if (c->worker.joinable()) c->worker.join();
   for (int32_t s = 0; s < c->max_seqs; ++s) (void)unmap_tail(c, s, 0);
   for (auto h : c->pool) (void)hipMemRelease(h);
   for (int t = 0; t < 2; ++t)
@@ -174,18 +203,16 @@ extern "C" kv_status kv_vcache_ptrs(const kv_vcache* c, void** k, void** v) {
   return KV_OK;
 }
 
-extern "C" kv_status kv_vcache_reserve(kv_vcache* c, int32_t seq,
-                                       int32_t num_tokens,
-                                       int32_t* pages_mapped) {
-  if (!c) return kvp_fail(KV_EINVAL, "kv_vcache_reserve: cache is NULL");
-  if (seq < 0 || seq >= c->max_seqs || num_tokens < 0 ||
-      num_tokens > c->max_context)
-    return kvp_fail(KV_EINVAL,
-                    "kv_vcache_reserve: seq %d / tokens %d outside [0, %d) / "
-                    "[0, %d]",
-                    seq, num_tokens, c->max_seqs, c->max_context);
-  const int32_t want =
-      (int32_t)(((int64_t)num_tokens + c->page_tokens - 1) / c->page_tokens);
+namespace {
+
+int32_t pages_for(const kv_vcache* c, int32_t tokens) {
+  return (int32_t)(((int64_t)tokens + c->page_tokens - 1) / c->page_tokens);
+}
+
+// Map the pages of sequence seq below page `want` that are not mapped yet;
+// *pages_mapped (may be NULL) = pages mapped here. The caller holds c->mu.
+kv_status map_upto(kv_vcache* c, int32_t seq, int32_t want,
+                   int32_t* pages_mapped) {
   const int32_t have = c->pages[seq];
   if (pages_mapped) *pages_mapped = 0;
   if (want <= have) return KV_OK;
@@ -218,7 +245,7 @@ extern "C" kv_status kv_vcache_reserve(kv_vcache* c, int32_t seq,
         } else {
           hipError_t e = hipMemCreate(&h, c->page_bytes, &prop, 0);
           if (e != hipSuccess) {
-            st = hip_fail("kv_vcache_reserve: hipMemCreate", e);
+            st = hip_fail("kv_vcache: hipMemCreate", e);
             break;
           }
           fresh = true;
@@ -236,7 +263,7 @@ extern "C" kv_status kv_vcache_reserve(kv_vcache* c, int32_t seq,
           } else {
             c->pool.push_back(h);
           }
-          st = hip_fail("kv_vcache_reserve: hipMemMap/hipMemSetAccess", e);
+          st = hip_fail("kv_vcache: hipMemMap/hipMemSetAccess", e);
           break;
         }
         c->handles[region * c->pages_per_region + p] = h;
@@ -255,23 +282,109 @@ extern "C" kv_status kv_vcache_reserve(kv_vcache* c, int32_t seq,
   return KV_OK;
 }
 
+// The mapping thread: serves queued requests in order until stopped.
+void worker_main(kv_vcache* c) {
+  (void)hipSetDevice(c->device);
+  std::unique_lock<std::mutex> lk(c->mu);
+  for (;;) {
+    c->cv.wait(lk, [c] { return c->stop || !c->queue.empty(); });
+    if (c->stop) return;
+    const std::pair<int32_t, int32_t> r = c->queue.front();
+    c->queue.pop_front();
+    c->busy = true;
+    const kv_status st = map_upto(c, r.first, pages_for(c, r.second), nullptr);
+    if (st != KV_OK && c->async_status == KV_OK) {
+      c->async_status = st;
+      c->async_msg = kv_last_error();
+    }
+    c->busy = false;
+    c->cv.notify_all();
+  }
+}
+
+}  // namespace
+
+extern "C" kv_status kv_vcache_reserve(kv_vcache* c, int32_t seq,
+                                       int32_t num_tokens,
+                                       int32_t* pages_mapped) {
+  if (!c) return kvp_fail(KV_EINVAL, "kv_vcache_reserve: cache is NULL");
+  if (seq < 0 || seq >= c->max_seqs || num_tokens < 0 ||
+      num_tokens > c->max_context)
+    return kvp_fail(KV_EINVAL,
+                    "kv_vcache_reserve: seq %d / tokens %d outside [0, %d) / "
+                    "[0, %d]",
+                    seq, num_tokens, c->max_seqs, c->max_context);
+  std::lock_guard<std::mutex> lk(c->mu);
+  return map_upto(c, seq, pages_for(c, num_tokens), pages_mapped);
+}
+
+extern "C" kv_status kv_vcache_prefetch(kv_vcache* c, int32_t seq,
+                                        int32_t num_tokens) {
+  if (!c) return kvp_fail(KV_EINVAL, "kv_vcache_prefetch: cache is NULL");
+  if (seq < 0 || seq >= c->max_seqs || num_tokens < 0 ||
+      num_tokens > c->max_context)
+    return kvp_fail(KV_EINVAL,
+                    "kv_vcache_prefetch: seq %d / tokens %d outside [0, %d) / "
+                    "[0, %d]",
+                    seq, num_tokens, c->max_seqs, c->max_context);
+  std::lock_guard<std::mutex> lk(c->mu);
+  if (pages_for(c, num_tokens) <= c->pages[seq]) return KV_OK;
+  if (!c->worker.joinable()) {
+    try {
+      c->worker = std::thread(worker_main, c);
+    } catch (...) {
+      return kvp_fail(KV_ENOMEM, "kv_vcache_prefetch: cannot start the "
+                      "mapping thread");
+    }
+  }
+  try {
+    c->queue.emplace_back(seq, num_tokens);
+  } catch (const std::bad_alloc&) {
+    return kvp_fail(KV_ENOMEM, "kv_vcache_prefetch: host allocation");
+  }
+  c->cv.notify_all();
+  return KV_OK;
+}
+
+extern "C" kv_status kv_vcache_sync(kv_vcache* c) {
+  if (!c) return kvp_fail(KV_EINVAL, "kv_vcache_sync: cache is NULL");
+  std::unique_lock<std::mutex> lk(c->mu);
+  c->cv.wait(lk, [c] { return c->queue.empty() && !c->busy; });
+  const kv_status st = c->async_status;
+  const std::string msg = c->async_msg;
+  c->async_status = KV_OK;
+  c->async_msg.clear();
+  if (st != KV_OK) return kvp_fail(st, "kv_vcache_prefetch (earlier): %s",
+                                   msg.c_str());
+  return KV_OK;
+}
+
 extern "C" kv_status kv_vcache_release(kv_vcache* c, int32_t seq) {
   if (!c) return kvp_fail(KV_EINVAL, "kv_vcache_release: cache is NULL");
   if (seq < 0 || seq >= c->max_seqs)
     return kvp_fail(KV_EINVAL, "kv_vcache_release: seq %d outside [0, %d)",
                     seq, c->max_seqs);
+  std::lock_guard<std::mutex> lk(c->mu);
+  // queued requests for this sequence are dropped, not served later
+  for (auto it = c->queue.begin(); it != c->queue.end();)
+    it = it->first == seq ? c->queue.erase(it) : it + 1;
   return unmap_tail(c, seq, 0);
 }
 
 extern "C" int32_t kv_vcache_seq_pages(const kv_vcache* c, int32_t seq) {
   if (!c || seq < 0 || seq >= c->max_seqs) return -1;
+  std::lock_guard<std::mutex> lk(c->mu);
   return c->pages[seq];
 }
 
 extern "C" int64_t kv_vcache_mapped_bytes(const kv_vcache* c) {
-  return c ? c->mapped_pages * (int64_t)c->page_bytes : -1;
+  if (!c) return -1;
+  std::lock_guard<std::mutex> lk(c->mu);
+  return c->mapped_pages * (int64_t)c->page_bytes;
 }
 
 extern "C" int64_t kv_vcache_held_bytes(const kv_vcache* c) {
-  return c ? c->created_pages * (int64_t)c->page_bytes : -1;
+  if (!c) return -1;
+  std::lock_guard<std::mutex> lk(c->mu);
+  return c->created_pages * (int64_t)c->page_bytes;
 }

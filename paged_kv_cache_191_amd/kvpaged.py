@@ -109,6 +109,8 @@ SIGNATURES = {
     "kv_vcache_ptrs": (_I32, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
     "kv_vcache_reserve": (_I32, [_P, _I32, _I32, _PI32]),
     "kv_vcache_release": (_I32, [_P, _I32]),
+    "kv_vcache_prefetch": (_I32, [_P, _I32, _I32]),
+    "kv_vcache_sync": (_I32, [_P]),
     "kv_vcache_seq_pages": (_I32, [_P, _I32]),
     "kv_vcache_mapped_bytes": (_I64, [_P]),
     "kv_vcache_held_bytes": (_I64, [_P]),
@@ -774,6 +776,17 @@ class VCache:
                                        int(num_tokens), ctypes.byref(n)),
                "kv_vcache_reserve")
         return int(n.value)
+
+    def prefetch(self, seq: int, num_tokens: int) -> None:
+        """Queue the mapping of tokens [0, num_tokens) of seq for the cache's
+        mapping thread; returns at once."""
+        _check(lib().kv_vcache_prefetch(self._handle(), int(seq),
+                                        int(num_tokens)),
+               "kv_vcache_prefetch")
+
+    def sync(self) -> None:
+        """Wait for every queued mapping request; raise the first failure."""
+        _check(lib().kv_vcache_sync(self._handle()), "kv_vcache_sync")
 
     def release(self, seq: int) -> None:
         _check(lib().kv_vcache_release(self._handle(), int(seq)),

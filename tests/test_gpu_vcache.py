@@ -175,3 +175,57 @@ def test_reserve_rejects_bad_arguments():
         assert vc.mapped_bytes == 0
     with pytest.raises(kv.KVError):   # 16 fp32 rows of 8 values: 512 B pages
         kv.VCache(2, 256, 1, 8, torch.float32, 16)
+
+
+def test_prefetch_maps_ahead_of_reserve():
+    # Requests served by the cache's mapping thread: after sync the pages
+    # are there, reserve maps nothing more, and the kernels read them.
+    rng = np.random.default_rng(10)
+    P = 256
+    lengths = [700, 1, 1024, 0]
+    with kv.VCache(len(lengths), 1024, HKV, D, torch.bfloat16, P) as vc:
+        for s, L in enumerate(lengths):
+            vc.prefetch(s, L)
+        vc.sync()
+        pages = _expected_pages(lengths, P)
+        assert [vc.seq_pages(s) for s in range(len(lengths))] == pages
+        assert vc.mapped_bytes == sum(pages) * 2 * HKV * P * D * 2
+        assert all(vc.reserve(s, L) == 0 for s, L in enumerate(lengths))
+        ks, vs = _fill(vc, lengths, rng)
+        q = _bf16(rng, (len(lengths), HQ, D)).to(DEV)
+        got = _decode(vc, q, lengths)
+        want = O.decode_logical(q.float().cpu().numpy(), ks, vs, SCALE)
+        err = max_abs(got, want)
+        print(f"vcache decode after prefetch: max-abs {err:.2e}", flush=True)
+        assert err <= TOL
+        # a reserve racing a queued request: one of the two maps the page
+        vc.prefetch(1, 300)
+        mapped = vc.reserve(1, 300)
+        assert mapped in (0, 2 * HKV)
+        vc.sync()
+        assert vc.seq_pages(1) == 2
+
+
+def test_prefetch_release_and_close_with_requests_queued():
+    with kv.VCache(4, 4096, HKV, D, torch.bfloat16, 256) as vc:
+        for s in range(4):
+            vc.prefetch(s, 4096)
+        vc.release(2)   # a request still queued for it is dropped
+        vc.sync()
+        assert vc.seq_pages(2) == 0
+        assert [vc.seq_pages(s) for s in (0, 1, 3)] == [16, 16, 16]
+        for s in range(4):
+            vc.prefetch(s, 4096)
+        # leaving the block destroys the cache with requests still queued:
+        # they are dropped and the mapping thread is joined
+
+
+def test_prefetch_rejects_bad_arguments():
+    with kv.VCache(2, 256, HKV, D, torch.bfloat16, 128) as vc:
+        with pytest.raises(kv.KVError):
+            vc.prefetch(2, 16)
+        with pytest.raises(kv.KVError):
+            vc.prefetch(0, 257)
+        vc.prefetch(0, 0)              # nothing to map: no request
+        vc.sync()
+        assert vc.mapped_bytes == 0
