@@ -177,7 +177,9 @@ kv_status kv_reshape_and_cache(const void* k, const void* v,
  * updated in place. new_blocks: int32 [num_seqs], -1 = keep the entry;
  * device memory or pinned host memory (hipHostMalloc, torch's pin_memory),
  * which the kernel reads directly, so that a step uploads nothing; other
- * host memory -> KV_EINVAL. A sequence with L outside [0, bt_stride * B),
+ * host memory -> KV_EINVAL. The kernel reads new_blocks when it runs, not
+ * at the call: the host must not rewrite it before then (e.g. wait for an
+ * event recorded after the call). A sequence with L outside [0, bt_stride * B),
  * or whose block is outside [0, num_blocks), is left unchanged. The
  * contiguous layout is the case block_size = seq_stride with
  * block_tables[s][0] = s. The result equals kv_seq_append's table and slots
