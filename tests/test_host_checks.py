@@ -1,0 +1,120 @@
+"""Host-side checks that need no GPU: argument validation of the device
+append and demand-mapped cache entry points (they return before any HIP
+call), and bench.py's algorithmic byte count, traffic records and one-GPU
+guard."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+from native import ensure_built
+from paged_kv_cache_191_amd import kvpaged as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def setup_module(_):
+    ensure_built()
+
+
+def _append(L=None, **kw):
+    a = dict(k=None, v=None, nb=None, bt=None, stride=4, ctx=None, S=2,
+             kc=None, vc=None, N=8, B=16, hkv=2, d=128)
+    a.update(kw)
+    return L(a["k"], a["v"], a["nb"], a["bt"], a["stride"], a["ctx"], a["S"],
+             a["kc"], a["vc"], a["N"], a["B"], a["hkv"], a["d"])
+
+
+def test_append_token_argument_errors():
+    lib = kv.lib()
+
+    def call(dtype=kv.KV_BF16, **kw):
+        return _append(lambda *x: lib.kv_append_token(*x, dtype, None), **kw)
+
+    assert call(S=0) == kv.KV_OK                     # nothing to do
+    assert call() == kv.KV_EINVAL                    # NULL pointers
+    for bad in (dict(S=-1), dict(stride=0), dict(N=0), dict(B=0),
+                dict(hkv=0), dict(d=0)):
+        assert call(**bad) == kv.KV_EINVAL, bad
+        assert "bad shape" in kv.kv_last_error()
+    assert call(dtype=7) == kv.KV_EINVAL
+    assert "dtype" in kv.kv_last_error()
+
+
+def test_append_token_fp8_argument_errors():
+    lib = kv.lib()
+
+    def call(ks=1.0, vs=1.0, **kw):
+        return _append(lambda *x: lib.kv_append_token_fp8(*x, ks, vs, None),
+                       **kw)
+
+    assert call(S=0) == kv.KV_OK
+    assert call(d=12) == kv.KV_EINVAL                # D % 8 != 0
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("inf"), 1.0),
+                   (float("nan"), 1.0)):
+        assert call(ks=ks, vs=vs) == kv.KV_EINVAL
+        assert "scale" in kv.kv_last_error()
+    assert call() == kv.KV_EINVAL                    # NULL pointers
+
+
+def test_vcache_prefetch_and_sync_reject_null():
+    lib = kv.lib()
+    assert lib.kv_vcache_prefetch(None, 0, 16) == kv.KV_EINVAL
+    assert lib.kv_vcache_sync(None) == kv.KV_EINVAL
+
+
+def test_decode_bytes_counts_each_term_once():
+    sys.path.insert(0, ROOT)
+    import bench
+    ctx = np.array([35, 16, 1, 100])
+    hq, hkv, d, B = 8, 8, 64, 16
+    kvb = int(ctx.sum()) * hkv * d * 2 * 4      # K and V, fp32 (4 B)
+    qo = 2 * 4 * hq * d * 4
+    table = (3 + 1 + 1 + 7) * 4                  # blocks per sequence x 4 B
+    want = kvb + qo + table + 4 * 4
+    assert bench.decode_bytes(ctx, hq, hkv, d, B, True, esize=4) == want
+    assert bench.decode_bytes(ctx, hq, hkv, d, B, False, esize=4) == \
+        want - table
+    # a 32-token shared prefix counts once over the four sequences
+    ctx2 = ctx + 32
+    shared = bench.decode_bytes(ctx2, hq, hkv, d, B, True, esize=4,
+                                shared=32)
+    full = bench.decode_bytes(ctx2, hq, hkv, d, B, True, esize=4)
+    assert full - shared == 3 * 32 * hkv * d * 2 * 4
+    # fp8 K/V: one byte per value, q/o unchanged
+    fp8 = bench.decode_bytes(ctx, hq, hkv, d, B, True, esize=2, kv_esize=1)
+    assert fp8 == int(ctx.sum()) * hkv * d * 2 + 2 * 4 * hq * d * 2 + \
+        table + 16
+
+
+def test_traffic_records_parse():
+    # Each record holds measured and algorithmic bytes per launch and the
+    # hashes of its sources; bench.py reports the measured bytes only while
+    # the hashes match (else None).
+    sys.path.insert(0, ROOT)
+    import bench
+    for w, path in bench.TRAFFIC_PROFILES.items():
+        vals = {}
+        hashes = 0
+        for line in open(path):
+            if line.startswith(("traffic_bytes_per_launch:",
+                                "algorithmic_bytes_per_launch:")):
+                k, v = line.split(":")
+                vals[k] = int(v)
+            hashes += line.startswith("source_sha256 ")
+        assert hashes >= 2, w
+        ratio = vals["traffic_bytes_per_launch"] / \
+            vals["algorithmic_bytes_per_launch"]
+        assert 1.0 <= ratio < 1.3, (w, ratio)
+        t = bench.recorded_traffic(w)
+        assert t is None or t == vals["traffic_bytes_per_launch"]
+    assert bench.recorded_traffic("no_such_workload") is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
