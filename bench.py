@@ -579,10 +579,11 @@ def run_cow(w, steps: int, warmup: int, device):
         n_new = np.zeros(S, dtype=np.int32)
         n_new[0] = P
         slots0, _ = pool.seq_append(table, lens, n_new)
-        for s in range(1, S):
-            pool.share(table[0, :nb_prefix].tolist())
-            table[s, :nb_prefix] = table[0, :nb_prefix]
-            lens[s] = P
+        # fork: one reference to each prefix block per other sequence, in
+        # one call (kv_block_share counts repeated ids once per occurrence)
+        pool.share(np.tile(table[0, :nb_prefix], S - 1))
+        table[1:, :nb_prefix] = table[0, :nb_prefix]
+        lens[1:] = P
         slots, pairs = pool.seq_append(table, lens)
         host_us.append(1e6 * (time.perf_counter() - t_h))
         n_pairs = len(pairs)
