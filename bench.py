@@ -598,6 +598,9 @@ def run_cow(w, steps: int, warmup: int, device):
         d_table = torch.from_numpy(table).to(device)
         d_lens = torch.from_numpy(lens).to(device)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        # keep the GPU busy while the step is queued, so that the events
+        # time the kernels and not the launch latency after the host work
+        torch.cuda._sleep(SPIN_CYCLES)
         ev[0].record()
         kv.kv_copy_blocks(kc, vc, d_pairs)
         ev[1].record()
