@@ -699,6 +699,7 @@ def prefill_pass(inp, layout: str, device):
             d_table = torch.from_numpy(table).to(device)
             q = q_dev[rows_d]
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            torch.cuda._sleep(SPIN_CYCLES)   # GPU busy while this is queued
             ev[0].record()
             kv.kv_reshape_and_cache(k_new, v_new, d_slots, kc, vc)
             ev[1].record()
