@@ -254,3 +254,38 @@ def test_append_fp8_matches_cache_write_and_codec():
             blk, off = int(slots[s]) // B, int(slots[s]) % B
             want_k = F.quantize(k[s].float().numpy(), np.float32(1 / ks))
             assert np.array_equal(kc[blk, :, off], want_k.reshape(hkv, D))
+
+
+def test_decode_step_through_device_append_full_size():
+    # The decode step as the bench times it, at the Llama-3-8B batch shape
+    # (64 sequences, 32/8 heads, contexts U{512..4096}): contexts written up
+    # to L - 1, then host kv_seq_append -> new block ids in pinned memory ->
+    # kv_append_token of each sequence's last row -> paged_attn_decode over
+    # the device-resident table and lengths, against the fp64 oracle.
+    w = W.WORKLOADS["llama3_8b_decode"]
+    inp = _draw(w, headroom=w.num_seqs)
+    ctx = W.context_lengths(inp)
+    B = w.block_size
+    cap = H.tables_capacity(int(ctx.max()), B)
+    nat = H.build_native(inp, B, cap, upto=ctx - 1)
+    orc = H.build_oracle(inp, B)
+    bt_dev = torch.from_numpy(nat.tables.copy()).cuda()
+    lens_dev = torch.from_numpy(nat.lens.copy()).cuda()
+    _, pairs, new_blocks = _host_step(nat, B)
+    assert len(pairs) == 0 and nat.lens.tolist() == ctx.tolist()
+    last = torch.from_numpy(np.array([W.logical_rows(inp, s)[-1]
+                                      for s in range(w.num_seqs)]))
+    nb = torch.from_numpy(new_blocks).pin_memory()
+    kv.kv_append_token(inp.k[last].cuda(), inp.v[last].cuda(), nb, bt_dev,
+                       lens_dev, nat.k_cache, nat.v_cache)
+    out = torch.empty_like(inp.q.cuda())
+    kv.paged_attn_decode(out, inp.q.cuda(), nat.k_cache, nat.v_cache, bt_dev,
+                         lens_dev, int(ctx.max()), H.scale_of(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(lens_dev.cpu().numpy(), ctx)
+    assert np.array_equal(bt_dev.cpu().numpy(), nat.tables)
+    want = O.decode_paged(inp.q.float().numpy(), orc.k_pool, orc.v_pool,
+                          orc.tables, ctx, H.scale_of(w))
+    err = H.max_abs(out.float().cpu().numpy(), want)
+    _log(f"decode step through kv_append_token: max-abs {err:.3e}")
+    assert err <= H.tolerance(w)
