@@ -1,7 +1,8 @@
 """One small invocation of the hot path on cuda:0, checked against the fp64
 oracle: allocation and slot mapping through the native allocator, cache
-write, paged decode (fp32 generic path and bf16 MFMA path) and paged
-chunked prefill (bf16 MFMA path). Raises on any mismatch."""
+write, paged decode (fp32 generic path and bf16 MFMA path), one decode step
+through the device-side append (block table and lengths on the device) and
+paged chunked prefill (bf16 MFMA path). Raises on any mismatch."""
 from __future__ import annotations
 
 import numpy as np
@@ -73,6 +74,56 @@ def run() -> None:
               flush=True)
         if not err <= tol:
             raise AssertionError(f"decode {w.name}: max-abs {err}")
+    # --- one decode step through the device-side append (bf16) ------------
+    w = W.WORKLOADS["llama3_8b_decode"].replace(
+        num_seqs=4, length_range=(1, 700), name="smoke_step")
+    B, S = w.block_size, w.num_seqs
+    inp = W.draw(w, lambda L: O.pool_blocks_exact(L, B) + S)
+    cap = max(1, -(-(int(inp.lengths.max()) + 1) // B))
+    pool, tables, lens, kc, vc = _fill(inp, B, cap, dev)
+    mp = A.ModelPool(len(inp.free_order), B, inp.free_order)
+    mt, ml = [[] for _ in range(S)], [0] * S
+    st, mslots, _ = A.append_tokens(mp, mt, ml, inp.lengths.tolist(), cap)
+    kp = np.full((len(inp.free_order), B, w.num_kv_heads, w.head_dim),
+                 np.nan, dtype=np.float32)
+    vp = np.full_like(kp, np.nan)
+    O.scatter_rows(kp, inp.k.float().numpy(), mslots)
+    O.scatter_rows(vp, inp.v.float().numpy(), mslots)
+    bt_d = torch.from_numpy(tables).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    ar = np.arange(S)
+    idx = lens // B
+    before = tables[ar, idx].copy()
+    _, pairs = pool.seq_append(tables, lens)        # one token each
+    after = tables[ar, idx]
+    new_blocks = torch.from_numpy(
+        np.where(after != before, after, -1).astype(np.int32)).pin_memory()
+    g = np.random.default_rng([w.seed, 77])
+    shape = (S, w.num_kv_heads, w.head_dim)
+    k_new = torch.from_numpy(g.standard_normal(shape, dtype=np.float32)).to(
+        torch.bfloat16)
+    v_new = torch.from_numpy(g.standard_normal(shape, dtype=np.float32)).to(
+        torch.bfloat16)
+    kv.kv_append_token(k_new.to(dev), v_new.to(dev), new_blocks, bt_d, lens_d,
+                       kc, vc)
+    q = inp.q.to(dev)
+    out = torch.empty_like(q)
+    scale = 1.0 / float(np.sqrt(w.head_dim))
+    kv.paged_attn_decode(out, q, kc, vc, bt_d, lens_d, int(lens.max()), scale)
+    torch.cuda.synchronize()
+    st, mslots, _ = A.append_tokens(mp, mt, ml, [1] * S, cap)
+    assert st == A.OK and len(pairs) == 0
+    O.scatter_rows(kp, k_new.float().numpy(), mslots)
+    O.scatter_rows(vp, v_new.float().numpy(), mslots)
+    if lens_d.cpu().tolist() != ml or any(
+            mt[s] != bt_d[s, :len(mt[s])].cpu().tolist() for s in range(S)):
+        raise AssertionError("device table or lengths differ from the oracle")
+    want = O.decode_paged(inp.q.float().numpy(), kp, vp, mt, ml, scale)
+    err = float(np.abs(out.float().cpu().numpy() - want).max())
+    print(f"smoke decode step (device append): max-abs {err:.2e} (tol 2e-2)",
+          flush=True)
+    if not err <= 2e-2:
+        raise AssertionError(f"decode step: max-abs {err}")
     # --- chunked prefill, bf16 MFMA path -----------------------------------
     w = W.WORKLOADS["yi6b_chunked_prefill_b16"].replace(
         num_seqs=2, lengths=(200, 77), name="smoke_prefill")
