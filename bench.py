@@ -501,6 +501,52 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     return res
 
 
+def run_tiny_decode(device, launches: int = 50):
+    """The small fp32 decode configuration (4 sequences, contexts 35, 16, 1
+    and 100, 8/8 heads, head_dim 64, block 16, 32-block pool): the generic
+    path, latency-bound, so its time is reported without a roofline. Each
+    launch is timed with events behind a GPU spin (kernel time, not launch
+    latency)."""
+    import torch
+    from paged_kv_cache_191_amd import kvpaged as kv
+    from paged_kv_cache_191_amd import workloads as W
+    w = W.WORKLOADS["decode_tiny_f32"]
+    B, S = w.block_size, w.num_seqs
+    inp = W.draw(w, lambda L: pool_blocks(kv, w, L))
+    n_pool = len(inp.free_order)
+    pool = kv.KVPool(n_pool, B, inp.free_order)
+    cap = -(-int(inp.lengths.max()) // B)
+    table = np.full((S, cap), -1, dtype=np.int32)
+    lens = np.zeros(S, dtype=np.int32)
+    slots, _ = pool.seq_append(table, lens, inp.lengths.astype(np.int32))
+    kc = torch.zeros((n_pool, w.num_kv_heads, B, w.head_dim),
+                     dtype=torch.float32, device=device)
+    vc = torch.zeros_like(kc)
+    kv.kv_reshape_and_cache(inp.k.to(device), inp.v.to(device),
+                            torch.from_numpy(slots).to(device), kc, vc)
+    q = inp.q.to(device)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(table).to(device)
+    ctx = torch.from_numpy(lens).to(device)
+    scale = 1.0 / float(np.sqrt(w.head_dim))
+    times = []
+    for i in range(launches + 10):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda._sleep(SPIN_CYCLES)
+        ev[0].record()
+        kv.paged_attn_decode(out, q, kc, vc, bt, ctx, int(lens.max()), scale)
+        ev[1].record()
+        if i >= 10:
+            times.append(ev)
+    torch.cuda.synchronize()
+    us = stats_ms([a.elapsed_time(b) for a, b in times])
+    pool.close()
+    return {"tokens": int(lens.sum()), "dtype": "f32",
+            "decode_op_us_median": 1e3 * us["median"],
+            "decode_op_us_p10": 1e3 * us["p10"],
+            "decode_op_us_p90": 1e3 * us["p90"]}
+
+
 def run_swap(w, device, n_blocks: int = 2048, reps: int = 5):
     """Swap of n_blocks blocks of the workload's pool shape (K and V) out to a
     pinned host pool and back in (kv_swap_blocks), timed with events: the
@@ -901,7 +947,7 @@ def main() -> int:
     headroom = wd.num_seqs * (-(-(args.steps + args.warmup +
                                   APPEND_TIMING_STEPS) // wd.block_size)
                               + 1)
-    paged = contig = inp = cow = plain = vattn = swap = fp8 = None
+    paged = contig = inp = cow = plain = vattn = swap = fp8 = tiny = None
     if not args.no_decode:
         log(f"drawing {wd.name}")
         inp = W.draw(wd, lambda L: pool_blocks(kv, wd, L, headroom))
@@ -942,6 +988,8 @@ def main() -> int:
         if default_workload:
             log("block swap to pinned host memory and back")
             swap = run_swap(wd, device)
+            log("small fp32 decode (latency)")
+            tiny = run_tiny_decode(device)
 
     prefill = None
     if not args.no_prefill and (default_workload or args.no_decode):
@@ -1045,6 +1093,8 @@ def main() -> int:
         line["copy_on_write"] = rounded(cow)
     if swap:
         line["block_swap"] = rounded(swap)
+    if tiny:
+        line["decode_tiny_f32"] = rounded(tiny)
     if prefill:
         line["prefill"] = {k: {kk: round(vv, 4) for kk, vv in v.items()}
                            for k, v in prefill.items()}

@@ -649,8 +649,13 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 
 // ---------------------------------------------------------------------------
 // Generic path: one wave per (query head, sequence); lanes over head_dim
-// (<= 256); one token at a time with an online softmax.
+// (<= 256); an online softmax over the tokens in order. The loads of
+// kGenTokens tokens (table entries, then their K and V rows) are issued
+// together, so the loop waits on memory once per group rather than twice
+// per token; tokens past the context re-read the last one and are skipped.
 // ---------------------------------------------------------------------------
+constexpr int kGenTokens = 8;
+
 template <typename T, bool PAGED>
 __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
   const int h = blockIdx.x;
@@ -668,36 +673,47 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
     acc[i] = 0.f;
   }
   float m_run = -INFINITY, l = 0.f;
-  for (int p = 0; p < ctx; ++p) {
-    int64_t row;  // head row of (token p, KV head g)
-    if (PAGED) {
-      int b = a.bt[(int64_t)s * a.bt_stride + p / a.block_size];
-      b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      row = ((int64_t)b * a.hkv + g) * a.block_size + p % a.block_size;
-    } else {
-      row = ((int64_t)s * a.hkv + g) * a.seq_stride + p;
-    }
-    const T* kp = (const T*)a.k + row * D;
-    const T* vp = (const T*)a.v + row * D;
-    float dot = 0.f;
+  for (int p0 = 0; p0 < ctx; p0 += kGenTokens) {
+    float kk[kGenTokens][4], vv[kGenTokens][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = lane + kWave * i;
-      if (d < D) dot += qv[i] * to_f32<T>(kp[d]);
-    }
-    dot = wave_sum(dot);
-    const float x = dot * a.scale_log2;
-    const float m_new = fmaxf(m_run, x);
-    const float alpha = fast_exp2(m_run - m_new);
-    const float pr = fast_exp2(x - m_new);
-    l = l * alpha + pr;
+    for (int t = 0; t < kGenTokens; ++t) {
+      const int p = min(p0 + t, ctx - 1);
+      int64_t row;  // head row of (token p, KV head g)
+      if (PAGED) {
+        int b = a.bt[(int64_t)s * a.bt_stride + p / a.block_size];
+        b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+        row = ((int64_t)b * a.hkv + g) * a.block_size + p % a.block_size;
+      } else {
+        row = ((int64_t)s * a.hkv + g) * a.seq_stride + p;
+      }
+      const T* kp = (const T*)a.k + row * D;
+      const T* vp = (const T*)a.v + row * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = lane + kWave * i;
-      const float vv = d < D ? to_f32<T>(vp[d]) : 0.f;
-      acc[i] = acc[i] * alpha + pr * vv;
+      for (int i = 0; i < 4; ++i) {
+        const int d = lane + kWave * i;
+        kk[t][i] = d < D ? to_f32<T>(kp[d]) : 0.f;
+        vv[t][i] = d < D ? to_f32<T>(vp[d]) : 0.f;
+      }
     }
-    m_run = m_new;
+    float x[kGenTokens];
+#pragma unroll
+    for (int t = 0; t < kGenTokens; ++t) {
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dot += qv[i] * kk[t][i];
+      x[t] = wave_sum(dot) * a.scale_log2;
+    }
+#pragma unroll
+    for (int t = 0; t < kGenTokens; ++t) {
+      if (p0 + t >= ctx) break;  // wave-uniform
+      const float m_new = fmaxf(m_run, x[t]);
+      const float alpha = fast_exp2(m_run - m_new);
+      const float pr = fast_exp2(x[t] - m_new);
+      l = l * alpha + pr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = acc[i] * alpha + pr * vv[t][i];
+      m_run = m_new;
+    }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   T* op = (T*)a.out + ((int64_t)s * a.hq + h) * D;
