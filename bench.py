@@ -305,8 +305,9 @@ class DecodeReplica:
         else:
             self.a_table = torch.arange(S, dtype=torch.int32,
                                         device=device).view(S, 1)
-        # the pinned buffers are rewritten only after the last GPU work that
-        # read them is done
+        # The pinned block-id buffer is rewritten only after the append that
+        # read it has run: `uploaded` is an event recorded after that append
+        # (the decode op's start event in a step).
         self.uploaded = torch.cuda.Event()
         self.uploaded.record()
         self.scale = 1.0 / float(np.sqrt(w.head_dim))
@@ -344,9 +345,10 @@ class DecodeReplica:
         if self.vmm:
             self.vc.close()
 
-    def cache_write(self) -> None:
-        """Device part of the append: the new token's row in the cache (and,
-        on the append path, the table entry and length on the device)."""
+    def cache_write(self, done=None) -> None:
+        """Device part of the append: the new token's row in the cache, the
+        table entry and the length on the device. `done` (an event, default
+        a new one) is recorded after it and marks the pinned buffer free."""
         kv = self.kv
         if self.fp8:
             kv.kv_append_token_fp8(self.new_k, self.new_v, self.h_newb,
@@ -355,15 +357,15 @@ class DecodeReplica:
         else:
             kv.kv_append_token(self.new_k, self.new_v, self.h_newb,
                                self.a_table, self.d_lens, self.k, self.v)
+        self.uploaded = done if done is not None else self.torch.cuda.Event()
         self.uploaded.record()
 
     def device_step(self, ev=None) -> None:
-        """Cache write, then the decode op, bracketed by ev[0], ev[1]."""
+        """Cache write, then the decode op, bracketed by ev[0], ev[1]; ev[0]
+        also marks the end of the cache write."""
         kv = self.kv
-        self.cache_write()
+        self.cache_write(ev[0] if ev is not None else None)
         max_ctx = int(self.h_lens.max())
-        if ev is not None:
-            ev[0].record()
         if self.fp8:
             kv.paged_attn_decode_fp8(self.out, self.q, self.k, self.v,
                                      self.d_table, self.d_lens, max_ctx,
@@ -440,8 +442,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         e = tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
         torch.cuda._sleep(SPIN_CYCLES)
         e[0].record()
-        r.cache_write()
-        e[1].record()
+        r.cache_write(e[1])
         rc_ev.append(e)
     torch.cuda.synchronize()
     rc = stats_ms([a.elapsed_time(b) for a, b in rc_ev])
