@@ -80,6 +80,12 @@ kv_status hip_fail(const char* what, hipError_t e) {
 // back to the pool.
 kv_status unmap_tail(kv_vcache* c, int32_t s, int32_t keep) {
   const int32_t have = c->pages[s];
+  if (have <= keep) return KV_OK;
+  try {  // room in the pool for every handle unmapped below
+    c->pool.reserve(c->pool.size() + (size_t)(have - keep) * 2 * c->hkv);
+  } catch (const std::bad_alloc&) {
+    return kvp_fail(KV_ENOMEM, "kv_vcache: host allocation");
+  }
   for (int t = 0; t < 2; ++t)
     for (int32_t g = 0; g < c->hkv; ++g)
       for (int32_t p = keep; p < have; ++p) {
@@ -227,7 +233,18 @@ kv_status map_upto(kv_vcache* c, int32_t seq, int32_t want,
     char* va;
     hipMemGenericAllocationHandle_t h;
   };
+  // Host storage for every page this call may map, and for returning them
+  // to the pool, is reserved first: nothing below can throw (this also runs
+  // on the mapping thread, where an escaping exception would end the
+  // process).
+  const size_t n_map = (size_t)(want - have) * 2 * c->hkv;
   std::vector<Done> done;
+  try {
+    done.reserve(n_map);
+    c->pool.reserve(c->pool.size() + n_map);
+  } catch (const std::bad_alloc&) {
+    return kvp_fail(KV_ENOMEM, "kv_vcache: host allocation");
+  }
   kv_status st = KV_OK;
   for (int32_t p = have; p < want && st == KV_OK; ++p)
     for (int t = 0; t < 2 && st == KV_OK; ++t)
@@ -295,7 +312,11 @@ void worker_main(kv_vcache* c) {
     const kv_status st = map_upto(c, r.first, pages_for(c, r.second), nullptr);
     if (st != KV_OK && c->async_status == KV_OK) {
       c->async_status = st;
-      c->async_msg = kv_last_error();
+      try {
+        c->async_msg = kv_last_error();
+      } catch (...) {
+        c->async_msg.clear();  // the status alone is reported
+      }
     }
     c->busy = false;
     c->cv.notify_all();
