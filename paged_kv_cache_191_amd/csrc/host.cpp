@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <new>
+#include <algorithm>
 #include <vector>
 
 #include "kvpaged_internal.h"
@@ -75,10 +76,16 @@ extern "C" kv_status kv_pool_create(int32_t num_blocks, int32_t block_size,
   p->block_size = block_size;
   p->head = 0;
   p->count = num_blocks;
-  p->ring.assign(num_blocks, 0);
-  p->rc.assign(num_blocks, 0);
+  std::vector<char> seen;
+  try {
+    p->ring.assign(num_blocks, 0);
+    p->rc.assign(num_blocks, 0);
+    if (init_free_order) seen.assign(num_blocks, 0);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return kvp_fail(KV_ENOMEM, "kv_pool_create: host allocation failed");
+  }
   if (init_free_order) {
-    std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
       int32_t b = init_free_order[i];
       if (b < 0 || b >= num_blocks || seen[b]) {
@@ -123,7 +130,12 @@ extern "C" kv_status kv_block_free(kv_pool* pool, int32_t n,
       return kvp_fail(KV_EINVAL, "kv_block_free: id %d outside the pool",
                       ids[i]);
   // An id may repeat: check the total drop per id before changing anything.
-  std::vector<int32_t> drop(pool->num_blocks, 0);
+  std::vector<int32_t> drop;
+  try {
+    drop.assign(pool->num_blocks, 0);
+  } catch (const std::bad_alloc&) {
+    return kvp_fail(KV_ENOMEM, "kv_block_free: host allocation failed");
+  }
   for (int32_t i = 0; i < n; ++i) ++drop[ids[i]];
   for (int32_t i = 0; i < n; ++i)
     if (drop[ids[i]] > pool->rc[ids[i]])
@@ -232,6 +244,20 @@ extern "C" kv_status kv_seq_append(kv_pool* pool, int32_t* block_tables,
   // entries in reverse.
   const int32_t saved_head = pool->head, saved_count = pool->count;
   std::vector<TableEdit> edits, rc_edits;
+  // Room for every undo record first, so that nothing below can throw: a
+  // sequence takes at most add / B + 1 new blocks (one table and one
+  // refcount record each) and copies at most one shared block (one table
+  // and two refcount records).
+  {
+    const int64_t fresh = std::min<int64_t>(pool->count, total / B + num_seqs);
+    const int64_t cows = std::min<int64_t>(cow_capacity, num_seqs);
+    try {
+      edits.reserve((size_t)(fresh + cows));
+      rc_edits.reserve((size_t)(fresh + 2 * cows));
+    } catch (const std::bad_alloc&) {
+      return kvp_fail(KV_ENOMEM, "kv_seq_append: host allocation failed");
+    }
+  }
   auto set_rc = [&](int32_t b, int32_t v) {
     rc_edits.push_back({&pool->rc[b], pool->rc[b]});
     pool->rc[b] = v;

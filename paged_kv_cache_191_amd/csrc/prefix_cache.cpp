@@ -157,7 +157,12 @@ extern "C" kv_status kv_prefix_cache_lookup(kv_prefix_cache* c,
   } catch (const std::bad_alloc&) {
     return kvp_fail(KV_ENOMEM, "kv_prefix_cache_lookup: host allocation");
   }
-  std::vector<int32_t> ids(found.size());
+  std::vector<int32_t> ids;
+  try {
+    ids.resize(found.size());
+  } catch (const std::bad_alloc&) {
+    return kvp_fail(KV_ENOMEM, "kv_prefix_cache_lookup: host allocation");
+  }
   for (size_t i = 0; i < found.size(); ++i) ids[i] = found[i]->block;
   if (!ids.empty()) {
     const kv_status st = kv_block_share(c->pool, (int32_t)ids.size(),
@@ -233,9 +238,14 @@ extern "C" int32_t kv_prefix_cache_evict(kv_prefix_cache* c, int32_t n,
     return -1;
   }
   std::vector<std::pair<uint64_t, uint64_t>> cands;  // (last_use, key)
-  for (auto& kvp : c->entries)
-    if (kv_block_refcount(c->pool, kvp.second.block) == 1)
-      cands.push_back({kvp.second.last_use, kvp.first});
+  try {
+    for (auto& kvp : c->entries)
+      if (kv_block_refcount(c->pool, kvp.second.block) == 1)
+        cands.push_back({kvp.second.last_use, kvp.first});
+  } catch (const std::bad_alloc&) {
+    kvp_fail(KV_ENOMEM, "kv_prefix_cache_evict: host allocation");
+    return -1;
+  }
   std::sort(cands.begin(), cands.end());
   int32_t done = 0;
   for (size_t i = 0; i < cands.size() && done < n; ++i) {
