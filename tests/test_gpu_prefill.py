@@ -174,6 +174,41 @@ def test_prefill_full_size_sampled(name, layout):
         assert np.isfinite(got).all()
 
 
+@pytest.mark.parametrize("chunks", [(1, 2, 3, 4, 5, 6),
+                                    (8, 9, 10, 11, 12, 13, 14)])
+def test_prefill_full_size_every_chunk(chunks):
+    # The same Yi-6B-shaped workload, paged B = 16: the 13 chunks the test
+    # above leaves out, 256 whole rows each (every sequence's first and last
+    # row of the chunk, block boundaries, the rest seeded), so that every
+    # chunk of the pass is checked against the oracle. Two halves keep each
+    # test's CPU oracle time short.
+    name = "yi6b_chunked_prefill_b16"
+    w = W.WORKLOADS[name]
+    _log(f"drawing {name}")
+    inp = _draw(w)
+    B = w.block_size
+    total = int(inp.lengths.max())
+    nat = H.build_native(inp, B, H.tables_capacity(total, B))
+    orc = H.build_oracle(inp, B)
+    C = w.chunk
+    assert max(chunks) < total // C
+    for ci in chunks:
+        qrows, cu, start, ctx = _chunk_meta(inp, ci * C, C)
+        got = _run_prefill(inp, "paged", nat, None, None, qrows, cu, start,
+                           ctx)
+        must = ([int(x) for x in cu[:-1]] + [int(x) - 1 for x in cu[1:]] +
+                [15, 16, 63, 64, 65, C + 15, C + 16])
+        sample = W.sample_rows(100 + ci, len(qrows), 256, must)
+        q_all = inp.q[torch.from_numpy(qrows)].float().numpy()
+        want = O.prefill_paged(q_all, cu, start, orc.k_pool, orc.v_pool,
+                               orc.tables, ctx, H.scale_of(w), True,
+                               rows=sample)
+        err = H.max_abs(got[sample], want[sample])
+        _log(f"{name} chunk {ci}: {len(sample)} rows, max-abs {err:.3e}")
+        assert err <= H.tolerance(w), (ci, err)
+        assert np.isfinite(got).all()
+
+
 def test_prefill_repeat_is_bit_identical():
     w = W.WORKLOADS["yi6b_chunked_prefill_b16"].replace(
         num_seqs=2, lengths=(500, 333), name="prefill_repeat")
