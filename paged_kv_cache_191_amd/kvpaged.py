@@ -390,6 +390,41 @@ def _dev(t, name: str, dtype=None):
     return t.data_ptr()
 
 
+def _ndim(t, n: int, name: str) -> None:
+    if len(t.shape) != n:
+        raise ValueError(f"{name} must have {n} dimensions, has shape "
+                         f"{tuple(t.shape)}")
+
+
+def _rows(t, n: int, name: str) -> None:
+    """t holds at least n rows (entries of its first dimension): the
+    kernels index rows 0..n-1 of it without a bound they could check."""
+    if len(t.shape) < 1 or t.shape[0] < n:
+        raise ValueError(f"{name} needs at least {n} rows, has shape "
+                         f"{tuple(t.shape)}")
+
+
+def _same(a, b, an: str, bn: str) -> None:
+    if tuple(a.shape) != tuple(b.shape):
+        raise ValueError(f"{an} {tuple(a.shape)} and {bn} {tuple(b.shape)} "
+                         "differ in shape")
+
+
+def _attn_shapes(out, q, k, v, head_dim_of_k: int, S: int,
+                 per_seq=()) -> None:
+    """Shape agreement the attention kernels assume: out like q, V like K,
+    one head_dim, and one row per sequence in every per-sequence input."""
+    _ndim(q, 3, "q")
+    _same(out, q, "out", "q")
+    _ndim(k, 4, "k cache")
+    _same(v, k, "v cache", "k cache")
+    if head_dim_of_k != q.shape[2]:
+        raise ValueError(f"head_dim of q ({q.shape[2]}) and of the cache "
+                         f"({head_dim_of_k}) differ")
+    for t, name in per_seq:
+        _rows(t, S, name)
+
+
 def _stream(stream=None):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -404,6 +439,10 @@ def kv_reshape_and_cache(k, v, slots, k_cache, v_cache, stream=None) -> None:
     nb, chkv, bs, cd = k_cache.shape
     if (chkv, cd) != (hkv, d):
         raise ValueError("cache and rows disagree on Hkv or head_dim")
+    _same(v, k, "v", "k")
+    _same(v_cache, k_cache, "v_cache", "k_cache")
+    _ndim(slots, 1, "slots")
+    _rows(slots, n, "slots")
     st = lib().kv_reshape_and_cache(
         _dev(k, "k"), _dev(v, "v", k.dtype), _dev(slots, "slots", torch.int64),
         n, _dev(k_cache, "k_cache", k.dtype), _dev(v_cache, "v_cache", k.dtype),
@@ -429,6 +468,9 @@ def kv_reshape_and_cache_fp8(k, v, slots, k_cache, v_cache, k_scale: float,
     nb, chkv, bs, cd = k_cache.shape
     if (chkv, cd) != (hkv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("caches and rows disagree on shape")
+    _same(v, k, "v", "k")
+    _ndim(slots, 1, "slots")
+    _rows(slots, n, "slots")
     st = lib().kv_reshape_and_cache_fp8(
         _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
         _dev(slots, "slots", torch.int64), n, _fp8_cache(k_cache, "k_cache"),
@@ -440,6 +482,9 @@ def kv_reshape_and_cache_fp8(k, v, slots, k_cache, v_cache, k_scale: float,
 def kv_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
     torch = _torch()
     nb, hkv, bs, d = k_cache.shape
+    _same(v_cache, k_cache, "v_cache", "k_cache")
+    if len(src_dst.shape) != 2 or src_dst.shape[1] != 2:
+        raise ValueError("src_dst must be [n, 2]")
     st = lib().kv_copy_blocks(
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
         _dev(src_dst, "src_dst", torch.int32), src_dst.shape[0], nb, bs, hkv,
@@ -467,6 +512,9 @@ def kv_append_token(k, v, new_blocks, block_tables, context_lens, k_cache,
                          "row per sequence")
     if not new_blocks.is_contiguous() or new_blocks.dtype != torch.int32:
         raise ValueError("new_blocks must be a contiguous int32 tensor")
+    _ndim(new_blocks, 1, "new_blocks")
+    _ndim(block_tables, 2, "block_tables")
+    _ndim(context_lens, 1, "context_lens")
     st = lib().kv_append_token(
         _dev(k, "k"), _dev(v, "v", k.dtype), new_blocks.data_ptr(),
         _dev(block_tables, "block_tables", torch.int32),
@@ -494,6 +542,9 @@ def kv_append_token_fp8(k, v, new_blocks, block_tables, context_lens,
                          "row per sequence")
     if not new_blocks.is_contiguous() or new_blocks.dtype != torch.int32:
         raise ValueError("new_blocks must be a contiguous int32 tensor")
+    _ndim(new_blocks, 1, "new_blocks")
+    _ndim(block_tables, 2, "block_tables")
+    _ndim(context_lens, 1, "context_lens")
     st = lib().kv_append_token_fp8(
         _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
         new_blocks.data_ptr(), _dev(block_tables, "block_tables", torch.int32),
@@ -510,6 +561,10 @@ def kv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:
     db = dst_k.shape[0]
     if tuple(dst_k.shape[1:]) != (hkv, bs, d):
         raise ValueError("the pools differ in Hkv, block_size or head_dim")
+    _same(src_v, src_k, "src_v", "src_k")
+    _same(dst_v, dst_k, "dst_v", "dst_k")
+    if len(pairs.shape) != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
     for t, name in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"),
                     (dst_v, "dst_v"), (pairs, "pairs")):
         if not t.is_contiguous():
@@ -552,7 +607,11 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                       stream=None) -> None:
     torch = _torch()
     S, hq, d = q.shape
-    nb, hkv, bs, _ = k_cache.shape
+    nb, hkv, bs, dk = k_cache.shape
+    _attn_shapes(out, q, k_cache, v_cache, dk, S,
+                 ((block_tables, "block_tables"),
+                  (context_lens, "context_lens")))
+    _ndim(block_tables, 2, "block_tables")
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
     st = lib().paged_attn_decode(
@@ -572,7 +631,11 @@ def paged_attn_decode_fp8(out, q, k_cache, v_cache, block_tables,
     """paged_attn_decode over fp8 E4M3 caches; q, out bf16."""
     torch = _torch()
     S, hq, d = q.shape
-    nb, hkv, bs, _ = k_cache.shape
+    nb, hkv, bs, dk = k_cache.shape
+    _attn_shapes(out, q, k_cache, v_cache, dk, S,
+                 ((block_tables, "block_tables"),
+                  (context_lens, "context_lens")))
+    _ndim(block_tables, 2, "block_tables")
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
     st = lib().paged_attn_decode_fp8(
@@ -592,7 +655,9 @@ def contig_attn_decode_fp8(out, q, k, v, context_lens, max_context: int,
     """contig_attn_decode over fp8 E4M3 caches [S, Hkv, Lmax, D]."""
     torch = _torch()
     S, hq, d = q.shape
-    _, hkv, lmax, _ = k.shape
+    _, hkv, lmax, dk = k.shape
+    _attn_shapes(out, q, k, v, dk, S,
+                 ((k, "k"), (context_lens, "context_lens")))
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
     st = lib().contig_attn_decode_fp8(
@@ -632,7 +697,11 @@ def paged_attn_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
     """group_starts: device int32 [G + 1]; shared_lens: device int32 [G]."""
     torch = _torch()
     S, hq, d = q.shape
-    nb, hkv, bs, _ = k_cache.shape
+    nb, hkv, bs, dk = k_cache.shape
+    _attn_shapes(out, q, k_cache, v_cache, dk, S,
+                 ((block_tables, "block_tables"),
+                  (context_lens, "context_lens")))
+    _ndim(block_tables, 2, "block_tables")
     G = shared_lens.shape[0]
     if group_starts.shape[0] != G + 1:
         raise ValueError("group_starts must have num_groups + 1 entries")
@@ -657,7 +726,9 @@ def contig_attn_decode(out, q, k, v, context_lens, max_context: int,
                        scale: float, workspace=None, stream=None) -> None:
     torch = _torch()
     S, hq, d = q.shape
-    _, hkv, lmax, _ = k.shape
+    _, hkv, lmax, dk = k.shape
+    _attn_shapes(out, q, k, v, dk, S,
+                 ((k, "k"), (context_lens, "context_lens")))
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
     st = lib().contig_attn_decode(
@@ -674,8 +745,14 @@ def paged_attn_prefill(out, q, cu_q_lens, q_start_pos, max_q_len: int,
                        scale: float, causal: bool = True, stream=None) -> None:
     torch = _torch()
     T, hq, d = q.shape
-    nb, hkv, bs, _ = k_cache.shape
+    nb, hkv, bs, dk = k_cache.shape
+    _ndim(cu_q_lens, 1, "cu_q_lens")
     S = cu_q_lens.shape[0] - 1
+    _attn_shapes(out, q, k_cache, v_cache, dk, S,
+                 ((block_tables, "block_tables"),
+                  (context_lens, "context_lens"),
+                  (q_start_pos, "q_start_pos")))
+    _ndim(block_tables, 2, "block_tables")
     st = lib().paged_attn_prefill(
         _dev(out, "out", q.dtype), _dev(q, "q"),
         _dev(cu_q_lens, "cu_q_lens", torch.int32),
@@ -693,10 +770,12 @@ def contig_attn_prefill(out, q, cu_q_lens, q_start_pos, max_q_len: int, k, v,
                         stream=None) -> None:
     torch = _torch()
     T, hq, d = q.shape
+    _ndim(cu_q_lens, 1, "cu_q_lens")
     S = cu_q_lens.shape[0] - 1
-    _, hkv, lmax, _ = k.shape
-    if k.shape[0] < S:
-        raise ValueError("k holds fewer sequences than cu_q_lens describes")
+    _, hkv, lmax, dk = k.shape
+    _attn_shapes(out, q, k, v, dk, S,
+                 ((k, "k"), (context_lens, "context_lens"),
+                  (q_start_pos, "q_start_pos")))
     st = lib().contig_attn_prefill(
         _dev(out, "out", q.dtype), _dev(q, "q"),
         _dev(cu_q_lens, "cu_q_lens", torch.int32),
