@@ -293,8 +293,12 @@ kv_status paged_attn_decode_shared_prefix(
  * context_lens[s] tokens already in the cache (including this chunk's
  * own K/V). With causal != 0 a query at position p sees keys 0..p (and
  * < context_lens[s]); otherwise all context keys. max_q_len bounds every
- * sequence's query count. cu_q_lens, q_start_pos and context_lens are
- * device int32 arrays. [The prefill kernels the vAttention newsletter
+ * sequence's query count (the grid covers max_q_len rows per sequence; the
+ * rows of a sequence with more queries are left unspecified). cu_q_lens,
+ * q_start_pos and context_lens are device int32 arrays, read by the kernel
+ * without a bound it could check: cu_q_lens starts at 0 and does not
+ * decrease, and q and out hold cu_q_lens[num_seqs] rows of
+ * [num_q_heads, head_dim]. [The prefill kernels the vAttention newsletter
  * compares in "İddia ve Gerçeklik".] */
 kv_status paged_attn_prefill(void* out, const void* q,
                              const int32_t* cu_q_lens,
