@@ -287,3 +287,41 @@ def test_decode_fp8_errors():
     with pytest.raises(kv.KVError, match="UNSUPPORTED"):
         kv.paged_attn_decode_fp8(torch.empty_like(q64), q64, kc64, kc64, bt,
                                  ctx, 1, 0.1, 1.0, 1.0)
+
+
+def _fp8_shape(seed):
+    g = np.random.default_rng([3000, seed])
+    hkv = int(g.choice([1, 2, 4, 8]))
+    group = (1, 2, 4, 7, 8, 16, 20, 5)[seed % 8]    # each size once
+    S = int(g.integers(2, 33))
+    lens = g.integers(1, int(g.integers(2, 1500)), size=S, endpoint=True)
+    if seed % 2 == 0:
+        lens[S // 2] = 0                           # an empty context
+    spec = dict(num_seqs=S, num_kv_heads=hkv, num_q_heads=hkv * group,
+                head_dim=128, block_size=(16, 32, 48, 64)[seed % 4],
+                lengths=tuple(int(x) for x in lens), length_range=None)
+    scales = tuple(float(np.float32(x)) for x in g.uniform(0.012, 0.05, 2))
+    return spec, scales
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_fp8_random_shapes(seed):
+    """Seeded random shapes over fp8 caches: batch size, KV heads, head
+    groups that fill one or two MFMA column blocks, block sizes, context
+    lengths (empty ones included) and per-tensor scales; paged and
+    contiguous against the oracle on the dequantised codes."""
+    spec, (ks, vs) = _fp8_shape(seed)
+    w = W.WORKLOADS["llama3_8b_decode"].replace(name=f"fp8_rand_{seed}",
+                                               seed=3000 + seed, **spec)
+    inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens))
+    ctx = W.context_lengths(inp)
+    cap = H.tables_capacity(int(ctx.max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    kc, vc = _fill_fp8(inp, nat, ks, vs)
+    kp, vp = _oracle_codes(inp, orc, ks, vs)
+    outs, want = _decode_fp8_both(inp, nat, orc, kc, vc, kp, vp, ks, vs)
+    _log(f"{w.name} {spec} scales {ks:.4f} {vs:.4f} contexts "
+         f"{int(ctx.min())}..{int(ctx.max())}")
+    _check(outs, want, w.name)
+    assert np.array_equal(outs["paged"], outs["contig"])
