@@ -1,9 +1,10 @@
 """GPU parity on seeded random shapes, through the C ABI: paged and
-contiguous decode, and paged chunked prefill (causal and not), against the
-fp64 oracle. Each seed draws the batch size, head grouping, head_dim, block
-size, dtype and context lengths, so the fast (MFMA) and generic paths, block
-sizes that are and are not powers of two, GQA groups that fill one or two
-MFMA column blocks, and empty contexts are all covered."""
+contiguous decode, and paged and contiguous chunked prefill (causal and
+not), against the fp64 oracle. Each seed draws the batch size, head
+grouping, head_dim, block size, dtype and context lengths, so the fast
+(MFMA) and generic paths, block sizes that are and are not powers of two,
+GQA groups that fill one or two MFMA column blocks, and empty contexts are
+all covered."""
 import sys
 
 import numpy as np
@@ -111,11 +112,19 @@ def test_prefill_random_shapes(seed):
                           nat.k_cache, nat.v_cache, nat.bt,
                           torch.from_numpy(lens).cuda(), H.scale_of(w),
                           causal)
+    # the contiguous layout of the same data (unused tail rows NaN)
+    kc, vc = H.contig_from_inputs(inp, int(lens.max()))
+    oc = torch.full_like(q, float("nan"))
+    kv.contig_attn_prefill(oc, q, torch.from_numpy(cu).cuda(),
+                           torch.from_numpy(start).cuda(), int(nq.max()), kc,
+                           vc, torch.from_numpy(lens).cuda(), H.scale_of(w),
+                           causal)
     torch.cuda.synchronize()
     want = O.prefill_paged(inp.q[torch.from_numpy(rows)].float().numpy(), cu,
                            start, orc.k_pool, orc.v_pool, orc.tables, lens,
                            H.scale_of(w), causal)
-    err = H.max_abs(out.float().cpu().numpy(), want)
-    _log(f"{w.name} {spec} causal={causal} q={nq.tolist()}: max-abs "
-         f"{err:.2e}")
-    assert err <= H.tolerance(w), err
+    for name, got in (("paged", out), ("contig", oc)):
+        err = H.max_abs(got.float().cpu().numpy(), want)
+        _log(f"{w.name} {spec} causal={causal} q={nq.tolist()} {name}: "
+             f"max-abs {err:.2e}")
+        assert err <= H.tolerance(w), (name, err)
