@@ -140,6 +140,36 @@ def test_mixed_groups(B, hq, hkv):
     assert max_abs(run_plain(b, scale), want) <= TOL
 
 
+def _random_groups(seed):
+    g = np.random.default_rng([4000, seed])
+    groups = []
+    for _ in range(int(g.integers(1, 7))):
+        m = int(g.choice([1, 2, 3, 8, 17, 40]))
+        P = int(g.integers(0, 700))
+        own = [int(x) for x in g.integers(0, 300, size=m)]
+        groups.append((m, P, own, None))
+    B = (16, 32, 48, 64)[seed % 4]
+    hkv = int(g.choice([1, 2, 8]))
+    return groups, B, hkv * (4, 8, 16)[seed % 3], hkv
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_groups(seed):
+    """Seeded random group layouts: group count and sizes, prefix and own
+    lengths (empty ones included), block sizes that are and are not powers
+    of two, head groups of 4, 8 and 16."""
+    groups, B, hq, hkv = _random_groups(seed)
+    b = build_groups(groups, B, hq, hkv, seed=4100 + seed)
+    scale = 1.0 / np.sqrt(128)
+    want = expect(b, scale)
+    err = max_abs(run_shared(b, scale), want)
+    print(f"random groups {seed}: B={B} {hq}/{hkv} "
+          f"{[(m, P) for m, P, _, _ in groups]}: max-abs {err:.2e}",
+          flush=True)
+    assert err <= TOL
+    assert max_abs(run_plain(b, scale), want) <= TOL
+
+
 def test_one_big_group_long_prefix():
     own = list(np.random.default_rng(5).integers(0, 300, size=70))
     own[3] = 0
