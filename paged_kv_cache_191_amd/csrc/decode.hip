@@ -648,19 +648,27 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Generic path: one wave per (query head, sequence); lanes over head_dim
-// (<= 256); an online softmax over the tokens in order. The loads of
-// kGenTokens tokens (table entries, then their K and V rows) are issued
-// together, so the loop waits on memory once per group rather than twice
-// per token; tokens past the context re-read the last one and are skipped.
+// Generic path: one workgroup of kGenWaves waves per (query head, sequence);
+// lanes over head_dim (<= 256). The tokens are taken in groups of
+// kGenTokens, group j by wave j % kGenWaves, each wave with its own online
+// softmax; the waves' (max, sum, output) are then merged exactly through
+// LDS. The loads of a group (table entries, then their K and V rows) are
+// issued together, so a wave waits on memory once per group rather than
+// twice per token; tokens past the context re-read the last one and are
+// skipped.
 // ---------------------------------------------------------------------------
 constexpr int kGenTokens = 8;
+constexpr int kGenWaves = 8;
 
 template <typename T, bool PAGED>
-__global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kGenWaves * kWave) void decode_generic_kernel(
+    DecodeArgs a) {
+  __shared__ float sm_acc[kGenWaves][4][kWave];
+  __shared__ float sm_ml[kGenWaves][2];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = h / a.group;
   const int D = a.head_dim;
   const int ctx = clamp_ctx(a, s, PAGED);
@@ -673,7 +681,7 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
     acc[i] = 0.f;
   }
   float m_run = -INFINITY, l = 0.f;
-  for (int p0 = 0; p0 < ctx; p0 += kGenTokens) {
+  for (int p0 = kGenTokens * w; p0 < ctx; p0 += kGenTokens * kGenWaves) {
     float kk[kGenTokens][4], vv[kGenTokens][4];
 #pragma unroll
     for (int t = 0; t < kGenTokens; ++t) {
@@ -715,12 +723,33 @@ __global__ __launch_bounds__(kWave) void decode_generic_kernel(DecodeArgs a) {
       m_run = m_new;
     }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  // exact merge of the waves: o = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w
+  if (lane == 0) {
+    sm_ml[w][0] = m_run;
+    sm_ml[w][1] = l;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sm_acc[w][i][lane] = acc[i];
+  __syncthreads();
+  if (w != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int ww = 0; ww < kGenWaves; ++ww) M = fmaxf(M, sm_ml[ww][0]);
+  float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ww = 0; ww < kGenWaves; ++ww) {
+    const float mw = sm_ml[ww][0];
+    const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+    L += f * sm_ml[ww][1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] += f * sm_acc[ww][i][lane];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   T* op = (T*)a.out + ((int64_t)s * a.hq + h) * D;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int d = lane + kWave * i;
-    if (d < D) op[d] = from_f32<T>(acc[i] * inv);
+    if (d < D) op[d] = from_f32<T>(o[i] * inv);
   }
 }
 
@@ -866,14 +895,14 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
   dim3 grid(a.hq, a.num_seqs);
   if (dtype == KV_F32) {
     if (paged)
-      decode_generic_kernel<float, true><<<grid, kWave, 0, st>>>(a);
+      decode_generic_kernel<float, true><<<grid, kGenWaves * kWave, 0, st>>>(a);
     else
-      decode_generic_kernel<float, false><<<grid, kWave, 0, st>>>(a);
+      decode_generic_kernel<float, false><<<grid, kGenWaves * kWave, 0, st>>>(a);
   } else {
     if (paged)
-      decode_generic_kernel<bf16, true><<<grid, kWave, 0, st>>>(a);
+      decode_generic_kernel<bf16, true><<<grid, kGenWaves * kWave, 0, st>>>(a);
     else
-      decode_generic_kernel<bf16, false><<<grid, kWave, 0, st>>>(a);
+      decode_generic_kernel<bf16, false><<<grid, kGenWaves * kWave, 0, st>>>(a);
   }
   KVP_LAUNCH_CHECK(name);
   return KV_OK;
