@@ -213,18 +213,30 @@ kv_status kv_copy_blocks(void* k_cache, void* v_cache,
  * KV head, the tokens of all sequences are laid end to end and cut into
  * kv_decode_chunks() equal chunks, one workgroup each; a sequence cut by a
  * chunk boundary leaves partial softmax results that a second kernel merges
- * exactly. The workspace holds those partials;
- * kv_decode_workspace_bytes() gives the size needed (0 when the kernel for
- * the shape needs none). max_context bounds every context_lens[s] (larger
- * values are clamped to it, and to bt_stride * block_size for the paged
- * layout). Table entries outside [0, num_blocks) are clamped into range,
- * which keeps memory accesses in bounds but makes that output meaningless.
- * context_lens[s] == 0 gives a zero output row. Calls sharing one
- * workspace must be ordered (same stream). */
+ * exactly. The workspace (device memory, caller-owned, at least
+ * kv_decode_workspace_bytes() bytes; never NULL for num_seqs > 0) starts
+ * with a 256-byte header, followed, for head_dim 128, by those partials
+ * (an fp32 call uses the header only). max_context bounds every
+ * context_lens[s]: a value outside [0, max_context] (or beyond the table's
+ * bt_stride * block_size tokens, or the contiguous seq_stride) is clamped
+ * into range, which keeps memory accesses in bounds, and the number of
+ * sequences clamped in the call is stored in the header;
+ * kv_decode_clamped_count() reads it, so a stale bound is visible rather
+ * than silently shortening the attention. Table entries outside
+ * [0, num_blocks) are clamped into range (not counted), which keeps memory
+ * accesses in bounds but makes that output meaningless. context_lens[s] ==
+ * 0 gives a zero output row. Calls sharing one workspace must be ordered
+ * (same stream). */
 int32_t kv_decode_chunks(int32_t num_q_heads, int32_t num_kv_heads);
 size_t kv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_context);
+
+/* Number of sequences whose context_lens entry the last decode call on this
+ * workspace clamped (see above): waits for `stream`, then copies the count
+ * from the workspace header into *count. KV_EHIP if the copy fails. */
+kv_status kv_decode_clamped_count(const void* workspace, void* stream,
+                                  int32_t* count);
 
 kv_status paged_attn_decode(void* out, const void* q, const void* k_cache,
                             const void* v_cache, int32_t num_blocks,
@@ -345,9 +357,13 @@ kv_status kv_swap_blocks(const void* src_k, const void* src_v,
  * finite 448), one byte per value, in the same [blocks, Hkv, block_size, D]
  * (or [S, Hkv, seq_stride, D]) layout as the bf16 caches. A value x is
  * stored as E4M3(clamp(x * fl32(1 / scale), -448, 448)): fp32 product with
- * the reciprocal rounded to fp32, maxNum/minNum clamp (a NaN becomes -448),
- * round to nearest, ties to even; it reads back as E4M3 value * scale.
- * One scale per tensor (k_scale for K, v_scale for V), finite and > 0. */
+ * the reciprocal rounded to fp32, saturation of overflows and infinities to
+ * +-448, round to nearest, ties to even; a NaN stays NaN (the code
+ * S.1111.111 with x's sign). A code reads back as E4M3 value * scale.
+ * Scales: one per tensor (k_scale for K, v_scale for V, finite and > 0), or
+ * with the *_per_head calls one per KV head (device float arrays k_scales,
+ * v_scales of Hkv entries; each must be finite and > 0, else the codes or
+ * outputs of that head are meaningless). */
 
 /* kv_reshape_and_cache for an fp8 cache: k, v are bf16 rows [num_tokens,
  * Hkv, D] (16-byte aligned), the caches hold codes (8-byte aligned);
@@ -396,6 +412,41 @@ kv_status contig_attn_decode_fp8(void* out, const void* q, const void* k,
                                  int32_t head_dim, float scale, float k_scale,
                                  float v_scale, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* The fp8 calls above with one scale per KV head: k_scales, v_scales are
+ * device float arrays [Hkv]; head h's rows are stored with
+ * fl32(1 / k_scales[h]) (K) and fl32(1 / v_scales[h]) (V), and the decode
+ * folds k_scales[g] into the score scale of KV head g and applies
+ * v_scales[g] to its outputs. Other arguments, layouts and errors as in the
+ * per-tensor calls; NULL scale arrays -> KV_EINVAL. */
+kv_status kv_reshape_and_cache_fp8_per_head(
+    const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
+    void* k_cache, void* v_cache, int64_t num_slots, int32_t block_size,
+    int32_t num_kv_heads, int32_t head_dim, const float* k_scales,
+    const float* v_scales, void* stream);
+
+kv_status kv_append_token_fp8_per_head(
+    const void* k, const void* v, const int32_t* new_blocks,
+    int32_t* block_tables, int32_t bt_stride, int32_t* context_lens,
+    int32_t num_seqs, void* k_cache, void* v_cache, int32_t num_blocks,
+    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+    const float* k_scales, const float* v_scales, void* stream);
+
+kv_status paged_attn_decode_fp8_per_head(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+    const int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, const float* k_scales,
+    const float* v_scales, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+kv_status contig_attn_decode_fp8_per_head(
+    void* out, const void* q, const void* k, const void* v, int32_t seq_stride,
+    const int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+    const float* k_scales, const float* v_scales, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
  * Prefix cache over a block pool ["PagedAttention Nedir?" (bitcanli.com),
@@ -470,8 +521,11 @@ int32_t kv_prefix_cache_size(const kv_prefix_cache* cache);
  * or write only tokens [0, L) of a sequence reserved up to L: other
  * addresses of the range are unmapped. Released pages keep their physical
  * memory in the cache's pool and are mapped again before new pages are
- * created; kv_vcache_destroy frees everything. Before a release or destroy
- * the caller must have synchronized the work that reads those pages.
+ * created; kv_vcache_destroy frees everything. kv_vcache_release (when it
+ * unmaps anything) and kv_vcache_destroy first wait for all work queued on
+ * the cache's device (hipDeviceSynchronize), so a kernel still reading the
+ * pages finishes before they are unmapped; they are therefore not for use
+ * inside a captured graph.
  * Errors: KV_EINVAL (arguments), KV_ENOMEM (device memory), KV_EHIP (other
  * HIP failures); a failed reserve leaves the mapping unchanged. The calls
  * on a cache come from one host thread; the cache's own mapping thread

@@ -13,9 +13,13 @@ format - 1 sign bit,
 subnormals (mantissa/8 * 2^-6); no infinities; S.1111.111 is NaN, so the
 largest finite magnitude is 1.75 * 2^8 = 448. A value is stored as
 code = E4M3(x * inv_scale) with the product taken in fp32, clamped to
-[-448, 448] (IEEE maxNum/minNum: a NaN product becomes -448), and rounded to
-the nearest representable value, ties to the even code. It is read back as
-value(code) * scale.
+[-448, 448] (saturation: infinities and overflows become +-448), and rounded
+to the nearest representable value, ties to the even code. A NaN input
+stays NaN: it is stored as the NaN code with the input's sign bit (0x7F or
+0xFF), as the format's own conversion keeps it. A code is read back as
+value(code) * scale. The scale is one per tensor, or one per KV head (any
+array that broadcasts against the values, e.g. [Hkv, 1] for rows
+[T, Hkv, D]).
 
 The encoder is written as a search over the 256 codes of the definition,
 not as bit manipulation, so that it can be checked by eye.
@@ -25,6 +29,7 @@ from __future__ import annotations
 import numpy as np
 
 MAX = 448.0
+NAN_CODE = 0x7F     # S.1111.111 with S = 0; the sign bit is added for -NaN
 
 
 def decode(code: int) -> float:
@@ -69,20 +74,30 @@ def encode_value(x: float) -> int:
     return c
 
 
-def quantize(x, inv_scale: float) -> np.ndarray:
-    """Codes of x (any float array): fp32 product with inv_scale, clamp to
-    +-448 (maxNum/minNum), round to nearest, ties to even."""
-    prod = np.float32(np.asarray(x, dtype=np.float32)) * np.float32(inv_scale)
-    prod = np.fmin(np.fmax(prod, np.float32(-MAX)), np.float32(MAX))
+def quantize(x, inv_scale) -> np.ndarray:
+    """Codes of x (any float array): fp32 product with inv_scale (a number,
+    or an array broadcasting against x), clamp to +-448, round to nearest,
+    ties to even; a NaN input gives the NaN code with its sign."""
+    x32 = np.asarray(x, dtype=np.float32)
+    with np.errstate(invalid="ignore"):   # signalling NaNs stay NaN
+        prod = x32 * np.asarray(inv_scale, dtype=np.float32)
+    nan = np.isnan(prod)
+    prod = np.where(nan, np.float32(0.0), prod)
+    prod = np.minimum(np.maximum(prod, np.float32(-MAX)), np.float32(MAX))
     # each distinct fp32 bit pattern (so -0 and +0 stay apart) is encoded
     # once by the search above
     bits, inverse = np.unique(np.ascontiguousarray(prod).view(np.uint32),
                               return_inverse=True)
     codes = np.array([encode_value(float(b)) for b in bits.view(np.float32)],
                      dtype=np.uint8)
-    return codes[inverse.reshape(-1)].reshape(prod.shape)
+    out = codes[inverse.reshape(-1)].reshape(prod.shape)
+    nan_codes = np.where(np.signbit(np.broadcast_to(x32, prod.shape)),
+                         NAN_CODE | 0x80, NAN_CODE).astype(np.uint8)
+    return np.where(nan, nan_codes, out).astype(np.uint8)
 
 
-def dequantize(codes, scale: float) -> np.ndarray:
-    """fp64 values of codes, times scale."""
-    return _VALUES[np.asarray(codes, dtype=np.int64)] * float(scale)
+def dequantize(codes, scale) -> np.ndarray:
+    """fp64 values of codes, times scale (a number, or an array broadcasting
+    against codes)."""
+    return _VALUES[np.asarray(codes, dtype=np.int64)] * np.asarray(
+        scale, dtype=np.float64)

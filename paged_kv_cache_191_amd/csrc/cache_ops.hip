@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void append_token_kernel(
       const Src* src = is_v ? v : k;
       Dst* dst = is_v ? v_cache : k_cache;
       dst[(((int64_t)blk * num_kv_heads + h) * block_size + off) *
-              units_per_head + u] = conv(src[(int64_t)s * per_tensor + r], is_v);
+              units_per_head + u] =
+          conv(src[(int64_t)s * per_tensor + r], is_v, h);
     }
   }
   // every thread has read ctx[s] and the table entry before they change
@@ -113,19 +114,22 @@ __global__ __launch_bounds__(256) void append_token_kernel(
 
 struct CopyUnit {
   template <typename U>
-  __device__ U operator()(U x, bool) const { return x; }
+  __device__ U operator()(U x, bool, int64_t) const { return x; }
 };
 
 size_t elem_size(kv_dtype dt) { return dt == KV_F32 ? 4 : 2; }
 
-// bf16 -> fp8 E4M3 code of x * inv: fp32 product, clamped to the format's
-// finite range with maxNum/minNum (a NaN product becomes -448), then the
-// hardware conversion (round to nearest, ties to even).
+// bf16 -> fp8 E4M3 code of x * inv: fp32 product, saturated to the
+// format's finite range (+-448), then the hardware conversion (round to
+// nearest, ties to even). A NaN input is handled by fp8_pack4.
 __device__ __forceinline__ float fp8_prep(uint32_t bf16_bits, float inv) {
   const float x = __builtin_bit_cast(float, bf16_bits << 16) * inv;
   return fminf(fmaxf(x, -448.f), 448.f);
 }
 
+// Four bf16 values (two dwords) -> four codes. A NaN input (bf16 exponent
+// all ones, mantissa non-zero) is stored as the NaN code S.1111.111 with the
+// input's sign, whatever the clamp above made of it: E4M3 keeps NaN.
 __device__ __forceinline__ uint32_t fp8_pack4(uint32_t w0, uint32_t w1,
                                               float inv) {
   int r = 0;
@@ -133,7 +137,23 @@ __device__ __forceinline__ uint32_t fp8_pack4(uint32_t w0, uint32_t w1,
                                       fp8_prep(w0 >> 16, inv), r, false);
   r = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prep(w1 & 0xFFFF, inv),
                                       fp8_prep(w1 >> 16, inv), r, true);
-  return (uint32_t)r;
+  uint32_t out = (uint32_t)r;
+  const uint32_t h[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if ((h[i] & 0x7FFFu) > 0x7F80u) {
+      const uint32_t nan_code = 0x7Fu | ((h[i] >> 8) & 0x80u);
+      out = (out & ~(0xFFu << (8 * i))) | (nan_code << (8 * i));
+    }
+  }
+  return out;
+}
+
+// Reciprocal of the scale of head h: per-head scales (device array) when
+// given, else the tensor's. 1.f / x is correctly rounded in HIP device code.
+__device__ __forceinline__ float fp8_inv(const float* scales, float inv,
+                                         int64_t h) {
+  return scales ? 1.f / scales[h] : inv;
 }
 
 // fp8 variant of scatter_rows_kernel: one item = 8 values of one head row
@@ -142,7 +162,8 @@ __global__ __launch_bounds__(256) void scatter_rows_fp8_kernel(
     const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const int64_t* __restrict__ slots, int32_t num_tokens, u32x2* k_cache,
     u32x2* v_cache, int64_t num_slots, int32_t block_size,
-    int32_t num_kv_heads, int32_t units_per_head, float k_inv, float v_inv) {
+    int32_t num_kv_heads, int32_t units_per_head, float k_inv, float v_inv,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales) {
   const int64_t per_token = (int64_t)num_kv_heads * units_per_head;
   const int64_t per_tensor = (int64_t)num_tokens * per_token;
   const int64_t total = 2 * per_tensor;
@@ -159,7 +180,8 @@ __global__ __launch_bounds__(256) void scatter_rows_fp8_kernel(
     const int64_t blk = slot / block_size;
     const int64_t off = slot - blk * block_size;
     const u32x4 x = (is_v ? v : k)[t * per_token + r];
-    const float inv = is_v ? v_inv : k_inv;
+    const float inv =
+        is_v ? fp8_inv(v_scales, v_inv, h) : fp8_inv(k_scales, k_inv, h);
     u32x2 c;
     c[0] = fp8_pack4(x[0], x[1], inv);
     c[1] = fp8_pack4(x[2], x[3], inv);
@@ -169,11 +191,15 @@ __global__ __launch_bounds__(256) void scatter_rows_fp8_kernel(
   }
 }
 
-// 8 bf16 values -> 8 E4M3 codes, K or V scale
+// 8 bf16 values of head h -> 8 E4M3 codes, with the K or V scale (per
+// tensor, or per head when the arrays are given)
 struct Fp8Unit {
   float k_inv, v_inv;
-  __device__ u32x2 operator()(u32x4 x, bool is_v) const {
-    const float inv = is_v ? v_inv : k_inv;
+  const float* k_scales;
+  const float* v_scales;
+  __device__ u32x2 operator()(u32x4 x, bool is_v, int64_t h) const {
+    const float inv =
+        is_v ? fp8_inv(v_scales, v_inv, h) : fp8_inv(k_scales, k_inv, h);
     u32x2 c;
     c[0] = fp8_pack4(x[0], x[1], inv);
     c[1] = fp8_pack4(x[2], x[3], inv);
@@ -183,12 +209,17 @@ struct Fp8Unit {
 
 }  // namespace
 
-extern "C" kv_status kv_reshape_and_cache_fp8(
-    const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
-    void* k_cache, void* v_cache, int64_t num_slots, int32_t block_size,
-    int32_t num_kv_heads, int32_t head_dim, float k_scale, float v_scale,
-    void* stream) {
-  const char* name = "kv_reshape_and_cache_fp8";
+namespace {
+// Shared body of the fp8 cache writes: one scale per tensor (k_scale,
+// v_scale) or, when k_scales / v_scales are given, one per KV head.
+kv_status reshape_and_cache_fp8(const char* name, const void* k,
+                                const void* v, const int64_t* slots,
+                                int32_t num_tokens, void* k_cache,
+                                void* v_cache, int64_t num_slots,
+                                int32_t block_size, int32_t num_kv_heads,
+                                int32_t head_dim, float k_scale, float v_scale,
+                                const float* k_scales, const float* v_scales,
+                                void* stream) {
   if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       head_dim % 8 != 0 || num_slots < 0 || block_size <= 0 ||
       num_slots % block_size != 0)
@@ -214,9 +245,35 @@ extern "C" kv_status kv_reshape_and_cache_fp8(
   const int64_t g = (items + threads - 1) / threads;
   scatter_rows_fp8_kernel<<<(int)(g < 65536 ? g : 65536), threads, 0, st>>>(
       (const u32x4*)k, (const u32x4*)v, slots, num_tokens, (u32x2*)k_cache,
-      (u32x2*)v_cache, num_slots, block_size, num_kv_heads, uph, k_inv, v_inv);
+      (u32x2*)v_cache, num_slots, block_size, num_kv_heads, uph, k_inv, v_inv,
+      k_scales, v_scales);
   KVP_LAUNCH_CHECK(name);
   return KV_OK;
+}
+}  // namespace
+
+extern "C" kv_status kv_reshape_and_cache_fp8(
+    const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
+    void* k_cache, void* v_cache, int64_t num_slots, int32_t block_size,
+    int32_t num_kv_heads, int32_t head_dim, float k_scale, float v_scale,
+    void* stream) {
+  return reshape_and_cache_fp8("kv_reshape_and_cache_fp8", k, v, slots,
+                               num_tokens, k_cache, v_cache, num_slots,
+                               block_size, num_kv_heads, head_dim, k_scale,
+                               v_scale, nullptr, nullptr, stream);
+}
+
+extern "C" kv_status kv_reshape_and_cache_fp8_per_head(
+    const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
+    void* k_cache, void* v_cache, int64_t num_slots, int32_t block_size,
+    int32_t num_kv_heads, int32_t head_dim, const float* k_scales,
+    const float* v_scales, void* stream) {
+  const char* name = "kv_reshape_and_cache_fp8_per_head";
+  if (num_tokens > 0 && (!k_scales || !v_scales))
+    return kvp_fail(KV_EINVAL, "%s: NULL scale array", name);
+  return reshape_and_cache_fp8(name, k, v, slots, num_tokens, k_cache,
+                               v_cache, num_slots, block_size, num_kv_heads,
+                               head_dim, 1.f, 1.f, k_scales, v_scales, stream);
 }
 
 extern "C" kv_status kv_reshape_and_cache(const void* k, const void* v,
@@ -444,13 +501,15 @@ extern "C" kv_status kv_append_token(const void* k, const void* v,
   return KV_OK;
 }
 
-extern "C" kv_status kv_append_token_fp8(
-    const void* k, const void* v, const int32_t* new_blocks,
-    int32_t* block_tables, int32_t bt_stride, int32_t* context_lens,
-    int32_t num_seqs, void* k_cache, void* v_cache, int32_t num_blocks,
-    int32_t block_size, int32_t num_kv_heads, int32_t head_dim, float k_scale,
-    float v_scale, void* stream) {
-  const char* name = "kv_append_token_fp8";
+namespace {
+kv_status append_token_fp8(const char* name, const void* k, const void* v,
+                           const int32_t* new_blocks, int32_t* block_tables,
+                           int32_t bt_stride, int32_t* context_lens,
+                           int32_t num_seqs, void* k_cache, void* v_cache,
+                           int32_t num_blocks, int32_t block_size,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           float k_scale, float v_scale, const float* k_scales,
+                           const float* v_scales, void* stream) {
   if (num_seqs < 0 || bt_stride <= 0 || num_blocks <= 0 || block_size <= 0 ||
       num_kv_heads <= 0 || head_dim <= 0 || head_dim % 8 != 0)
     return kvp_fail(KV_EINVAL, "%s: bad shape (S=%d stride=%d N=%d B=%d "
@@ -475,7 +534,37 @@ extern "C" kv_status kv_append_token_fp8(
   append_token_kernel<<<num_seqs, 256, 0, (hipStream_t)stream>>>(
       (const u32x4*)k, (const u32x4*)v, nb, block_tables, bt_stride,
       context_lens, (u32x2*)k_cache, (u32x2*)v_cache, num_blocks, block_size,
-      num_kv_heads, head_dim / 8, Fp8Unit{1.f / k_scale, 1.f / v_scale});
+      num_kv_heads, head_dim / 8,
+      Fp8Unit{1.f / k_scale, 1.f / v_scale, k_scales, v_scales});
   KVP_LAUNCH_CHECK(name);
   return KV_OK;
+}
+}  // namespace
+
+extern "C" kv_status kv_append_token_fp8(
+    const void* k, const void* v, const int32_t* new_blocks,
+    int32_t* block_tables, int32_t bt_stride, int32_t* context_lens,
+    int32_t num_seqs, void* k_cache, void* v_cache, int32_t num_blocks,
+    int32_t block_size, int32_t num_kv_heads, int32_t head_dim, float k_scale,
+    float v_scale, void* stream) {
+  return append_token_fp8("kv_append_token_fp8", k, v, new_blocks,
+                          block_tables, bt_stride, context_lens, num_seqs,
+                          k_cache, v_cache, num_blocks, block_size,
+                          num_kv_heads, head_dim, k_scale, v_scale, nullptr,
+                          nullptr, stream);
+}
+
+extern "C" kv_status kv_append_token_fp8_per_head(
+    const void* k, const void* v, const int32_t* new_blocks,
+    int32_t* block_tables, int32_t bt_stride, int32_t* context_lens,
+    int32_t num_seqs, void* k_cache, void* v_cache, int32_t num_blocks,
+    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+    const float* k_scales, const float* v_scales, void* stream) {
+  const char* name = "kv_append_token_fp8_per_head";
+  if (num_seqs > 0 && (!k_scales || !v_scales))
+    return kvp_fail(KV_EINVAL, "%s: NULL scale array", name);
+  return append_token_fp8(name, k, v, new_blocks, block_tables, bt_stride,
+                          context_lens, num_seqs, k_cache, v_cache,
+                          num_blocks, block_size, num_kv_heads, head_dim, 1.f,
+                          1.f, k_scales, v_scales, stream);
 }

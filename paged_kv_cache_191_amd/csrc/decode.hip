@@ -41,8 +41,16 @@
 //     last context group (rows already in flight, served by the cache);
 //     tokens past the context are selected out (score -inf, V 0), never
 //     multiplied by 0, so NaN in unused slots cannot leak.
-// Generic path (fp32, or shapes the fast path does not cover): one wave per
-// (sequence, query head), lanes over head_dim, tokens in order.
+// Generic path (fp32, or shapes the fast path does not cover): one
+// workgroup of 8 waves per (query head, sequence), lanes over head_dim; the
+// tokens go to the waves in groups of 8, each wave keeps its own softmax
+// state, and the 8 states are merged exactly through LDS.
+//
+// Contexts: a context_lens entry outside [0, bound], bound = min(max_context,
+// the table's or the sequence's capacity), is clamped into it so that every
+// access stays in bounds. The number of such sequences of the last call is
+// kept in the workspace header (kv_decode_clamped_count reads it), so that a
+// stale bound is visible instead of silently shortening the attention.
 //
 // Shared prefix (paged_attn_decode_shared_prefix): when groups of sequences
 // hold the same first tokens in the same physical blocks (a forked prompt,
@@ -87,8 +95,12 @@ struct DecodeArgs {
   int32_t group;        // hq / hkv
   int32_t head_blocks;  // ceil(group / 16)
   int32_t head_dim;
-  float scale_log2;     // scale * log2(e) (fp8 K/V: times k_scale)
+  float scale_log2;     // scale * log2(e) (fp8 K/V per tensor: times k_scale)
   float v_scale;        // fp8 K/V: scale of V (outputs are multiplied by it)
+  const float* k_scales;  // fp8 K/V per KV head [Hkv] (NULL: per tensor)
+  const float* v_scales;
+  int32_t* ws_hdr;      // workspace header: [0] = sequences clamped
+  int32_t clamp_add;    // 0: store the count, 1: add it (later launches)
   int32_t n_chunks;     // chunks per (KV head, head block)
   float* ws_o;          // [n_chunks, 2, Hq, D] unnormalised partial outputs
   float* ws_ml;         // [n_chunks, 2, Hq, 2] (reference max, sum)
@@ -103,9 +115,8 @@ struct DecodeArgs {
   float* whole_ml;      // [S, Hq, 2]
 };
 
-__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int c,
                                          bool paged) {
-  int c = a.ctx[s];
   c = c < 0 ? 0 : c;
   c = c > a.max_ctx ? a.max_ctx : c;
   if (paged) {
@@ -115,6 +126,18 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
     c = a.seq_stride;
   }
   return c;
+}
+
+__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
+                                         bool paged) {
+  return clamp_len(a, a.ctx[s], paged);
+}
+
+// Workgroup 0 of a launch records how many of its sequences were clamped.
+__device__ __forceinline__ void record_clamped(const DecodeArgs& a, int n) {
+  if (!a.ws_hdr) return;
+  if (a.clamp_add) a.ws_hdr[0] += n;
+  else a.ws_hdr[0] = n;
 }
 
 // Leading tokens of sequence s (context L) that the prefix partials cover;
@@ -179,6 +202,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   constexpr int KL = KV8 ? 2 : 4;  // 16-byte K loads per token row per tile
   __shared__ int s_cs[kMaxSeqs + 1];
   __shared__ int s_part[kWaves];
+  __shared__ int s_clamped;
   __shared__ float sm_o[kWaves][kHeadBlk][kD];
   __shared__ float sm_ml[kWaves][kHeadBlk][2];
 
@@ -199,12 +223,15 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   // the 256 per-thread sums are scanned (shuffles inside each wave, the
   // four wave totals through LDS) and s_cs is turned into offsets in place.
   {
+    if (tid == 0) s_clamped = 0;
     const int per = (S + kWaves * kWave - 1) / (kWaves * kWave);
     const int lo = tid * per;
     const int hi = min(S, lo + per);
-    int sum = 0;
+    int sum = 0, clamped = 0;
     for (int i = lo; i < hi; ++i) {
-      const int L = clamp_ctx(a, i, PAGED);
+      const int raw = a.ctx[i];
+      const int L = clamp_len(a, raw, PAGED);
+      clamped += L != raw;
       const int n = tiles_of(L - shared_of(a, i, L));
       s_cs[i] = n;
       sum += n;
@@ -217,6 +244,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     }
     if (lane == kWave - 1) s_part[w] = inc;
     __syncthreads();
+    if (clamped) atomicAdd(&s_clamped, clamped);
     int base = 0;  // tiles of the waves before this one
     for (int ww = 0; ww < w; ++ww) base += s_part[ww];
     int run = base + inc - sum;
@@ -229,8 +257,10 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     __syncthreads();
   }
   const int total = s_cs[S];
-  if (blockIdx.x == 0 && chunk == 0)
+  if (blockIdx.x == 0 && chunk == 0) {
     for (int i = tid; i <= S; i += kWaves * kWave) a.ws_cs[i] = s_cs[i];
+    if (tid == 0) record_clamped(a, s_clamped);
+  }
   const int C = chunk_tiles(total, a.n_chunks);
   const int c0 = chunk * C;
   if (c0 >= total) return;
@@ -247,6 +277,11 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     s = lo;
   }
 
+  // fp8 K/V: per-head scales fold into this KV head's score scale and
+  // output scale
+  const float scale_log2 = a.k_scales ? a.scale_log2 * a.k_scales[g]
+                                      : a.scale_log2;
+  const float v_scale = a.v_scales ? a.v_scales[g] : a.v_scale;
   const int h_in_group = hblk * kHeadBlk + r16;
   const bool h_valid = h_in_group < a.group;
   const int nh = min(kHeadBlk, a.group - hblk * kHeadBlk);
@@ -399,7 +434,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float v = sc[hf][r] * a.scale_log2;
+            const float v = sc[hf][r] * scale_log2;
             const int p = t + 16 * hf + 4 * grp + r;
             x[hf][r] = (full || p < hi) ? v : -INFINITY;
           }
@@ -521,7 +556,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
       }
       if constexpr (KV8) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc[jj] *= a.v_scale;
+        for (int jj = 0; jj < 8; ++jj) acc[jj] *= v_scale;
       }
       const int head = g * a.group + hblk * kHeadBlk + h;
       if (whole && P > 0) {
@@ -751,6 +786,17 @@ __global__ __launch_bounds__(kGenWaves * kWave) void decode_generic_kernel(
     const int d = lane + kWave * i;
     if (d < D) op[d] = from_f32<T>(o[i] * inv);
   }
+  // wave 0 of the first workgroup counts the clamped contexts
+  if (blockIdx.x == 0 && blockIdx.y == 0 && a.ws_hdr) {
+    int n = 0;
+    for (int i = lane; i < a.num_seqs; i += kWave) {
+      const int raw = a.ctx[i];
+      n += clamp_len(a, raw, PAGED) != raw;
+    }
+#pragma unroll
+    for (int o2 = 32; o2 > 0; o2 >>= 1) n += __shfl_xor(n, o2);
+    if (lane == 0) record_clamped(a, n);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -791,11 +837,15 @@ int choose_chunks(int num_kv_heads, int head_blocks) {
   return n < 1 ? 1 : n;
 }
 
+// Workspace: a 256-byte header (int32 [0] = sequences whose context was
+// clamped in the last call), then the stream-K partials and tile offsets.
+constexpr size_t kWsHeader = 256;
+
 size_t sk_workspace_bytes(int num_seqs, int hq, int n_chunks) {
   const size_t o = (size_t)n_chunks * 2 * hq * kD * sizeof(float);
   const size_t ml = (size_t)n_chunks * 2 * hq * 2 * sizeof(float);
   const size_t cs = (size_t)(num_seqs + 1) * sizeof(int32_t);
-  return o + ml + cs;
+  return kWsHeader + o + ml + cs;
 }
 
 bool fast_path_ok(kv_dtype dtype, int head_dim, int block_size, bool paged) {
@@ -847,7 +897,8 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
     if (!workspace || ws_bytes < need)
       return kvp_fail(KV_EINVAL, "%s: workspace of %zu bytes needed, %zu given",
                       name, need, ws_bytes);
-    a.ws_o = (float*)workspace;
+    a.ws_hdr = (int32_t*)workspace;
+    a.ws_o = (float*)((char*)workspace + kWsHeader);
     a.ws_ml = a.ws_o + (size_t)a.n_chunks * 2 * a.hq * kD;
     a.ws_cs = (int32_t*)(a.ws_ml + (size_t)a.n_chunks * 2 * a.hq * 2);
     // Batches of more than kMaxSeqs sequences run as several launches on
@@ -855,6 +906,7 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
     for (int s0 = 0; s0 < a.num_seqs; s0 += kMaxSeqs) {
       DecodeArgs b = a;
       b.num_seqs = min(kMaxSeqs, a.num_seqs - s0);
+      b.clamp_add = s0 > 0;
       b.out = (bf16*)a.out + (size_t)s0 * a.hq * kD;
       b.q = (const bf16*)a.q + (size_t)s0 * a.hq * kD;
       b.ctx = a.ctx + s0;
@@ -892,6 +944,10 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
   if (a.head_dim > 4 * kWave)
     return kvp_fail(KV_EUNSUPPORTED, "%s: head_dim %d > 256", name,
                     a.head_dim);
+  if (!workspace || ws_bytes < kWsHeader)
+    return kvp_fail(KV_EINVAL, "%s: workspace of %zu bytes needed, %zu given",
+                    name, kWsHeader, ws_bytes);
+  a.ws_hdr = (int32_t*)workspace;
   dim3 grid(a.hq, a.num_seqs);
   if (dtype == KV_F32) {
     if (paged)
@@ -1082,7 +1138,7 @@ extern "C" size_t kv_decode_workspace_bytes(int32_t num_seqs,
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads || head_dim <= 0)
     return 0;
-  if (head_dim != kD) return 0;  // the generic path needs no workspace
+  if (head_dim != kD) return kWsHeader;  // generic path: the header only
   const int hb = (num_q_heads / num_kv_heads + kHeadBlk - 1) / kHeadBlk;
   const int n = choose_chunks(num_kv_heads, hb);
   const int per_launch = num_seqs < kMaxSeqs ? num_seqs : kMaxSeqs;
@@ -1200,4 +1256,83 @@ extern "C" kv_status contig_attn_decode(
   a.scale_log2 = scale * kLog2e;
   return run_decode("contig_attn_decode", false, a, dtype, workspace,
                     workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" kv_status paged_attn_decode_fp8_per_head(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+    const int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, const float* k_scales,
+    const float* v_scales, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  const char* name = "paged_attn_decode_fp8_per_head";
+  if (num_seqs > 0 && (!k_scales || !v_scales))
+    return kvp_fail(KV_EINVAL, "%s: NULL scale array", name);
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.ctx = context_lens;
+  a.max_ctx = max_context;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale_log2 = scale * kLog2e;
+  a.v_scale = 1.f;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  return run_decode(name, true, a, KV_BF16, workspace, workspace_bytes,
+                    (hipStream_t)stream, true);
+}
+
+extern "C" kv_status contig_attn_decode_fp8_per_head(
+    void* out, const void* q, const void* k, const void* v, int32_t seq_stride,
+    const int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+    const float* k_scales, const float* v_scales, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* name = "contig_attn_decode_fp8_per_head";
+  if (num_seqs > 0 && (!k_scales || !v_scales))
+    return kvp_fail(KV_EINVAL, "%s: NULL scale array", name);
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.seq_stride = seq_stride;
+  a.block_size = 16;
+  a.ctx = context_lens;
+  a.max_ctx = max_context;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale_log2 = scale * kLog2e;
+  a.v_scale = 1.f;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  return run_decode(name, false, a, KV_BF16, workspace, workspace_bytes,
+                    (hipStream_t)stream, true);
+}
+
+extern "C" kv_status kv_decode_clamped_count(const void* workspace,
+                                             void* stream, int32_t* count) {
+  if (!workspace || !count)
+    return kvp_fail(KV_EINVAL, "kv_decode_clamped_count: NULL pointer");
+  hipStream_t st = (hipStream_t)stream;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return kvp_fail(KV_EHIP, "kv_decode_clamped_count: copy failed: %s",
+                    hipGetErrorString(hipGetLastError()));
+  *count = v;
+  return KV_OK;
 }

@@ -76,11 +76,31 @@ kv_status hip_fail(const char* what, hipError_t e) {
                   what, hipGetErrorString(e));
 }
 
+// Wait for all work queued on the cache's device: a kernel still in flight
+// may read pages that are about to be unmapped.
+kv_status drain_device(const kv_vcache* c) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail("kv_vcache: hipGetDevice", e);
+  if (cur != c->device && (e = hipSetDevice(c->device)) != hipSuccess)
+    return hip_fail("kv_vcache: hipSetDevice", e);
+  e = hipDeviceSynchronize();
+  if (cur != c->device) (void)hipSetDevice(cur);
+  if (e != hipSuccess) return hip_fail("kv_vcache: hipDeviceSynchronize", e);
+  return KV_OK;
+}
+
 // Unmap pages [keep, mapped) of every region of sequence s; their handles go
-// back to the pool.
-kv_status unmap_tail(kv_vcache* c, int32_t s, int32_t keep) {
+// back to the pool. With `drain`, the device's queued work is waited for
+// first (false only when the caller has just done so).
+kv_status unmap_tail(kv_vcache* c, int32_t s, int32_t keep,
+                     bool drain = true) {
   const int32_t have = c->pages[s];
   if (have <= keep) return KV_OK;
+  if (drain) {
+    const kv_status st = drain_device(c);
+    if (st != KV_OK) return st;
+  }
   try {  // room in the pool for every handle unmapped below
     c->pool.reserve(c->pool.size() + (size_t)(have - keep) * 2 * c->hkv);
   } catch (const std::bad_alloc&) {
@@ -195,7 +215,8 @@ extern "C" void kv_vcache_destroy(kv_vcache* c) {
   }
   c->cv.notify_all();
   if (c->worker.joinable()) c->worker.join();
-  for (int32_t s = 0; s < c->max_seqs; ++s) (void)unmap_tail(c, s, 0);
+  (void)drain_device(c);  // nothing may still read the pages
+  for (int32_t s = 0; s < c->max_seqs; ++s) (void)unmap_tail(c, s, 0, false);
   for (auto h : c->pool) (void)hipMemRelease(h);
   for (int t = 0; t < 2; ++t)
     if (c->base[t]) (void)hipMemAddressFree(c->base[t], c->tensor_bytes);

@@ -74,6 +74,20 @@ SIGNATURES = {
     "contig_attn_decode_fp8": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32,
                                       _I32, _I32, _I32, _F, _F, _F, _P, _SZ,
                                       _P]),
+    "kv_reshape_and_cache_fp8_per_head": (_I32, [_P, _P, _P, _I32, _P, _P,
+                                                 _I64, _I32, _I32, _I32, _P,
+                                                 _P, _P]),
+    "kv_append_token_fp8_per_head": (_I32, [_P, _P, _P, _P, _I32, _P, _I32,
+                                            _P, _P, _I32, _I32, _I32, _I32,
+                                            _P, _P, _P]),
+    "paged_attn_decode_fp8_per_head": (_I32, [_P, _P, _P, _P, _I32, _P, _I32,
+                                              _P, _I32, _I32, _I32, _I32,
+                                              _I32, _I32, _F, _P, _P, _P,
+                                              _SZ, _P]),
+    "contig_attn_decode_fp8_per_head": (_I32, [_P, _P, _P, _P, _I32, _P, _I32,
+                                               _I32, _I32, _I32, _I32, _F, _P,
+                                               _P, _P, _SZ, _P]),
+    "kv_decode_clamped_count": (_I32, [_P, _P, _PI32]),
     "kv_decode_chunks": (_I32, [_I32, _I32]),
     "kv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "paged_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
@@ -479,6 +493,37 @@ def kv_reshape_and_cache_fp8(k, v, slots, k_cache, v_cache, k_scale: float,
     _check(st, "kv_reshape_and_cache_fp8")
 
 
+def _head_scales(t, hkv: int, name: str):
+    """Pointer of a device float32 [Hkv] array of per-head scales."""
+    torch = _torch()
+    if tuple(t.shape) != (hkv,):
+        raise ValueError(f"{name} must have shape ({hkv},), has "
+                         f"{tuple(t.shape)}")
+    return _dev(t, name, torch.float32)
+
+
+def kv_reshape_and_cache_fp8_per_head(k, v, slots, k_cache, v_cache,
+                                      k_scales, v_scales,
+                                      stream=None) -> None:
+    """kv_reshape_and_cache_fp8 with one scale per KV head: k_scales,
+    v_scales are device float32 [Hkv]."""
+    torch = _torch()
+    n, hkv, d = k.shape
+    nb, chkv, bs, cd = k_cache.shape
+    if (chkv, cd) != (hkv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches and rows disagree on shape")
+    _same(v, k, "v", "k")
+    _ndim(slots, 1, "slots")
+    _rows(slots, n, "slots")
+    st = lib().kv_reshape_and_cache_fp8_per_head(
+        _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+        _dev(slots, "slots", torch.int64), n, _fp8_cache(k_cache, "k_cache"),
+        _fp8_cache(v_cache, "v_cache"), nb * bs, bs, hkv, d,
+        _head_scales(k_scales, hkv, "k_scales"),
+        _head_scales(v_scales, hkv, "v_scales"), _stream(stream))
+    _check(st, "kv_reshape_and_cache_fp8_per_head")
+
+
 def kv_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
     torch = _torch()
     nb, hkv, bs, d = k_cache.shape
@@ -552,6 +597,37 @@ def kv_append_token_fp8(k, v, new_blocks, block_tables, context_lens,
         S, _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"), nb,
         bs, hkv, d, float(k_scale), float(v_scale), _stream(stream))
     _check(st, "kv_append_token_fp8")
+
+
+def kv_append_token_fp8_per_head(k, v, new_blocks, block_tables,
+                                 context_lens, k_cache, v_cache, k_scales,
+                                 v_scales, stream=None) -> None:
+    """kv_append_token_fp8 with one scale per KV head (device float32
+    [Hkv])."""
+    torch = _torch()
+    S, hkv, d = k.shape
+    nb, chkv, bs, cd = k_cache.shape
+    if (chkv, cd) != (hkv, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches and rows disagree on shape")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v differ in shape")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S or \
+            new_blocks.shape[0] != S:
+        raise ValueError("block_tables, context_lens and new_blocks need one "
+                         "row per sequence")
+    if not new_blocks.is_contiguous() or new_blocks.dtype != torch.int32:
+        raise ValueError("new_blocks must be a contiguous int32 tensor")
+    _ndim(new_blocks, 1, "new_blocks")
+    _ndim(block_tables, 2, "block_tables")
+    _ndim(context_lens, 1, "context_lens")
+    st = lib().kv_append_token_fp8_per_head(
+        _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+        new_blocks.data_ptr(), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        S, _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"), nb,
+        bs, hkv, d, _head_scales(k_scales, hkv, "k_scales"),
+        _head_scales(v_scales, hkv, "v_scales"), _stream(stream))
+    _check(st, "kv_append_token_fp8_per_head")
 
 
 def kv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:
@@ -667,6 +743,65 @@ def contig_attn_decode_fp8(out, q, k, v, context_lens, max_context: int,
         hq, hkv, d, float(scale), float(k_scale), float(v_scale),
         _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "contig_attn_decode_fp8")
+
+
+def paged_attn_decode_fp8_per_head(out, q, k_cache, v_cache, block_tables,
+                                   context_lens, max_context: int,
+                                   scale: float, k_scales, v_scales,
+                                   workspace=None, stream=None) -> None:
+    """paged_attn_decode_fp8 with one scale per KV head (device float32
+    [Hkv])."""
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, hkv, bs, dk = k_cache.shape
+    _attn_shapes(out, q, k_cache, v_cache, dk, S,
+                 ((block_tables, "block_tables"),
+                  (context_lens, "context_lens")))
+    _ndim(block_tables, 2, "block_tables")
+    if workspace is None:
+        workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
+    st = lib().paged_attn_decode_fp8_per_head(
+        _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+        _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"), nb,
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context), S, hq, hkv, d, bs, float(scale),
+        _head_scales(k_scales, hkv, "k_scales"),
+        _head_scales(v_scales, hkv, "v_scales"),
+        _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "paged_attn_decode_fp8_per_head")
+
+
+def contig_attn_decode_fp8_per_head(out, q, k, v, context_lens,
+                                    max_context: int, scale: float, k_scales,
+                                    v_scales, workspace=None,
+                                    stream=None) -> None:
+    """contig_attn_decode_fp8 with one scale per KV head."""
+    torch = _torch()
+    S, hq, d = q.shape
+    _, hkv, lmax, dk = k.shape
+    _attn_shapes(out, q, k, v, dk, S,
+                 ((k, "k"), (context_lens, "context_lens")))
+    if workspace is None:
+        workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
+    st = lib().contig_attn_decode_fp8_per_head(
+        _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+        _fp8_cache(k, "k"), _fp8_cache(v, "v"), lmax,
+        _dev(context_lens, "context_lens", torch.int32), int(max_context), S,
+        hq, hkv, d, float(scale), _head_scales(k_scales, hkv, "k_scales"),
+        _head_scales(v_scales, hkv, "v_scales"),
+        _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "contig_attn_decode_fp8_per_head")
+
+
+def kv_decode_clamped_count(workspace, stream=None) -> int:
+    """Sequences whose context length the last decode call on `workspace`
+    clamped (waits for the stream)."""
+    n = ctypes.c_int32(0)
+    st = lib().kv_decode_clamped_count(_dev(workspace, "workspace"),
+                                       _stream(stream), ctypes.byref(n))
+    _check(st, "kv_decode_clamped_count")
+    return int(n.value)
 
 
 def kv_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads,

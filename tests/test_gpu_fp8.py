@@ -1,8 +1,9 @@
 """GPU parity of the fp8 E4M3 K/V cache through the C ABI: the quantising
 cache write bit for bit against the oracle's codec (oracle/fp8.py), and
 decode over fp8 caches against the fp64 oracle run on the dequantised
-values. Unused cache bytes start as 0x7F (an E4M3 NaN), so a kernel that
-reads a slot past a context fails the comparison."""
+values, with one scale per tensor or one per KV head. Unused cache bytes
+start as 0x7F (an E4M3 NaN), so a kernel that reads a slot past a context
+fails the comparison."""
 import sys
 
 import numpy as np
@@ -32,14 +33,40 @@ def _setup():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
 
 
-def _inv(scale: float) -> float:
-    """The fp32 reciprocal the cache write multiplies by."""
+def _per_head(scale) -> bool:
+    return isinstance(scale, np.ndarray)
+
+
+def _inv(scale):
+    """The fp32 reciprocal the cache write multiplies by: a number, or for
+    per-head scales an [Hkv, 1] array that broadcasts over rows [.., Hkv,
+    D]."""
+    if _per_head(scale):
+        return (np.float32(1.0) / scale.astype(np.float32))[:, None]
     return float(np.float32(1.0) / np.float32(scale))
+
+
+def _scale_b(scale):
+    """A scale as the oracle's dequantisation takes it ([Hkv, 1] per head)."""
+    return scale[:, None] if _per_head(scale) else scale
+
+
+def _dev_scales(scale):
+    return torch.from_numpy(scale.astype(np.float32)).cuda()
+
+
+def _write_fp8(k, v, slots, kc, vc, ks, vs):
+    """kv_reshape_and_cache_fp8, or its per-head form for array scales."""
+    if _per_head(ks):
+        kv.kv_reshape_and_cache_fp8_per_head(k, v, slots, kc, vc,
+                                             _dev_scales(ks), _dev_scales(vs))
+    else:
+        kv.kv_reshape_and_cache_fp8(k, v, slots, kc, vc, ks, vs)
 
 
 def _fill_fp8(inp, nat, k_scale, v_scale):
     """fp8 paged caches [N, Hkv, B, D] holding every context row of the
-    native tables (written in one kv_reshape_and_cache_fp8 call)."""
+    native tables (written in one cache-write call)."""
     w = inp.workload
     B = w.block_size
     kc = torch.full(tuple(nat.k_cache.shape), NAN_CODE, dtype=torch.uint8,
@@ -52,9 +79,8 @@ def _fill_fp8(inp, nat, k_scale, v_scale):
     slots = kv.kv_slot_mapping(nat.tables, seq_ids, pos, B)
     rows = np.concatenate([W.logical_rows(inp, s) for s in range(len(ctx))])
     r = torch.from_numpy(rows)
-    kv.kv_reshape_and_cache_fp8(inp.k[r].cuda(), inp.v[r].cuda(),
-                                torch.from_numpy(slots).cuda(), kc, vc,
-                                k_scale, v_scale)
+    _write_fp8(inp.k[r].cuda(), inp.v[r].cuda(),
+               torch.from_numpy(slots).cuda(), kc, vc, k_scale, v_scale)
     torch.cuda.synchronize()
     return kc, vc
 
@@ -82,8 +108,8 @@ def _oracle_codes(inp, orc, k_scale, v_scale, seqs=None):
 
 
 def _dequant_pool(codes, scale):
-    """Values of an oracle code pool (NaN where 0x7F)."""
-    return F.dequantize(codes, scale)
+    """Values of an oracle code pool [N, B, Hkv, D] (NaN where 0x7F)."""
+    return F.dequantize(codes, _scale_b(scale))
 
 
 def _small_workload(seed=11):
@@ -170,8 +196,13 @@ def _decode_fp8_both(inp, nat, orc, kc, vc, kp, vp, ks, vs, seqs=None,
     max_ctx = int(ctx.max())
     q = inp.q.cuda()
     out = torch.empty_like(q)
-    kv.paged_attn_decode_fp8(out, q, kc, vc, nat.bt, nat.ctx, max_ctx, scale,
-                             ks, vs)
+    if _per_head(ks):
+        kv.paged_attn_decode_fp8_per_head(out, q, kc, vc, nat.bt, nat.ctx,
+                                          max_ctx, scale, _dev_scales(ks),
+                                          _dev_scales(vs))
+    else:
+        kv.paged_attn_decode_fp8(out, q, kc, vc, nat.bt, nat.ctx, max_ctx,
+                                 scale, ks, vs)
     outs = {"paged": out}
     if contig:
         # contiguous fp8 caches [S, Hkv, Lmax, D] written by the same call,
@@ -184,12 +215,17 @@ def _decode_fp8_both(inp, nat, orc, kc, vc, kp, vp, ks, vs, seqs=None,
         slots = np.concatenate([s * max_ctx + np.arange(int(ctx[s]))
                                 for s in range(S)]).astype(np.int64)
         r = torch.from_numpy(rows)
-        kv.kv_reshape_and_cache_fp8(inp.k[r].cuda(), inp.v[r].cuda(),
-                                    torch.from_numpy(slots).cuda(), ck, cv,
-                                    ks, vs)
+        _write_fp8(inp.k[r].cuda(), inp.v[r].cuda(),
+                   torch.from_numpy(slots).cuda(), ck, cv, ks, vs)
         oc = torch.empty_like(q)
-        kv.contig_attn_decode_fp8(oc, q, ck, cv, nat.ctx, max_ctx, scale, ks,
-                                  vs)
+        if _per_head(ks):
+            kv.contig_attn_decode_fp8_per_head(oc, q, ck, cv, nat.ctx,
+                                               max_ctx, scale,
+                                               _dev_scales(ks),
+                                               _dev_scales(vs))
+        else:
+            kv.contig_attn_decode_fp8(oc, q, ck, cv, nat.ctx, max_ctx, scale,
+                                      ks, vs)
         outs["contig"] = oc
     torch.cuda.synchronize()
     want = O.decode_paged(inp.q.float().numpy(), _dequant_pool(kp, ks),
@@ -325,3 +361,173 @@ def test_decode_fp8_random_shapes(seed):
          f"{int(ctx.min())}..{int(ctx.max())}")
     _check(outs, want, w.name)
     assert np.array_equal(outs["paged"], outs["contig"])
+
+
+# ------------------------------------------------------- per-head scales --
+def _head_scales(seed, hkv):
+    """Seeded per-head K and V scales, spread over a factor of about 8 so
+    that a scale taken from the wrong head changes the codes."""
+    g = np.random.default_rng([4000, seed])
+    return (g.uniform(0.006, 0.05, hkv).astype(np.float32),
+            g.uniform(0.006, 0.05, hkv).astype(np.float32))
+
+
+def test_fp8_per_head_cache_write_bit_exact():
+    w = _small_workload(seed=13)
+    inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens, 4))
+    cap = H.tables_capacity(int(W.context_lengths(inp).max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    ks, vs = _head_scales(0, w.num_kv_heads)
+    kc, vc = _fill_fp8(inp, nat, ks, vs)
+    kp, vp = _oracle_codes(inp, orc, ks, vs)
+    assert np.array_equal(kc.permute(0, 2, 1, 3).cpu().numpy(), kp)
+    assert np.array_equal(vc.permute(0, 2, 1, 3).cpu().numpy(), vp)
+    # the per-head codes differ from those of any single tensor scale
+    kp0, _ = _oracle_codes(inp, orc, float(ks[0]), float(vs[0]))
+    assert not np.array_equal(kp, kp0)
+
+
+def test_fp8_per_head_special_values():
+    """NaN (both signs), infinities and saturation under per-head scales."""
+    D, hkv = 128, 2
+    g = np.random.default_rng(8)
+    rows = g.standard_normal((3, hkv, D)).astype(np.float32) * 60
+    rows[0, 0, 2:4] = [np.inf, -np.inf]
+    rows[1, 1, :2] = [1e30, -1e30]
+    k = torch.from_numpy(rows).to(torch.bfloat16)
+    v = torch.from_numpy(-rows).to(torch.bfloat16)
+    # NaNs of both signs, as bf16 bit patterns (torch's fp32 -> bf16
+    # conversion would make every NaN 0xFFFF)
+    for t in (k, v):
+        bits = t.view(torch.int16)
+        bits[0, 0, 0] = 0x7FC0                 # +NaN
+        bits[0, 0, 1] = -64                    # 0xFFC0, -NaN
+        bits[1, 1, 2] = 0x7F81                 # +NaN, low payload
+    ks = np.array([0.5, 0.02], dtype=np.float32)
+    vs = np.array([3.0, 0.0123], dtype=np.float32)
+    kc = torch.full((2, hkv, 16, D), NAN_CODE, dtype=torch.uint8,
+                    device="cuda")
+    vc = torch.full_like(kc, NAN_CODE)
+    slots = torch.tensor([17, -1, 2], dtype=torch.int64, device="cuda")
+    _write_fp8(k.cuda(), v.cuda(), slots, kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    want_k = F.quantize(k.float().numpy(), _inv(ks))
+    want_v = F.quantize(v.float().numpy(), _inv(vs))
+    got_k = kc.permute(0, 2, 1, 3).cpu().numpy()
+    got_v = vc.permute(0, 2, 1, 3).cpu().numpy()
+    for t, slot in ((0, 17), (2, 2)):
+        b, o = divmod(slot, 16)
+        assert np.array_equal(got_k[b, o], want_k[t]), t
+        assert np.array_equal(got_v[b, o], want_v[t]), t
+    assert want_k[0, 0, :2].tolist() == [0x7F, 0xFF]
+    assert want_k[1, 1, 2] == 0x7F
+    # the padded row (slot -1) wrote nothing
+    written = {(1, 1), (0, 2)}
+    for b in range(2):
+        for o in range(16):
+            if (b, o) not in written:
+                assert (got_k[b, o] == NAN_CODE).all()
+                assert (got_v[b, o] == NAN_CODE).all()
+
+
+def test_fp8_per_head_append_token():
+    """The device append with per-head scales equals the per-head cache
+    write of the same rows into the same slots, and the oracle's codes."""
+    w = _small_workload(seed=14)
+    S, B, hkv, D = w.num_seqs, w.block_size, w.num_kv_heads, w.head_dim
+    ks, vs = _head_scales(1, hkv)
+    g = np.random.default_rng(15)
+    lens = np.array(w.lengths, dtype=np.int32)
+    cap = H.tables_capacity(int(lens.max()) + 1, B)
+    n_pool = sum(-(-int(n + 1) // B) for n in lens) + 4
+    pool = kv.KVPool(n_pool, B)
+    table = np.full((S, cap), -1, dtype=np.int32)
+    cur = np.zeros(S, dtype=np.int32)
+    pool.seq_append(table, cur, lens)
+    before = table.copy()
+    _, pairs = pool.seq_append(table, cur)          # one more token each
+    assert len(pairs) == 0
+    newb = np.where(table != before, table, -1).max(axis=1).astype(np.int32)
+    rows = torch.from_numpy(
+        g.standard_normal((S, hkv, D)).astype(np.float32) * 5).to(
+        torch.bfloat16)
+    vrows = torch.from_numpy(
+        g.standard_normal((S, hkv, D)).astype(np.float32) * 5).to(
+        torch.bfloat16)
+    kc = torch.full((n_pool, hkv, B, D), NAN_CODE, dtype=torch.uint8,
+                    device="cuda")
+    vc = torch.full_like(kc, NAN_CODE)
+    kc2, vc2 = kc.clone(), vc.clone()
+    d_table = torch.from_numpy(before).cuda()
+    d_lens = torch.from_numpy(lens.copy()).cuda()
+    kv.kv_append_token_fp8_per_head(rows.cuda(), vrows.cuda(),
+                                    torch.from_numpy(newb).cuda(), d_table,
+                                    d_lens, kc, vc, _dev_scales(ks),
+                                    _dev_scales(vs))
+    slots = np.array([table[s, lens[s] // B] * B + lens[s] % B
+                      for s in range(S)], dtype=np.int64)
+    _write_fp8(rows.cuda(), vrows.cuda(), torch.from_numpy(slots).cuda(),
+               kc2, vc2, ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
+    assert np.array_equal(d_table.cpu().numpy(), table)
+    assert np.array_equal(d_lens.cpu().numpy(), lens + 1)
+    want_k = F.quantize(rows.float().numpy(), _inv(ks))
+    got_k = kc.permute(0, 2, 1, 3).cpu().numpy()
+    for s in range(S):
+        b, o = divmod(int(slots[s]), B)
+        assert np.array_equal(got_k[b, o], want_k[s]), s
+    pool.close()
+
+
+def test_decode_fp8_per_head_small():
+    w = _small_workload(seed=16)
+    inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens, 4))
+    cap = H.tables_capacity(int(W.context_lengths(inp).max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    ks, vs = _head_scales(2, w.num_kv_heads)
+    kc, vc = _fill_fp8(inp, nat, ks, vs)
+    kp, vp = _oracle_codes(inp, orc, ks, vs)
+    outs, want = _decode_fp8_both(inp, nat, orc, kc, vc, kp, vp, ks, vs)
+    _check(outs, want, "fp8_per_head_small")
+    assert np.array_equal(outs["paged"], outs["contig"])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_fp8_per_head_random_shapes(seed):
+    """Random shapes as above with one scale per KV head."""
+    spec, _ = _fp8_shape(seed + 8)
+    w = W.WORKLOADS["llama3_8b_decode"].replace(name=f"fp8_ph_rand_{seed}",
+                                               seed=3100 + seed, **spec)
+    inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens))
+    ctx = W.context_lengths(inp)
+    cap = H.tables_capacity(int(ctx.max()), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    ks, vs = _head_scales(10 + seed, w.num_kv_heads)
+    kc, vc = _fill_fp8(inp, nat, ks, vs)
+    kp, vp = _oracle_codes(inp, orc, ks, vs)
+    outs, want = _decode_fp8_both(inp, nat, orc, kc, vc, kp, vp, ks, vs)
+    _log(f"{w.name} {spec} per-head scales contexts "
+         f"{int(ctx.min())}..{int(ctx.max())}")
+    _check(outs, want, w.name)
+    assert np.array_equal(outs["paged"], outs["contig"])
+
+
+def test_fp8_per_head_errors():
+    k = torch.zeros((2, 2, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((1, 2, 16, 128), dtype=torch.uint8, device="cuda")
+    slots = torch.zeros(2, dtype=torch.int64, device="cuda")
+    good = torch.ones(2, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):      # one scale per KV head
+        kv.kv_reshape_and_cache_fp8_per_head(
+            k, k, slots, kc, kc.clone(), torch.ones(3, device="cuda"), good)
+    with pytest.raises(TypeError):
+        kv.kv_reshape_and_cache_fp8_per_head(
+            k, k, slots, kc, kc.clone(), good.double(), good)
+    st = kv.lib().kv_reshape_and_cache_fp8_per_head(
+        k.data_ptr(), k.data_ptr(), slots.data_ptr(), 2, kc.data_ptr(),
+        kc.data_ptr(), 16, 16, 2, 128, None, good.data_ptr(), None)
+    assert st == kv.KV_EINVAL

@@ -1,7 +1,9 @@
 """Pins of the FP8 E4M3 codec (oracle/fp8.py) against the format's
 definition: code points of the OCP E4M3 table, the value range, round to
-nearest with ties to even, the clamp, and the exactness of dequantised
-values in bf16."""
+nearest with ties to even, the clamp, NaN kept as the NaN code, dequantised
+values worked by hand (per tensor and per KV head), torch's own
+float8_e4m3fn conversion on in-range values, and the exactness of
+dequantised values in bf16."""
 import numpy as np
 import pytest
 import torch
@@ -50,7 +52,7 @@ def test_quantize_clamps_in_fp32():
     x = np.array([1e6, -1e6, 449.0, 448.0, 300.0, np.nan], dtype=np.float32)
     got = fp8.quantize(x, 1.0).tolist()
     assert got[:5] == [0x7E, 0xFE, 0x7E, 0x7E, fp8.encode_value(288.0)]
-    assert got[5] == 0xFE                      # maxNum/minNum: NaN -> -448
+    assert got[5] == 0x7F                      # NaN stays NaN
     # the product is taken in fp32 before rounding
     x = np.array([3.0], dtype=np.float32)
     inv = np.float32(1 / 3.0)
@@ -63,3 +65,57 @@ def test_dequantised_values_are_exact_in_bf16():
                      if not np.isnan(fp8.decode(c))], dtype=np.float32)
     t = torch.from_numpy(vals)
     assert torch.equal(t.to(torch.bfloat16).float(), t)
+
+
+def test_nan_keeps_its_sign_and_infinities_saturate():
+    x = np.array([np.nan, -np.nan, np.inf, -np.inf], dtype=np.float32)
+    assert fp8.quantize(x, 0.25).tolist() == [0x7F, 0xFF, 0x7E, 0xFE]
+
+
+@pytest.mark.parametrize("code,scale,value", [
+    (0x38, 0.5, 0.5),                 # 1.0 * 0.5
+    (0x7E, 0.01, 4.48),               # 448 * 0.01
+    (0xB8, 2.0, -2.0),                # -1.0 * 2
+    (0x01, 4.0, 2.0 ** -7),           # 2^-9 * 4
+    (0x3C, 3.0, 4.5),                 # 1.5 * 3
+    (0xC4, 0.125, -0.375),            # -(1 + 4/8) * 2 * 0.125
+    (0x00, 7.0, 0.0),
+])
+def test_dequantize_by_hand(code, scale, value):
+    got = fp8.dequantize(np.array([code]), scale)[0]
+    assert got == pytest.approx(value, rel=1e-15, abs=0)
+
+
+def test_dequantize_nan_code_is_nan():
+    assert np.isnan(fp8.dequantize(np.array([0x7F, 0xFF]), 2.0)).all()
+
+
+def test_per_head_scales_by_hand():
+    # rows [T=1, Hkv=2, D=2]; head 0 scale 2 (inv 0.5), head 1 scale 0.25
+    # (inv 4): head 0 stores 1.0 * 0.5 = 0.5 (0x30) and 3.0 * 0.5 = 1.5
+    # (0x3C); head 1 stores 1.0 * 4 = 4 (0x48) and -0.5 * 4 = -2 (0xC0)
+    x = np.array([[[1.0, 3.0], [1.0, -0.5]]], dtype=np.float32)
+    inv = np.array([[0.5], [4.0]], dtype=np.float32)
+    codes = fp8.quantize(x, inv)
+    assert codes.tolist() == [[[0x30, 0x3C], [0x48, 0xC0]]]
+    back = fp8.dequantize(codes, np.array([[2.0], [0.25]]))
+    assert back.tolist() == [[[1.0, 3.0], [1.0, -0.5]]]
+
+
+def test_matches_torch_float8_e4m3fn_in_range():
+    # torch's conversion (round to nearest even) on fp32 products within the
+    # finite range, and on NaN; above 448 torch does not saturate, so those
+    # are left out (the saturation is this codec's stated reading)
+    rng = np.random.default_rng(3)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * 40,
+        rng.standard_normal(20000).astype(np.float32) * 0.02,
+        np.array([np.nan, -np.nan, 0.0, -0.0, 448.0, -448.0],
+                 dtype=np.float32)])
+    inv = np.float32(1.0 / 1.7)
+    prod = x * inv
+    keep = np.isnan(prod) | (np.abs(prod) <= 448.0)
+    x, prod = x[keep], prod[keep]
+    ref = torch.from_numpy(prod).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+    assert np.array_equal(fp8.quantize(x, inv), ref)

@@ -5,7 +5,9 @@ a dropped term, a wrong sign, a wrong or swapped index, an operand in the
 wrong place, the wrong end of a queue. The oracle's pins
 (test_oracle_pins.py and test_oracle_allocator.py) must fail on every one.
 The mutated oracle is a copy in a temporary directory, run in a child
-process; the repository's files are not modified.
+process; the repository's files are not modified. The pins that run are
+those of the attention oracle, the model allocator, the FP8 codec and the
+prefix-cache model.
 """
 import os
 import shutil
@@ -15,6 +17,8 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_allocator.py",
+             "test_oracle_fp8.py", "test_oracle_prefix_cache.py")
 
 MUTATIONS = [
     ("attention.py", "return h // (num_q_heads // num_kv_heads)",
@@ -45,6 +49,33 @@ MUTATIONS = [
     ("attention.py", "        pool[blk, off] = rows[r]",
      "        pool[off % pool.shape[0], blk % pool.shape[1]] = rows[r]",
      "scatter with transposed indices"),
+    ("attention.py", "        if slot < 0:\n            continue\n", "",
+     "padding slot written"),
+    ("fp8.py", "    return _VALUES[np.asarray(codes, dtype=np.int64)] * np.asarray(",
+     "    return _VALUES[np.asarray(codes, dtype=np.int64)] / np.asarray(",
+     "dequantise divides by the scale"),
+    ("fp8.py", "    return np.where(nan, nan_codes, out).astype(np.uint8)",
+     "    return out.astype(np.uint8)", "NaN stored as a finite code"),
+    ("fp8.py", "even = [c for c in tied if (c & 1) == 0]",
+     "even = [c for c in tied if (c & 1) == 1]", "ties to the odd code"),
+    ("fp8.py", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)",
+     "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)", "exponent bias 8"),
+    ("fp8.py",
+     "    prod = np.minimum(np.maximum(prod, np.float32(-MAX)), np.float32(MAX))\n",
+     "", "no saturation before rounding"),
+    ("fp8.py", "    prod = x32 * np.asarray(inv_scale, dtype=np.float32)",
+     "    prod = x32 * np.asarray(inv_scale, dtype=np.float32).T",
+     "per-head scales on the wrong axis"),
+    ("prefix_cache.py",
+     'data = struct.pack("<QQ", parent & MASK64, salt & MASK64)',
+     'data = struct.pack("<QQ", 0, salt & MASK64)', "key ignores the parent"),
+    ("prefix_cache.py",
+     "if e is None or e.parent != parent or e.tokens != toks:\n            return None",
+     "if e is None:\n            return None", "collision taken as a hit"),
+    ("prefix_cache.py", "for e in reversed(entries):", "for e in entries:",
+     "chains stamped head first"),
+    ("prefix_cache.py", "for _, k in cands[:max(0, n)]:",
+     "for _, k in cands[::-1][:max(0, n)]:", "most recent evicted first"),
     ("allocator.py", "ids = [self.free.popleft() for _ in range(n)]",
      "ids = [self.free.pop() for _ in range(n)]", "LIFO instead of FIFO"),
     ("allocator.py", "            if self.rc[b] == 0:\n                self.free.append(b)",
@@ -61,8 +92,7 @@ def _mutated_tree(tmp, fname, old, new):
     shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(tmp, "oracle"),
                     ignore=shutil.ignore_patterns("__pycache__"))
     os.makedirs(os.path.join(tmp, "tests"))
-    for f in ("conftest.py", "test_oracle_pins.py",
-              "test_oracle_allocator.py"):
+    for f in ("conftest.py",) + PIN_FILES:
         shutil.copy(os.path.join(ROOT, "tests", f),
                     os.path.join(tmp, "tests", f))
     shutil.copytree(os.path.join(ROOT, "tests", "golden"),
@@ -78,8 +108,7 @@ def _run_pins(tmp):
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     return subprocess.run(
         [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-         "-m", "not gpu", "tests/test_oracle_pins.py",
-         "tests/test_oracle_allocator.py"],
+         "-m", "not gpu"] + [os.path.join("tests", f) for f in PIN_FILES],
         cwd=tmp, env=env, capture_output=True, text=True, timeout=600)
 
 

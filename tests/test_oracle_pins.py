@@ -93,6 +93,18 @@ def test_slot_bijection():
                      for s, n in enumerate(lens) for p in range(n)]
 
 
+
+def test_scatter_skips_padding_slots():
+    # A negative slot is padding: nothing is written anywhere (in particular
+    # not at the pool's last slot, where a negative index would land).
+    pool = np.full((3, 4, 1, 2), np.nan)
+    rows = np.arange(8, dtype=np.float64).reshape(4, 1, 2)
+    O.scatter_rows(pool, rows, [-1, 5, -1, 2])
+    want = np.full((3, 4, 1, 2), np.nan)
+    want[1, 1] = rows[1]          # slot 5 = block 1, offset 1
+    want[0, 2] = rows[3]          # slot 2 = block 0, offset 2
+    assert np.array_equal(pool, want, equal_nan=True)
+
 # --------------------------------------------------------------- softmax --
 def _decimal_attend(q, K, V, scale):
     getcontext().prec = 50
