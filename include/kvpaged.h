@@ -248,6 +248,29 @@ kv_status paged_attn_decode(void* out, const void* q, const void* k_cache,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* paged_attn_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments and result as paged_attn_decode, without the
+ * workspace: the kernels use a scratch array of 16 MiB that the library
+ * holds in each GPU's memory from load until the process ends (found once
+ * per device with hipGetSymbolAddress). Calls allocate nothing (no
+ * hipMalloc, hipFree or allocating library routine). A shape whose
+ * workspace (kv_decode_workspace_bytes) exceeds 16 MiB -> KV_EINVAL. Every
+ * call on a GPU shares that GPU's scratch and leaves its contents behind:
+ * calls that overlap on one GPU (different streams, or threads) race and
+ * must be ordered by the caller. The clamp count of this call stays in the
+ * scratch (use paged_attn_decode to read it). */
+kv_status paged_attn_decode_noalloc(void* out, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    int32_t num_blocks,
+                                    const int32_t* block_tables,
+                                    int32_t bt_stride,
+                                    const int32_t* context_lens,
+                                    int32_t max_context, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    float scale, kv_dtype dtype, void* stream);
+
 /* Same on the contiguous layout [num_seqs, Hkv, seq_stride, D]. */
 kv_status contig_attn_decode(void* out, const void* q, const void* k,
                              const void* v, int32_t seq_stride,

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = ["host.cpp", "prefix_cache.cpp", "vcache.cpp", "cache_ops.hip",
-           "decode.hip", "prefill.hip"]
+           "decode.hip", "decode_noalloc.hip", "prefill.hip"]
 LIB = os.path.join(HERE, "libkvpaged.so")
 ARCH = os.environ.get("KVPAGED_ARCH", "gfx950")
 

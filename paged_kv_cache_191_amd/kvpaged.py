@@ -93,6 +93,9 @@ SIGNATURES = {
     "paged_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
                                  _I32, _I32, _I32, _I32, _I32, _F, _I32, _P,
                                  _SZ, _P]),
+    "paged_attn_decode_noalloc": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P,
+                                         _I32, _I32, _I32, _I32, _I32, _I32,
+                                         _F, _I32, _P]),
     "contig_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32,
                                   _I32, _I32, _I32, _F, _I32, _P, _SZ, _P]),
     "kv_decode_shared_prefix_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32,
@@ -698,6 +701,29 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         int(max_context), S, hq, hkv, d, bs, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "paged_attn_decode")
+
+
+def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables,
+                              context_lens, max_context: int, scale: float,
+                              stream=None) -> None:
+    """paged_attn_decode on the library's per-device scratch: nothing is
+    allocated (for callers that cannot allocate, e.g. under graph
+    capture). Overlapping calls on one GPU race."""
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, hkv, bs, dk = k_cache.shape
+    _attn_shapes(out, q, k_cache, v_cache, dk, S,
+                 ((block_tables, "block_tables"),
+                  (context_lens, "context_lens")))
+    _ndim(block_tables, 2, "block_tables")
+    st = lib().paged_attn_decode_noalloc(
+        _dev(out, "out", q.dtype), _dev(q, "q"),
+        _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
+        nb, _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context), S, hq, hkv, d, bs, float(scale), _dtype_code(q),
+        _stream(stream))
+    _check(st, "paged_attn_decode_noalloc")
 
 
 def paged_attn_decode_fp8(out, q, k_cache, v_cache, block_tables,

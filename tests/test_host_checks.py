@@ -118,3 +118,25 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_noalloc_decode_rejects_oversized_workspace():
+    """paged_attn_decode_noalloc refuses a shape whose workspace exceeds its
+    16 MiB scratch before touching any device (forced here by a huge chunk
+    count; host logic only, in a child process so that the override is read
+    fresh)."""
+    code = (
+        "import ctypes\n"
+        "from paged_kv_cache_191_amd import kvpaged as kv\n"
+        "f = kv.lib().paged_attn_decode_noalloc\n"
+        "p = ctypes.c_void_p(16)\n"
+        "st = f(p, p, p, p, 4, p, 4, p, 64, 2, 32, 8, 128, 16, 0.1, "
+        "kv.KV_BF16, None)\n"
+        "print(st, kv.kv_last_error())\n")
+    env = dict(os.environ, KVPAGED_DECODE_CHUNKS="100000")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    st, msg = r.stdout.split(" ", 1)
+    assert int(st) == kv.KV_EINVAL
+    assert "scratch" in msg
