@@ -1,6 +1,34 @@
 """Benchmark of the paged-KV hot path on one MI355X.
 
-A step is one decode step of a batch of sequences, each growing by one token:
+The default run measures every configuration of the workload set, each
+against its kernel's roofline, next to its contiguous (vAttention layout)
+counterpart, and next to the fp64 CPU oracle timed on a bounded sample:
+
+  decode_tiny_f32      4 sequences (contexts 35, 16, 1, 100), 8/8 heads,
+                       head_dim 64, fp32, block 16: the generic decode path,
+                       latency-bound (time only, no roofline claim);
+  llama3_8b_decode     (the headline) 64 sequences, 32 q / 8 kv heads,
+                       block 16, contexts uniform in 512..4096; paged,
+                       contiguous, contiguous on demand-mapped memory, and
+                       paged over fp8 E4M3 caches with per-head scales;
+  yi6b_chunked_prefill 4 x 32768 tokens in 2048-token chunks, 32 q / 4 kv
+                       heads, causal: paged B=16, paged B=64, contiguous,
+                       contiguous on demand-mapped memory;
+  yi34b_long_decode    4 sequences of 196608 tokens, 56 q / 8 kv heads,
+                       block 64 (split-K over the context); paged,
+                       contiguous, demand-mapped, fp8;
+  prefix_share_decode  256 sequences sharing a 4096-token prefix (256 blocks
+                       at refcount 256, written once) plus own suffixes
+                       uniform in 64..1024, 32 q / 8 kv heads, block 16: the
+                       shared-prefix decode, plain paged decode, contiguous
+                       (prefix copied per sequence), and the copy-on-write
+                       case (a 4104-token prefix whose last block is half
+                       full, copied by 255 of the 256 sequences);
+  block_swap           2048 blocks out to pinned host memory and back.
+All values are synthetic N(0, 1) bf16 (U[-1, 1) fp32 for the small decode)
+of the model layers the vAttention evaluation names; head_dim 128.
+
+A decode step is one step of a batch of sequences, each growing by one token:
   host   kv_seq_append: allocation when a block fills (copy-on-write of a
          shared, partly filled block), slot mapping; the block ids it took
          go to a pinned int32 [S] buffer;
@@ -9,42 +37,30 @@ A step is one decode step of a batch of sequences, each growing by one token:
          K/V, length + 1; the table and lengths stay on the device),
          paged_attn_decode (stream-K partitions + exact merge).
 The contiguous layouts take the same kernel with one "block" per sequence;
-the fp8 decode its fp8 form (kv_append_token_fp8).
+the fp8 decode its fp8 form (kv_append_token_fp8_per_head).
 Four independent replicas of the whole batch (pools, tables, queries) rotate
 so that no step finds its K/V in the 256 MB last-level cache.
 
-Workloads (--workload; shapes of the model layers the vAttention evaluation
-names, synthetic N(0, 1) bf16 values, head_dim 128):
-  llama3_8b_decode     (default) 64 sequences, 32 q / 8 kv heads, block 16,
-                       contexts uniform in 512..4096;
-  yi34b_long_decode    4 sequences of 196608 tokens, 56 q / 8 kv heads,
-                       block 64;
-  prefix_share_decode  256 sequences sharing a 4096-token prefix (256 blocks
-                       at refcount 256, written once) plus own suffixes
-                       uniform in 64..1024, 32 q / 8 kv heads, block 16; also
-                       the copy-on-write case: a 4104-token prefix whose last
-                       block is half full, so the first appended token of
-                       255 of the 256 sequences copies it.
-
-`value` = decode algorithmic bytes (K+V once per KV head, q, o, block-table
-entries, lengths) summed over the timed steps / wall time of those steps.
-With a shared prefix the prefix counts once (unique bytes); the bytes the
-sequences read logically are reported beside it as "effective" GB/s, which
-can exceed the HBM peak because the shared blocks are served from cache.
-The same JSON line carries:
-  roofline     - the decode op alone (HIP events around each call on its
-                 stream) against 8 TB/s, with the HBM traffic counted by
-                 hardware counters when they were taken on these sources;
-  contig       - the same steps on the contiguous layout, and the
-                 paged-vs-contiguous time of the decode op;
-  prefill      - (default workload) one chunked-prefill pass of the
-                 Yi-6B-shaped workload (4 x 32768 tokens, 2048-token chunks,
-                 32/4 heads) per layout (paged B=16, paged B=64, contiguous):
-                 TFLOP/s of the attention calls against 2.5 PFLOP/s bf16;
-  memory       - block-internal waste of the paged pool next to the
-                 contiguous reservation's;
-  cpu_baseline - the fp64 oracle on this host's cores on the same decode
-                 workload (all threads, then one).
+`value` = decode algorithmic bytes of the headline workload (K+V once per KV
+head, q, o, block-table entries, lengths) summed over the timed steps / wall
+time of those steps. With a shared prefix the prefix counts once (unique
+bytes); the bytes the sequences read logically are reported beside it as
+"effective" GB/s, which can exceed the HBM peak because the shared blocks are
+served from cache. The same JSON line carries:
+  roofline      - the headline decode op (HIP events around each call on its
+                  stream) against 8 TB/s, with the HBM traffic counted by
+                  hardware counters when they were taken on these sources;
+  rooflines     - the same record for every other measured kernel: decode
+                  ops of each workload and layout, the prefill passes
+                  (algorithmic FLOPs against 2.5 PFLOP/s bf16), the cache
+                  writes and the copy-on-write block copy;
+  prefill       - the paged B=16 prefill's roofline record, with every
+                  layout's figures beside it;
+  paged_vs_contig_overhead - (t_paged - t_contig) / t_contig per
+                  configuration (per block size for the prefill);
+  cpu_oracle    - the fp64 oracle, single-threaded, per configuration;
+  cpu_baseline  - the headline workload's entry of cpu_oracle;
+  configs       - every figure of every configuration.
 """
 from __future__ import annotations
 
@@ -83,9 +99,6 @@ VMM_PREFILL_PAGE_TOKENS = 1024
 # pages one process maps at most in a decode run (each page is one device
 # allocation; larger pages are used when the contexts would need more)
 VMM_MAX_PAGES = 16384
-# per-tensor scale of the fp8 E4M3 caches: N(0, 1) K/V values up to about
-# 5.5 land near the format's largest finite value, 448
-FP8_SCALE = 0.0123
 
 TRAFFIC_PROFILES = {
     "llama3_8b_decode": os.path.join(ROOT, "profiles",
@@ -97,11 +110,11 @@ TRAFFIC_PROFILES = {
 }
 
 
-def recorded_traffic(workload: str = "llama3_8b_decode"):
+def recorded_traffic(workload: str = "llama3_8b_decode", fp8: bool = False):
     """HBM bytes per decode launch from the committed counter summary
-    (FETCH_SIZE/WRITE_SIZE, calibrated on a plain copy), or None when no
-    summary exists for the workload or the decode sources differ from the
-    ones the counters were taken on."""
+    (FETCH_SIZE/WRITE_SIZE, calibrated on a plain copy; the fp8 op's line
+    when `fp8`), or None when no summary exists for the workload or the
+    decode sources differ from the ones the counters were taken on."""
     import hashlib
     path = TRAFFIC_PROFILES.get(workload)
     if path is None:
@@ -111,8 +124,10 @@ def recorded_traffic(workload: str = "llama3_8b_decode"):
     except OSError:
         return None
     value = None
+    key = ("fp8_traffic_bytes_per_launch:" if fp8 else
+           "traffic_bytes_per_launch:")
     for line in text:
-        if line.startswith("traffic_bytes_per_launch:"):
+        if line.startswith(key):
             value = int(line.split(":")[1])
         elif line.startswith("source_sha256 "):
             rel, digest = line[len("source_sha256 "):].rsplit(": ", 1)
@@ -173,7 +188,7 @@ class DecodeReplica:
 
     def __init__(self, inp, k_dev, v_dev, new_k, new_v, paged: bool,
                  steps: int, device, shared_op: bool = False,
-                 vmm_page_tokens: int = 0, fp8: bool = False):
+                 vmm_page_tokens: int = 0, fp8_scales=None):
         import torch
         from paged_kv_cache_191_amd import kvpaged as kv
         from paged_kv_cache_191_amd import workloads as W
@@ -206,10 +221,11 @@ class DecodeReplica:
         self.out = torch.empty_like(self.q)
         self.new_k, self.new_v = new_k, new_v
         tdt = inp.k.dtype
-        # fp8 E4M3 caches (paged only), one scale per tensor
-        self.fp8 = fp8 and paged
+        # fp8 E4M3 caches (paged only), one scale per KV head
+        self.fp8 = fp8_scales is not None and paged
         if self.fp8:
             tdt = torch.uint8
+            self.k_scales, self.v_scales = fp8_scales
         self.h_table[:] = -1
         self.h_lens[:] = 0
         self.shared = 0
@@ -229,9 +245,9 @@ class DecodeReplica:
                     W.logical_rows(inp, s)[first:first + count]).to(device)
                 d_slots = torch.from_numpy(slots).to(device)
                 if self.fp8:
-                    kv.kv_reshape_and_cache_fp8(k_dev[rows], v_dev[rows],
-                                                d_slots, self.k, self.v,
-                                                FP8_SCALE, FP8_SCALE)
+                    kv.kv_reshape_and_cache_fp8_per_head(
+                        k_dev[rows], v_dev[rows], d_slots, self.k, self.v,
+                        self.k_scales, self.v_scales)
                 else:
                     kv.kv_reshape_and_cache(k_dev[rows], v_dev[rows],
                                             d_slots, self.k, self.v)
@@ -351,9 +367,9 @@ class DecodeReplica:
         a new one) is recorded after it and marks the pinned buffer free."""
         kv = self.kv
         if self.fp8:
-            kv.kv_append_token_fp8(self.new_k, self.new_v, self.h_newb,
-                                   self.a_table, self.d_lens, self.k, self.v,
-                                   FP8_SCALE, FP8_SCALE)
+            kv.kv_append_token_fp8_per_head(
+                self.new_k, self.new_v, self.h_newb, self.a_table,
+                self.d_lens, self.k, self.v, self.k_scales, self.v_scales)
         else:
             kv.kv_append_token(self.new_k, self.new_v, self.h_newb,
                                self.a_table, self.d_lens, self.k, self.v)
@@ -367,10 +383,9 @@ class DecodeReplica:
         self.cache_write(ev[0] if ev is not None else None)
         max_ctx = int(self.h_lens.max())
         if self.fp8:
-            kv.paged_attn_decode_fp8(self.out, self.q, self.k, self.v,
-                                     self.d_table, self.d_lens, max_ctx,
-                                     self.scale, FP8_SCALE, FP8_SCALE,
-                                     self.ws)
+            kv.paged_attn_decode_fp8_per_head(
+                self.out, self.q, self.k, self.v, self.d_table, self.d_lens,
+                max_ctx, self.scale, self.k_scales, self.v_scales, self.ws)
         elif self.shared_op:
             kv.paged_attn_decode_shared_prefix(
                 self.out, self.q, self.k, self.v, self.d_table, self.d_lens,
@@ -397,6 +412,14 @@ def new_token_kv(w, device):
     return mk[0], mk[1]
 
 
+def fp8_head_scales(k_dev, v_dev):
+    """Per-KV-head scales of the fp8 caches: the largest |value| of each
+    head over the workload's rows maps to E4M3's largest finite value, 448
+    (set-up, before the timed steps)."""
+    return tuple((t.abs().amax(dim=(0, 2)).float() / 448.0).contiguous()
+                 for t in (k_dev, v_dev))
+
+
 def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
                device, shared_op: bool = False, vmm_page_tokens: int = 0,
                fp8: bool = False):
@@ -404,10 +427,10 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     w = inp.workload
     new_k, new_v = new_token_kv(w, device)
     k_dev, v_dev = inp.k.to(device), inp.v.to(device)
+    scales = fp8_head_scales(k_dev, v_dev) if fp8 else None
     reps_ = [DecodeReplica(inp, k_dev, v_dev, new_k, new_v, paged,
                            steps + warmup + APPEND_TIMING_STEPS, device,
-                           shared_op,
-                           vmm_page_tokens, fp8)
+                           shared_op, vmm_page_tokens, scales)
              for _ in range(reps)]
     del k_dev, v_dev
     for i in range(warmup):
@@ -456,7 +479,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         "decode_op_ms_p90": op["p90"],
         "bytes_per_step": total_bytes / steps,
         "cache_write": "kv_append_token" if not fp8 else
-                       "kv_append_token_fp8",
+                       "kv_append_token_fp8_per_head",
         "cache_write_us_median": 1e3 * rc["median"],
     }
     res["decode_op_GBps"] = res["bytes_per_step"] / (op["mean"] * 1e-3) / 1e9
@@ -495,6 +518,9 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
             "waste_64KiB_pages": 1.0 - used / mapped_with(64 << 10),
             "waste_2MiB_pages": 1.0 - used / mapped_with(2 << 20),
         }
+    if fp8:
+        res["fp8_k_scales"] = [round(float(x), 6) for x in scales[0].cpu()]
+        res["fp8_v_scales"] = [round(float(x), 6) for x in scales[1].cpu()]
     for r in reps_:
         r.close()
     del reps_
@@ -812,71 +838,337 @@ def memory_waste(inp, lmax_reserved: int) -> dict:
             "contig_reserved_over_paged_held": round(reserved / held, 3)}
 
 
-def cpu_baseline(inp, budget_s: float = 12.0):
-    """The fp64 oracle (as it stands) on this host: paged decode of the
-    same workload, gather + conversion + attention timed, pool build not.
-    Timed with every BLAS thread, then with one."""
-    from oracle import allocator as A
-    from oracle import attention as O
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] +
-                      [1])
-    except Exception:
-        threadpool_limits = None
-        threads = 1
-    w = inp.workload
-    B = w.block_size
-    S = w.num_seqs
-    pool = A.ModelPool(len(inp.free_order), B, inp.free_order)
-    tables, lens = [[] for _ in range(S)], [0] * S
-    st, slots, _ = A.append_tokens(pool, tables, lens, inp.lengths.tolist(),
-                                   1 << 30)
-    assert st == A.OK
-    kp = np.zeros((len(inp.free_order), B, w.num_kv_heads, w.head_dim),
-                  dtype=np.float32)
-    vp = np.zeros_like(kp)
-    O.scatter_rows(kp, inp.k.float().numpy(), slots)
-    O.scatter_rows(vp, inp.v.float().numpy(), slots)
-    q = inp.q.float().numpy()
-    scale = 1.0 / float(np.sqrt(w.head_dim))
-
-    def timed(budget):
-        done, nbytes = 0, 0
-        t0 = time.perf_counter()
-        while True:
-            s = done % S
-            O.decode_paged(q, kp, vp, tables, lens, scale, seqs=[s])
-            nbytes += decode_bytes(np.array([lens[s]]), w.num_q_heads,
-                                   w.num_kv_heads, w.head_dim, B, True)
-            done += 1
-            if time.perf_counter() - t0 >= budget:
-                break
-        return done, nbytes, time.perf_counter() - t0
-
-    done, nbytes, dt = timed(budget_s)
-    one = None
-    if threadpool_limits is not None and threads > 1:
-        with threadpool_limits(limits=1):
-            d1, b1, t1 = timed(budget_s / 3)
-        one = round(b1 / t1 / 1e9, 4)
-    cpu_model = ""
+# ---------------------------------------------------------------------------
+# The fp64 oracle on this host (a reported baseline, not the target)
+# ---------------------------------------------------------------------------
+def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
+    return ""
+
+
+def _one_thread():
+    """A context that holds NumPy's BLAS pools at one thread: the oracle's
+    time goes to its per-token gather loop in Python, which runs on one core
+    whatever the BLAS threads (more threads measured slower)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except Exception:                                  # noqa: BLE001
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def _oracle_pool(inp, seqs, upto=None):
+    """The oracle's model allocator over the whole workload (host metadata
+    only) and float32 pools holding the rows of `seqs` (the prefix, if any,
+    written once by sequence 0 and shared by fork). Set-up, not timed."""
+    from oracle import allocator as A
+    from oracle import attention as O
+    from paged_kv_cache_191_amd import workloads as W
+    w = inp.workload
+    S, B = w.num_seqs, w.block_size
+    ctx = W.context_lengths(inp)
+    if upto is not None:
+        ctx = np.minimum(ctx, upto)
+    pool = A.ModelPool(len(inp.free_order), B, inp.free_order)
+    tables, lens = [[] for _ in range(S)], [0] * S
+    kp = np.zeros((len(inp.free_order), B, w.num_kv_heads, w.head_dim),
+                  dtype=np.float32)
+    vp = np.zeros_like(kp)
+    wanted = set(int(s) for s in seqs)
+    P = int(inp.prefix_rows)
+
+    def write(s, first, count, store):
+        n_new = [0] * S
+        n_new[s] = count
+        st, slots, _ = A.append_tokens(pool, tables, lens, n_new, 1 << 30)
+        assert st == A.OK
+        if store and count:
+            rows = W.logical_rows(inp, s)[first:first + count]
+            O.scatter_rows(kp, inp.k[rows].float().numpy(), slots)
+            O.scatter_rows(vp, inp.v[rows].float().numpy(), slots)
+
+    if P:
+        write(0, 0, P, True)
+        nb = O.blocks_needed(P, B)
+        for s in range(1, S):
+            assert pool.share(tables[0][:nb]) == A.OK
+            tables[s] = list(tables[0][:nb])
+            lens[s] = P
+    for s in range(S):
+        write(s, lens[s], int(ctx[s]) - lens[s], s in wanted)
+    return tables, lens, kp, vp
+
+
+def oracle_decode_rate(inp, seqs, budget_s: float):
+    """The oracle's paged decode (gather through the table, bf16 -> fp64,
+    attention) of the sequences `seqs`, cycled until `budget_s` has passed;
+    GB/s of the K/V, q, o and table bytes it reads (a shared prefix counts
+    once per sequence: the oracle has no sharing)."""
+    from oracle import attention as O
+    w = inp.workload
+    tables, lens, kp, vp = _oracle_pool(inp, seqs)
+    q = inp.q.float().numpy()
+    scale = 1.0 / float(np.sqrt(w.head_dim))
+    esize = 4 if w.dtype == "f32" else 2
+    done, nbytes = 0, 0
+    with _one_thread():
+        t0 = time.perf_counter()
+        while True:
+            s = int(seqs[done % len(seqs)])
+            O.decode_paged(q, kp, vp, tables, lens, scale, seqs=[s])
+            nbytes += decode_bytes(np.array([lens[s]]), w.num_q_heads,
+                                   w.num_kv_heads, w.head_dim, w.block_size,
+                                   True, esize=esize)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{done} sequence decodes of the {w.name} batch "
-                      f"({done / S:.2f} passes over its {S} sequences), "
-                      f"{dt:.1f} s of fp64 oracle time (gather through the "
-                      f"table, bf16->fp64, attention)",
-            "value_one_thread": one, "nproc": os.cpu_count(),
-            "cpu_model": cpu_model}
+            "cores": 1, "kind": "oracle",
+            "sample": f"{done} sequence decodes over sequences "
+                      f"{sorted(set(int(x) for x in seqs))[:8]}"
+                      f"{'...' if len(set(seqs)) > 8 else ''} of the "
+                      f"{w.name} batch, {dt:.1f} s of fp64 oracle time on one "
+                      f"thread (gather through the table, bf16->fp64, "
+                      f"attention)",
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
+
+
+def oracle_prefill_rate(inp, budget_s: float):
+    """The oracle's chunked prefill of sampled query rows of the last chunk
+    of sequence 0 (the heaviest rows: each sees up to 32768 keys), one call
+    per row, cycled until `budget_s` has passed; GFLOP/s of the rows'
+    algorithmic work (4 d Hq per visible key). The time covers the
+    oracle's gather of the sequence's K/V through the table and its
+    attention."""
+    from oracle import attention as O
+    w = inp.workload
+    C = w.chunk
+    N = int(inp.lengths[0])
+    tables, lens, kp, vp = _oracle_pool(inp, [0])
+    c0 = N - C
+    rows_all = np.arange(c0, N)
+    sample = rows_all[np.linspace(0, C - 1, 8).astype(int)]
+    q = inp.q[int(inp.cu[0]) + c0:int(inp.cu[0]) + N].float().numpy()
+    scale = 1.0 / float(np.sqrt(w.head_dim))
+    cu = [0, C]
+    done, flops = 0, 0.0
+    with _one_thread():
+        t0 = time.perf_counter()
+        while True:
+            p = int(sample[done % len(sample)])
+            O.prefill_paged(q, cu, [c0], kp, vp, tables[:1], [N], scale,
+                            True, rows=[p - c0])
+            flops += 4.0 * w.head_dim * w.num_q_heads * (p + 1)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e9, 4), "unit": "GFLOP/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{done} query rows (all 32 heads) at positions "
+                      f"{c0}..{N - 1} of sequence 0's last chunk, one oracle "
+                      f"call each, {dt:.1f} s of fp64 oracle time on one "
+                      f"thread (gather of the sequence's K/V through the "
+                      f"table, bf16->fp64, causal attention); the whole "
+                      f"pass is {35.185:.3f} TFLOP",
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
+
+
+# ---------------------------------------------------------------------------
+# Records
+# ---------------------------------------------------------------------------
+def roofline_record(bound: str, achieved: float, peak: float, unit: str,
+                    traffic=None, **extra) -> dict:
+    r = {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
+         "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic}
+    r.update(extra)
+    return r
+
+
+DECODE_KERNEL = "paged_attn_decode (decode_sk_kernel + decode_combine_kernel)"
+SHARED_KERNEL = ("paged_attn_decode_shared_prefix (prefill_pp_kernel<true,"
+                 "true> + decode_sk_kernel + decode_combine_kernel)")
+
+
+def decode_roofline(res: dict, kernel: str, traffic=None) -> dict:
+    return roofline_record(
+        "hbm", res["decode_op_GBps"], HBM_PEAK_GBPS, "GB/s", traffic,
+        kernel=kernel, bytes_per_launch=int(res["bytes_per_step"]),
+        ms_per_launch=round(res["decode_op_ms_mean"], 4))
+
+
+def overhead(t_paged: float, t_contig: float) -> float:
+    return round(t_paged / t_contig - 1.0, 4)
+
+
+def nested_round(d):
+    if isinstance(d, dict):
+        return {k: nested_round(v) for k, v in d.items()}
+    if isinstance(d, float):
+        return round(d, 4)
+    return d
+
+
+CTX_DESC = {"llama3_8b_decode": "U{512..4096}",
+            "yi34b_long_decode": "196608",
+            "prefix_share_decode": "4096 shared + U{64..1024}"}
+LMAX_RESERVED = {"llama3_8b_decode": 4096, "yi34b_long_decode": 196608,
+                 "prefix_share_decode": 4096 + 1024}
+
+
+def bench_decode_config(name: str, args, device) -> dict:
+    """Every layout of one decode workload, with its rooflines, the
+    paged-vs-contiguous overhead and the oracle's rate."""
+    from paged_kv_cache_191_amd import kvpaged as kv
+    from paged_kv_cache_191_amd import workloads as W
+    wd = W.WORKLOADS[name]
+    headroom = wd.num_seqs * (-(-(args.steps + args.warmup +
+                                  APPEND_TIMING_STEPS) // wd.block_size) + 1)
+    log(f"{name}: drawing")
+    inp = W.draw(wd, lambda L: pool_blocks(kv, wd, L, headroom))
+    runs = {}
+    prefix = wd.kind == "prefix"
+    log(f"{name}: paged decode steps")
+    runs["paged"] = run_decode(inp, True, args.steps, args.warmup,
+                               args.replicas, device, shared_op=prefix)
+    if prefix:
+        log(f"{name}: paged decode steps without prefix sharing")
+        runs["paged_without_sharing"] = run_decode(
+            inp, True, args.steps, args.warmup, args.replicas, device)
+    if not args.no_contig:
+        log(f"{name}: contiguous decode steps")
+        runs["contig"] = run_decode(inp, False, args.steps, args.warmup,
+                                    args.replicas, device)
+        if not args.no_vmm and not prefix:
+            log(f"{name}: contiguous decode steps on demand-mapped memory")
+            ctx = W.context_lengths(inp)
+            pt = args.vmm_page_tokens
+            while args.replicas * 2 * wd.num_kv_heads * int(
+                    np.sum(-(-(ctx + args.steps + args.warmup) // pt))) \
+                    > VMM_MAX_PAGES:
+                pt *= 2
+            try:
+                runs["contig_demand_mapped"] = run_decode(
+                    inp, False, args.steps, args.warmup, args.replicas,
+                    device, vmm_page_tokens=pt)
+            except kv.KVError as e:
+                log(f"demand-mapped decode failed: {e}")
+                runs["contig_demand_mapped"] = {"error": str(e)}
+    if not args.no_fp8 and not prefix:
+        log(f"{name}: paged decode steps over fp8 caches (per-head scales)")
+        runs["paged_fp8"] = run_decode(inp, True, args.steps, args.warmup,
+                                       args.replicas, device, fp8=True)
+    cow = None
+    if prefix and not args.no_cow:
+        log(f"{name}: copy-on-write step")
+        cow = run_cow(wd, args.steps, args.warmup, device)
+
+    paged = runs["paged"]
+    rl = {name: decode_roofline(paged, SHARED_KERNEL if prefix else
+                                DECODE_KERNEL, recorded_traffic(name))}
+    if "paged_without_sharing" in runs:
+        rl[name + "_without_sharing"] = decode_roofline(
+            runs["paged_without_sharing"], DECODE_KERNEL)
+    if "contig" in runs:
+        rl[name + "_contig"] = decode_roofline(
+            runs["contig"], "contig_attn_decode (decode_sk_kernel + "
+            "decode_combine_kernel)")
+    vm = runs.get("contig_demand_mapped")
+    if vm and "error" not in vm:
+        rl[name + "_contig_demand_mapped"] = decode_roofline(
+            vm, "contig_attn_decode on demand-mapped memory")
+    if "paged_fp8" in runs:
+        rl[name + "_fp8"] = decode_roofline(
+            runs["paged_fp8"], "paged_attn_decode_fp8_per_head "
+            "(decode_sk_kernel<true,true> + decode_combine_kernel)",
+            recorded_traffic(name, fp8=True))
+    if prefix:
+        # headline bytes: the shared prefix once (unique); the plain decode
+        # reads it once per sequence, mostly from cache
+        rl[name]["bytes"] = "unique"
+        rl[name + "_without_sharing"]["bytes"] = "unique"
+        if name + "_contig" in rl:
+            rl[name + "_contig"]["bytes"] = "logical (prefix per sequence)"
+    if cow:
+        rl["copy_blocks_cow"] = roofline_record(
+            "hbm", cow["copy_blocks_GBps"], HBM_PEAK_GBPS, "GB/s",
+            kernel="kv_copy_blocks (copy_blocks_kernel)",
+            us_per_launch=round(cow["copy_blocks_us_median"], 3),
+            blocks=cow["cow_copies"])
+    ovh = {}
+    if "contig" in runs:
+        ovh[name] = overhead(paged["decode_op_ms_mean"],
+                             runs["contig"]["decode_op_ms_mean"])
+        if prefix:
+            ovh[name + "_without_sharing"] = overhead(
+                runs["paged_without_sharing"]["decode_op_ms_mean"],
+                runs["contig"]["decode_op_ms_mean"])
+    if vm and "error" not in vm:
+        ovh[name + "_vs_demand_mapped"] = overhead(
+            paged["decode_op_ms_mean"], vm["decode_op_ms_mean"])
+    out = {"inp": inp, "runs": runs, "rooflines": rl, "overhead": ovh,
+           "cow": cow, "memory": memory_waste(inp, LMAX_RESERVED[name])}
+    if "paged_fp8" in runs:
+        out["fp8_speedup_vs_bf16"] = round(
+            paged["decode_op_ms_mean"] /
+            runs["paged_fp8"]["decode_op_ms_mean"], 4)
+    return out
+
+
+def bench_prefill(args, device) -> dict:
+    from paged_kv_cache_191_amd import kvpaged as kv
+    from paged_kv_cache_191_amd import workloads as W
+    layouts = {}
+    wanted = args.prefill_layouts.split(",")
+    pin16 = None
+    for name, layout in (("yi6b_chunked_prefill_b16", "paged_b16"),
+                         ("yi6b_chunked_prefill_b64", "paged_b64"),
+                         ("yi6b_chunked_prefill_b16", "contig"),
+                         ("yi6b_chunked_prefill_b16", "contig_vmm")):
+        if layout not in wanted:
+            continue
+        wp = W.WORKLOADS[name]
+        log(f"prefill {layout}")
+        pin = W.draw(wp, lambda L: pool_blocks(kv, wp, L))
+        if layout == "paged_b16":
+            pin16 = pin
+        r = prefill_pass(pin, {"contig": "contig", "contig_vmm": "vattn"}
+                         .get(layout, "paged"), device)
+        r["frac_of_peak"] = r["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+        layouts[layout] = r
+    kernels = {"paged_b16": "paged_attn_prefill (prefill_pp_kernel<true,"
+                            "false,true>)",
+               "paged_b64": "paged_attn_prefill (prefill_pp_kernel<true,"
+                            "false,true>)",
+               "contig": "contig_attn_prefill (prefill_pp_kernel<false,"
+                         "false,false>)",
+               "contig_vmm": "contig_attn_prefill on demand-mapped memory"}
+    rl, ovh = {}, {}
+    for lay, r in layouts.items():
+        rl["yi6b_chunked_prefill_" + lay] = roofline_record(
+            "mfma", r["TFLOPs"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
+            kernel=kernels[lay], tflop_per_pass=round(r["tflop"], 4),
+            ms_per_pass=round(r["attn_ms"], 4))
+        # the chunk's cache write: 2 x (read + write) of the new rows
+        rl["yi6b_reshape_and_cache_" + lay] = roofline_record(
+            "hbm", r["reshape_and_cache_GBps"], HBM_PEAK_GBPS, "GB/s",
+            kernel="kv_reshape_and_cache (scatter_rows_kernel)",
+            us_per_launch=round(r["reshape_and_cache_us_median"], 3))
+    if "contig" in layouts:
+        for lay in ("paged_b16", "paged_b64", "contig_vmm"):
+            if lay in layouts:
+                ovh["yi6b_chunked_prefill_" + lay] = overhead(
+                    layouts[lay]["attn_ms"], layouts["contig"]["attn_ms"])
+    return {"layouts": layouts, "rooflines": rl, "overhead": ovh,
+            "inp": pin16}
 
 
 def calibration_copy(device) -> None:
@@ -891,18 +1183,25 @@ def calibration_copy(device) -> None:
     torch.cuda.empty_cache()
 
 
+ALL_CONFIGS = ("decode_tiny_f32", "llama3_8b_decode", "yi6b_chunked_prefill",
+               "yi34b_long_decode", "prefix_share_decode", "block_swap")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=4)
-    ap.add_argument("--workload", default="llama3_8b_decode",
-                    choices=DECODE_WORKLOADS)
+    ap.add_argument("--configs", default=",".join(ALL_CONFIGS),
+                    help="configurations to run (default: all)")
+    ap.add_argument("--workload", default=None, choices=DECODE_WORKLOADS,
+                    help="run this decode workload only (no prefill, no "
+                         "other configuration); for profiling")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
-                    help="skip the decode steps (prefill / profiling runs); "
-                         "no bench line is printed")
+                    help="skip the decode configurations (prefill / "
+                         "profiling runs); no bench line is printed")
     ap.add_argument("--prefill-layouts",
                     default="paged_b16,paged_b64,contig,contig_vmm")
     ap.add_argument("--no-contig", action="store_true")
@@ -917,7 +1216,8 @@ def main() -> int:
                     help="skip the paged decode over fp8 E4M3 caches")
     ap.add_argument("--no-cow", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=4.0,
+                    help="seconds of oracle time per configuration")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference "
                          "kernel for hardware traffic counters)")
@@ -933,112 +1233,105 @@ def main() -> int:
 
     import torch
     from paged_kv_cache_191_amd import kvpaged as kv
-    from paged_kv_cache_191_amd import workloads as W
     kv.lib()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     device = torch.device("cuda:0")
-
     if args.calibration_copy:
         calibration_copy(device)
 
-    wd = W.WORKLOADS[args.workload]
-    default_workload = args.workload == "llama3_8b_decode"
-    headroom = wd.num_seqs * (-(-(args.steps + args.warmup +
-                                  APPEND_TIMING_STEPS) // wd.block_size)
-                              + 1)
-    paged = contig = inp = cow = plain = vattn = swap = fp8 = tiny = None
-    if not args.no_decode:
-        log(f"drawing {wd.name}")
-        inp = W.draw(wd, lambda L: pool_blocks(kv, wd, L, headroom))
-        log("paged decode steps")
-        shared_op = wd.kind == "prefix"
-        paged = run_decode(inp, True, args.steps, args.warmup, args.replicas,
-                           device, shared_op)
-        if shared_op:
-            log("paged decode steps without prefix sharing")
-            plain = run_decode(inp, True, args.steps, args.warmup,
-                               args.replicas, device)
-        if not args.no_contig:
-            log("contiguous decode steps")
-            contig = run_decode(inp, False, args.steps, args.warmup,
-                                args.replicas, device)
-            if not args.no_vmm and wd.kind != "prefix":
-                log("contiguous decode steps on demand-mapped memory")
-                ctx = W.context_lengths(inp)
-                pt = args.vmm_page_tokens
-                while args.replicas * 2 * wd.num_kv_heads * int(
-                        np.sum(-(-(ctx + args.steps + args.warmup) // pt))) \
-                        > VMM_MAX_PAGES:
-                    pt *= 2
-                try:
-                    vattn = run_decode(inp, False, args.steps, args.warmup,
-                                       args.replicas, device,
-                                       vmm_page_tokens=pt)
-                except kv.KVError as e:
-                    log(f"demand-mapped decode failed: {e}")
-                    vattn = {"error": str(e)}
-        if not args.no_fp8 and wd.kind != "prefix":
-            log("paged decode steps over fp8 caches")
-            fp8 = run_decode(inp, True, args.steps, args.warmup,
-                             args.replicas, device, fp8=True)
-        if wd.kind == "prefix" and not args.no_cow:
-            log("copy-on-write step")
-            cow = run_cow(wd, args.steps, args.warmup, device)
-        if default_workload:
-            log("block swap to pinned host memory and back")
-            swap = run_swap(wd, device)
+    configs = [c for c in args.configs.split(",") if c]
+    if args.workload:
+        configs = [args.workload]
+    if args.no_prefill:
+        configs = [c for c in configs if c != "yi6b_chunked_prefill"]
+    if args.no_decode:
+        configs = [c for c in configs if c == "yi6b_chunked_prefill"]
+    unknown = set(configs) - set(ALL_CONFIGS)
+    if unknown:
+        print(f"unknown configurations {sorted(unknown)}", file=sys.stderr)
+        return 2
+    cpu = not args.no_cpu_baseline
+
+    t_start = time.perf_counter()
+    rooflines, ovh, cpu_oracle, details = {}, {}, {}, {}
+    decoded = {}
+    prefill = None
+    for name in configs:
+        if name == "decode_tiny_f32":
             log("small fp32 decode (latency)")
             tiny = run_tiny_decode(device)
+            tiny["note"] = ("generic path, latency-bound: no roofline "
+                            "claim")
+            details[name] = nested_round(tiny)
+            if cpu:
+                from paged_kv_cache_191_amd import workloads as W
+                wt = W.WORKLOADS[name]
+                it = W.draw(wt, lambda L: pool_blocks(kv, wt, L))
+                cpu_oracle[name] = oracle_decode_rate(
+                    it, list(range(wt.num_seqs)), min(args.cpu_budget, 2.0))
+        elif name == "yi6b_chunked_prefill":
+            prefill = bench_prefill(args, device)
+            rooflines.update(prefill["rooflines"])
+            ovh.update(prefill["overhead"])
+            details[name] = {k: nested_round(v) for k, v in
+                             prefill["layouts"].items()}
+            if cpu and prefill["inp"] is not None:
+                log("prefill: oracle on sampled rows")
+                cpu_oracle[name] = oracle_prefill_rate(prefill["inp"],
+                                                       args.cpu_budget)
+            prefill["inp"] = None
+        elif name == "block_swap":
+            from paged_kv_cache_191_amd import workloads as W
+            log("block swap to pinned host memory and back")
+            details[name] = run_swap(W.WORKLOADS["llama3_8b_decode"], device)
+        else:
+            r = bench_decode_config(name, args, device)
+            decoded[name] = r
+            rooflines.update(r["rooflines"])
+            ovh.update(r["overhead"])
+            d = {k: nested_round(v) for k, v in r["runs"].items()}
+            d["cache_write_note"] = (
+                "cache_write_* fields: the step's append kernel, a few "
+                "hundred KB per launch: latency-bound, no roofline claim")
+            d["memory"] = r["memory"]
+            if r["cow"]:
+                d["copy_on_write"] = nested_round(r["cow"])
+            if "fp8_speedup_vs_bf16" in r:
+                d["fp8_speedup_vs_bf16"] = r["fp8_speedup_vs_bf16"]
+            details[name] = d
+            if cpu:
+                w = r["inp"].workload
+                log(f"{name}: oracle on a sample")
+                if name == "yi34b_long_decode":
+                    seqs = [0]
+                elif name == "prefix_share_decode":
+                    seqs = list(range(0, w.num_seqs, 37))
+                else:
+                    seqs = list(range(w.num_seqs))
+                cpu_oracle[name] = oracle_decode_rate(r["inp"], seqs,
+                                                      args.cpu_budget)
+            r["inp"] = None
+    log(f"all configurations done in {time.perf_counter() - t_start:.1f} s")
 
-    prefill = None
-    if not args.no_prefill and (default_workload or args.no_decode):
-        prefill = {}
-        wanted = args.prefill_layouts.split(",")
-        for name, layout in (("yi6b_chunked_prefill_b16", "paged_b16"),
-                             ("yi6b_chunked_prefill_b64", "paged_b64"),
-                             ("yi6b_chunked_prefill_b16", "contig"),
-                             ("yi6b_chunked_prefill_b16", "contig_vmm")):
-            if layout not in wanted:
-                continue
-            wp = W.WORKLOADS[name]
-            log(f"prefill {layout}")
-            pin = W.draw(wp, lambda L: pool_blocks(kv, wp, L))
-            r = prefill_pass(pin, {"contig": "contig", "contig_vmm": "vattn"}
-                             .get(layout, "paged"), device)
-            r["frac_of_peak"] = r["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
-            prefill[layout] = r
-        if "contig" in prefill:
-            for b in ("paged_b16", "paged_b64", "contig_vmm"):
-                if b in prefill:
-                    prefill[b]["overhead_vs_contig"] = (
-                        prefill[b]["attn_ms"] / prefill["contig"]["attn_ms"]
-                        - 1.0)
-    if args.no_decode:
-        log(f"prefill only: {json.dumps(prefill)}")
+    if not decoded:
+        log(f"no decode configuration: no bench line. prefill: "
+            f"{json.dumps(nested_round(details.get('yi6b_chunked_prefill')))}")
         return 0
-
-    cpu = None
-    if not args.no_cpu_baseline and wd.kind == "decode":
-        log("cpu baseline (fp64 oracle)")
-        cpu = cpu_baseline(inp, args.cpu_budget)
-
-    achieved = paged["decode_op_GBps"]
-    ctx_desc = {"llama3_8b_decode": "U{512..4096}",
-                "yi34b_long_decode": "196608",
-                "prefix_share_decode": "4096 shared + U{64..1024}"}
-    lmax_reserved = {"llama3_8b_decode": 4096,
-                     "yi34b_long_decode": 196608,
-                     "prefix_share_decode": 4096 + 1024}[wd.name]
+    head = "llama3_8b_decode" if "llama3_8b_decode" in decoded else \
+        next(iter(decoded))
+    hp = decoded[head]["runs"]["paged"]
+    wd = __import__("paged_kv_cache_191_amd.workloads",
+                    fromlist=["WORKLOADS"]).WORKLOADS[head]
     line = {
         "metric": METRIC,
-        "value": round(paged["step_GBps"], 2),
+        "value": round(hp["step_GBps"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(paged["ms_per_step"], 4),
+        "ms_per_step": round(hp["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1048,58 +1341,32 @@ def main() -> int:
             "workload": wd.name,
             "num_seqs": wd.num_seqs, "num_q_heads": wd.num_q_heads,
             "num_kv_heads": wd.num_kv_heads, "head_dim": wd.head_dim,
-            "block_size": wd.block_size, "context": ctx_desc[wd.name],
+            "block_size": wd.block_size, "context": CTX_DESC[wd.name],
             "step": "append+kv_append_token+" + (
-                "paged_attn_decode_shared_prefix" if plain else
-                "paged_attn_decode"),
+                "paged_attn_decode_shared_prefix" if wd.kind == "prefix"
+                else "paged_attn_decode"),
             "replicas": args.replicas,
+            "configs_run": configs,
         },
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": recorded_traffic(wd.name),
-            "kernel": ("paged_attn_decode_shared_prefix (prefill_pp_kernel"
-                       "<true,true> + decode_sk_kernel + decode_combine_kernel)"
-                       if plain else "paged_attn_decode (decode_sk_kernel + "
-                       "decode_combine_kernel)"),
-            "bytes_per_launch": int(paged["bytes_per_step"]),
-            "ms_per_launch": round(paged["decode_op_ms_mean"], 4),
-        },
-        "decode_paged": rounded(paged),
-        "memory": memory_waste(inp, lmax_reserved),
+        "roofline": rooflines[head],
     }
-    if plain:
-        line["decode_paged_without_sharing"] = rounded(plain)
-    if contig:
-        line["decode_contig"] = rounded(contig)
-        line["decode_paged_vs_contig_overhead"] = round(
-            paged["decode_op_ms_mean"] / contig["decode_op_ms_mean"] - 1.0, 4)
-    if vattn and "error" in vattn:
-        line["decode_contig_demand_mapped"] = vattn
-    elif vattn:
-        line["decode_contig_demand_mapped"] = {
-            k: (rounded(v) if isinstance(v, dict) else
-                round(v, 4) if isinstance(v, float) else v)
-            for k, v in vattn.items()}
-        line["decode_paged_vs_demand_mapped_overhead"] = round(
-            paged["decode_op_ms_mean"] / vattn["decode_op_ms_mean"] - 1.0, 4)
-    if fp8:
-        line["decode_paged_fp8"] = rounded(fp8)
-        line["decode_paged_fp8"]["frac_of_hbm_peak"] = round(
-            fp8["decode_op_GBps"] / HBM_PEAK_GBPS, 4)
-        line["decode_fp8_speedup_vs_bf16"] = round(
-            paged["decode_op_ms_mean"] / fp8["decode_op_ms_mean"], 4)
-    if cow:
-        line["copy_on_write"] = rounded(cow)
-    if swap:
-        line["block_swap"] = rounded(swap)
-    if tiny:
-        line["decode_tiny_f32"] = rounded(tiny)
-    if prefill:
-        line["prefill"] = {k: {kk: round(vv, 4) for kk, vv in v.items()}
-                           for k, v in prefill.items()}
-    line["cpu_baseline"] = cpu
+    if prefill and "paged_b16" in prefill["layouts"]:
+        p16 = dict(rooflines["yi6b_chunked_prefill_paged_b16"])
+        p16["overhead_vs_contig"] = ovh.get(
+            "yi6b_chunked_prefill_paged_b16")
+        p16["layouts"] = {
+            lay: {"TFLOPs": round(r["TFLOPs"], 1),
+                  "frac": round(r["frac_of_peak"], 4),
+                  "attn_ms": round(r["attn_ms"], 4),
+                  "overhead_vs_contig": ovh.get(
+                      "yi6b_chunked_prefill_" + lay)}
+            for lay, r in prefill["layouts"].items()}
+        line["prefill"] = p16
+    line["rooflines"] = rooflines
+    line["paged_vs_contig_overhead"] = ovh
+    line["cpu_oracle"] = cpu_oracle
+    line["configs"] = details
+    line["cpu_baseline"] = cpu_oracle.get(head)
     print(json.dumps(line), flush=True)
     return 0
 
