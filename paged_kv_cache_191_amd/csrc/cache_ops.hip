@@ -15,35 +15,72 @@ namespace {
 
 using namespace kvp;
 
-// One work item = one unit of one head of one token of K or V. Source
-// rows are token-major [T, Hkv, D]; destinations are head-major inside a
-// block: unit u of head h of slot goes to
-// ((slot / B) * Hkv + h) * B + slot % B (in head rows of D).
+// Rows of `per_token` units (Hkv heads x units_per_head) per token; a
+// workgroup of 256 threads covers `tpb` = 256 / per_token tokens at a time
+// (per_token <= 256), thread (token k, unit u) moving unit u of K and of V,
+// so the index arithmetic is done once per thread and the loop only walks
+// tokens. Destinations are head-major inside a block: unit u of head h of
+// slot goes to ((slot / B) * Hkv + h) * B + slot % B (in head rows).
+// bs_shift = log2(B) for power-of-two block sizes (else -1).
 template <typename U>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(
+    const U* __restrict__ k, const U* __restrict__ v,
+    const int64_t* __restrict__ slots, int32_t num_tokens, U* k_cache,
+    U* v_cache, int64_t num_slots, int32_t block_size, int32_t bs_shift,
+    int32_t num_kv_heads, int32_t units_per_head) {
+  const int per_token = num_kv_heads * units_per_head;
+  const int tpb = blockDim.x / per_token;
+  const int tk = threadIdx.x / per_token;
+  if (tk >= tpb) return;
+  const int u = threadIdx.x - tk * per_token;
+  const int h = u / units_per_head;
+  const int uu = u - h * units_per_head;
+  for (int64_t t = (int64_t)blockIdx.x * tpb + tk; t < num_tokens;
+       t += (int64_t)gridDim.x * tpb) {
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    int64_t blk, off;
+    if (bs_shift >= 0) {
+      blk = slot >> bs_shift;
+      off = slot & (block_size - 1);
+    } else {
+      blk = slot / block_size;
+      off = slot - blk * block_size;
+    }
+    const int64_t src = t * per_token + u;
+    const int64_t dst =
+        ((blk * num_kv_heads + h) * block_size + off) * units_per_head + uu;
+    const U kx = k[src];
+    const U vx = v[src];
+    k_cache[dst] = kx;
+    v_cache[dst] = vx;
+  }
+}
+
+// The same for rows of more than 256 units: one item = one unit of one
+// token (K and V).
+template <typename U>
+__global__ __launch_bounds__(256) void scatter_wide_rows_kernel(
     const U* __restrict__ k, const U* __restrict__ v,
     const int64_t* __restrict__ slots, int32_t num_tokens, U* k_cache,
     U* v_cache, int64_t num_slots, int32_t block_size, int32_t num_kv_heads,
     int32_t units_per_head) {
   const int64_t per_token = (int64_t)num_kv_heads * units_per_head;
-  const int64_t per_tensor = (int64_t)num_tokens * per_token;
-  const int64_t total = 2 * per_tensor;
+  const int64_t total = (int64_t)num_tokens * per_token;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const bool is_v = i >= per_tensor;
-    const int64_t j = is_v ? i - per_tensor : i;
-    const int64_t t = j / per_token;
-    const int64_t r = j - t * per_token;       // unit within the token row
+    const int64_t t = i / per_token;
+    const int64_t r = i - t * per_token;
     const int64_t h = r / units_per_head;
-    const int64_t u = r - h * units_per_head;
+    const int64_t uu = r - h * units_per_head;
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= num_slots) continue;
     const int64_t blk = slot / block_size;
     const int64_t off = slot - blk * block_size;
-    const U* src = is_v ? v : k;
-    U* dst = is_v ? v_cache : k_cache;
-    dst[((blk * num_kv_heads + h) * block_size + off) * units_per_head + u] =
-        src[t * per_token + r];
+    const int64_t dst =
+        ((blk * num_kv_heads + h) * block_size + off) * units_per_head + uu;
+    k_cache[dst] = k[i];
+    v_cache[dst] = v[i];
   }
 }
 
@@ -296,30 +333,32 @@ extern "C" kv_status kv_reshape_and_cache(const void* k, const void* v,
     return kvp_fail(KV_EINVAL, "kv_reshape_and_cache: NULL pointer");
   const int64_t head_bytes = (int64_t)head_dim * elem_size(dtype);
   hipStream_t st = (hipStream_t)stream;
-  const int threads = 256;
-  auto grid_for = [&](int64_t items) {
-    int64_t g = (items + threads - 1) / threads;
-    return (int)(g < 65536 ? g : 65536);
+  int bs_shift = -1;
+  if ((block_size & (block_size - 1)) == 0)
+    for (bs_shift = 0; (1 << bs_shift) < block_size; ++bs_shift) {}
+  auto go = [&](auto unit) {
+    using U = decltype(unit);
+    const int64_t uph = head_bytes / (int64_t)sizeof(U);
+    const int64_t per_token = uph * num_kv_heads;
+    if (per_token <= 256) {
+      const int64_t tpb = 256 / per_token;
+      const int64_t g = (num_tokens + tpb - 1) / tpb;
+      scatter_rows_kernel<U><<<(int)(g < 65536 ? g : 65536), 256, 0, st>>>(
+          (const U*)k, (const U*)v, slots, num_tokens, (U*)k_cache,
+          (U*)v_cache, num_slots, block_size, bs_shift, num_kv_heads,
+          (int32_t)uph);
+    } else {
+      const int64_t g = (num_tokens * per_token + 255) / 256;
+      scatter_wide_rows_kernel<U>
+          <<<(int)(g < 65536 ? g : 65536), 256, 0, st>>>(
+              (const U*)k, (const U*)v, slots, num_tokens, (U*)k_cache,
+              (U*)v_cache, num_slots, block_size, num_kv_heads,
+              (int32_t)uph);
+    }
   };
-  const int64_t heads = (int64_t)num_tokens * num_kv_heads;
-  if (head_bytes % 16 == 0) {
-    const int32_t uph = (int32_t)(head_bytes / 16);
-    scatter_rows_kernel<u32x4><<<grid_for(2 * heads * uph), threads, 0, st>>>(
-        (const u32x4*)k, (const u32x4*)v, slots, num_tokens, (u32x4*)k_cache,
-        (u32x4*)v_cache, num_slots, block_size, num_kv_heads, uph);
-  } else if (head_bytes % 4 == 0) {
-    const int32_t uph = (int32_t)(head_bytes / 4);
-    scatter_rows_kernel<uint32_t><<<grid_for(2 * heads * uph), threads, 0, st>>>(
-        (const uint32_t*)k, (const uint32_t*)v, slots, num_tokens,
-        (uint32_t*)k_cache, (uint32_t*)v_cache, num_slots, block_size,
-        num_kv_heads, uph);
-  } else {
-    const int32_t uph = (int32_t)(head_bytes / 2);
-    scatter_rows_kernel<uint16_t><<<grid_for(2 * heads * uph), threads, 0, st>>>(
-        (const uint16_t*)k, (const uint16_t*)v, slots, num_tokens,
-        (uint16_t*)k_cache, (uint16_t*)v_cache, num_slots, block_size,
-        num_kv_heads, uph);
-  }
+  if (head_bytes % 16 == 0) go(u32x4{});
+  else if (head_bytes % 4 == 0) go(uint32_t{});
+  else go(uint16_t{});
   KVP_LAUNCH_CHECK("kv_reshape_and_cache");
   return KV_OK;
 }
