@@ -302,9 +302,9 @@ kv_status contig_attn_decode(void* out, const void* q, const void* k,
  * group is read per sequence). Values outside these rules keep memory
  * accesses in bounds but make the affected outputs meaningless.
  * The workspace must hold kv_decode_shared_prefix_workspace_bytes() bytes.
- * The sharing pass needs bf16, head_dim 128, (Hq/Hkv) % 4 == 0, block_size
- * % 16 == 0 and at most 4096 sequences; other calls (and max_shared_len <
- * 16) run paged_attn_decode unchanged. */
+ * The sharing pass needs bf16, head_dim 128, block_size % 16 == 0 and at
+ * most 4096 sequences; other calls (and max_shared_len < 16) run
+ * paged_attn_decode unchanged. */
 size_t kv_decode_shared_prefix_workspace_bytes(int32_t num_seqs,
                                                int32_t num_q_heads,
                                                int32_t num_kv_heads,

@@ -975,11 +975,13 @@ int env_psplit_override() {
   return cached;
 }
 
-void choose_psplit(int num_seqs, int hq, int max_shared, int* nsplit,
-                   int* ksplit) {
+void choose_psplit(int num_seqs, int hq, int hkv, int max_shared,
+                   int* nsplit, int* ksplit) {
   const int ms = max_shared < 16 ? 16 : max_shared;
   const int rowblocks = (num_seqs + 31) / 32;
-  const int per_split = rowblocks * (hq / 4);
+  // prefix-pass workgroups per piece: row blocks x head blocks of 4 within
+  // each KV head's group
+  const int per_split = rowblocks * hkv * ((hq / hkv + 3) / 4);
   int n = (2 * device_cus() + per_split - 1) / per_split;
   if (env_psplit_override() > 0) n = env_psplit_override();
   const int max_n = (ms + 255) / 256;
@@ -992,7 +994,7 @@ void choose_psplit(int num_seqs, int hq, int max_shared, int* nsplit,
 bool shared_fast_ok(kv_dtype dtype, int hq, int hkv, int head_dim,
                     int block_size) {
   return dtype == KV_BF16 && head_dim == kD && block_size % 16 == 0 &&
-         hkv > 0 && hq % hkv == 0 && (hq / hkv) % 4 == 0;
+         hkv > 0 && hq % hkv == 0;
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -1015,7 +1017,8 @@ extern "C" size_t kv_decode_shared_prefix_workspace_bytes(
       !shared_fast_ok(KV_BF16, num_q_heads, num_kv_heads, head_dim, 16))
     return base;
   int nsplit, ksplit;
-  choose_psplit(num_seqs, num_q_heads, max_shared_len, &nsplit, &ksplit);
+  choose_psplit(num_seqs, num_q_heads, num_kv_heads, max_shared_len, &nsplit,
+                &ksplit);
   return align256(base) + shared_extra_bytes(num_seqs, num_q_heads, nsplit);
 }
 
@@ -1070,7 +1073,8 @@ extern "C" kv_status paged_attn_decode_shared_prefix(
     return kvp_fail(KV_EINVAL, "%s: workspace of %zu bytes needed, %zu given",
                     name, need, workspace_bytes);
   int nsplit, ksplit;
-  choose_psplit(num_seqs, num_q_heads, max_shared_len, &nsplit, &ksplit);
+  choose_psplit(num_seqs, num_q_heads, num_kv_heads, max_shared_len, &nsplit,
+                &ksplit);
   const size_t base = align256(kv_decode_workspace_bytes(
       num_seqs, num_q_heads, num_kv_heads, head_dim, max_context));
   char* wp = (char*)workspace + base;

@@ -7,10 +7,12 @@
 // A100; the paged and contiguous variants here share one kernel body, with
 // only the tile loader's row addressing different.
 //
-// Fast path (bf16, head_dim 128, group % 4 == 0, block_size % 16 == 0):
+// Fast path (bf16, head_dim 128, block_size % 16 == 0):
 //   * A workgroup of 8 waves owns 64 query rows of one sequence and 4 query
 //     heads of one KV head (grouped-query packing: the K/V tile in LDS serves
 //     all four heads and all 64 rows). Each wave owns one head and 32 rows.
+//     A group whose size is not a multiple of 4 ends in a partly empty block
+//     of heads; its spare waves repeat a valid head and store nothing.
 //   * Keys advance in tiles of 64, gathered through the block table (16
 //     consecutive keys share a block) with 16-byte direct global-to-LDS
 //     loads into double buffers: unpadded 256-byte rows, XOR-swizzled so
@@ -179,7 +181,10 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
   using Mask = std::true_type;
 
   const int tid = threadIdx.x;
-  const int hblocks = a.hq / 4;
+  // head blocks of 4 query heads inside each KV head's group (the last one
+  // partly empty when the group size is not a multiple of 4)
+  const int hb_per_kv = (a.group + 3) / 4;
+  const int hblocks = a.hkv * hb_per_kv;
   int bx, by, bz, split = 0;
   if (PREFIX) {
     int t = xcd_order(blockIdx.x, gridDim.x);
@@ -234,11 +239,15 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g2 = lane >> 5;
-  const int h = by * 4 + (w & 3);
-  const int kvh = (by * 4) / a.group;
+  const int kvh = by / hb_per_kv;
+  const int h_in_grp = (by % hb_per_kv) * 4 + (w & 3);
+  // A wave past the group's last head repeats that head's work (its tile
+  // loads and barriers are the workgroup's) and stores nothing.
+  const bool h_ok = h_in_grp < a.group;
+  const int h = kvh * a.group + (h_ok ? h_in_grp : a.group - 1);
   const int row0 = q0 + 32 * grp;  // first query row of this group
   if (PREFIX && kv_beg >= kv_end) {
-    if (row0 + l32 < nrows + q0 && g2 == 0) {
+    if (h_ok && row0 + l32 < nrows + q0 && g2 == 0) {
       const int64_t idx =
           ((int64_t)split * a.members + qbeg + row0 + l32) * a.hq + h;
       a.pml[2 * idx] = -INFINITY;
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
   }
   if (kv_end <= kv_beg) {
     // no key at all (empty context): zero rows
-    if (!PREFIX && row0 + l32 < q0 + nrows) {
+    if (!PREFIX && h_ok && row0 + l32 < q0 + nrows) {
       bf16* op = (bf16*)a.out + ((int64_t)(qbeg + row0 + l32) * a.hq + h) * kD +
                  64 * g2;
 #pragma unroll
@@ -603,7 +612,7 @@ __global__ __launch_bounds__(kPPWaves * kWave, 1) void prefill_pp_kernel(
 
   // ---- outputs of this group's rows
   l_part = halves_sum(l_part);
-  const bool row_ok = row0 + l32 < q0 + nrows;
+  const bool row_ok = h_ok && row0 + l32 < q0 + nrows;
   if (PREFIX) {
     if (row_ok) {
       const int64_t idx =
@@ -731,9 +740,10 @@ kv_status run_prefill(const char* name, bool paged, PrefillArgs a,
                    ? __builtin_ctz((unsigned)a.block_size)
                    : -1;
   const bool fast = dtype == KV_BF16 && a.head_dim == kD &&
-                    a.group % 4 == 0 && (!paged || a.block_size % 16 == 0);
+                    (!paged || a.block_size % 16 == 0);
   if (fast) {
-    dim3 grid((a.max_q_len + kPPRows - 1) / kPPRows, a.hq / 4, a.num_seqs);
+    dim3 grid((a.max_q_len + kPPRows - 1) / kPPRows,
+              a.hkv * ((a.group + 3) / 4), a.num_seqs);
     if ((int64_t)grid.x * grid.y * grid.z > INT32_MAX)
       return kvp_fail(KV_EUNSUPPORTED, "%s: too many query blocks", name);
     if (!paged)
@@ -798,7 +808,8 @@ kv_status kvp_prefix_partials(const KvpPrefixJob& j, hipStream_t st) {
   a.nsplit = j.nsplit;
   a.ksplit = j.ksplit;
   a.rowblocks = (j.max_group_size + kPPRows - 1) / kPPRows;
-  const int64_t n = (int64_t)a.rowblocks * (a.hq / 4) * a.nsplit *
+  const int64_t n = (int64_t)a.rowblocks * (a.hkv * ((a.group + 3) / 4)) *
+                    a.nsplit *
                     j.num_groups;
   if (n > INT32_MAX)
     return kvp_fail(KV_EUNSUPPORTED, "shared-prefix decode: too many groups");

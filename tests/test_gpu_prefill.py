@@ -103,10 +103,16 @@ def test_chunked_prefill_small(B, layout):
 
 
 @pytest.mark.parametrize("variant", ["noncausal", "f32_generic",
-                                     "g7_generic"])
+                                     "g7", "g1", "g5", "b8_generic",
+                                     "yi34b_g7_b64"])
 def test_prefill_variants(variant):
+    # Head groups that are not a multiple of 4 (g1, g5, g7, the Yi-34B shape
+    # 56 q / 8 kv heads) run the MFMA kernel with a partly empty last block
+    # of heads; fp32, and block sizes that are not a multiple of 16, run the
+    # generic kernel.
     base = W.WORKLOADS["yi6b_chunked_prefill_b16"]
     causal = True
+    nq = [20, 33]
     if variant == "noncausal":
         w = base.replace(num_seqs=2, lengths=(70, 131), name=variant)
         causal = False
@@ -114,15 +120,23 @@ def test_prefill_variants(variant):
         w = base.replace(num_seqs=2, lengths=(40, 77), dtype="f32",
                          dist="uniform", num_q_heads=8, num_kv_heads=2,
                          head_dim=64, name=variant)
+    elif variant == "b8_generic":
+        w = base.replace(num_seqs=2, lengths=(50, 97), num_q_heads=8,
+                         num_kv_heads=2, block_size=8, name=variant)
+    elif variant == "yi34b_g7_b64":
+        # two 64-row query blocks and a ragged one per sequence
+        w = base.replace(num_seqs=2, lengths=(300, 421), num_q_heads=56,
+                         num_kv_heads=8, block_size=64, name=variant)
+        nq = [150, 131]
     else:
-        w = base.replace(num_seqs=2, lengths=(50, 97), num_q_heads=14,
+        g = int(variant[1:])
+        w = base.replace(num_seqs=2, lengths=(50, 97), num_q_heads=2 * g,
                          num_kv_heads=2, name=variant)
     inp = _draw(w)
     B = w.block_size
     nat = H.build_native(inp, B, H.tables_capacity(int(inp.lengths.max()), B))
     orc = H.build_oracle(inp, B)
     # Query the last `nq` tokens of each sequence against its full context.
-    nq = [20, 33]
     rows = np.concatenate([np.arange(inp.cu[s + 1] - n, inp.cu[s + 1])
                            for s, n in enumerate(nq)]).astype(np.int64)
     cu = np.array([0, nq[0], nq[0] + nq[1]], dtype=np.int32)

@@ -80,7 +80,7 @@ def test_decode_random_shapes(seed):
 def _prefill_shape(seed):
     g = np.random.default_rng([2000, seed])
     hkv = int(g.choice([1, 2, 4]))
-    group = int(g.choice([4, 8, 12]))
+    group = int(g.choice([1, 2, 3, 4, 5, 7, 8, 12]))
     S = int(g.integers(1, 4))
     return dict(num_seqs=S, num_kv_heads=hkv, num_q_heads=hkv * group,
                 block_size=int(g.choice([16, 32, 48, 64])),
