@@ -39,7 +39,11 @@ A decode step is one step of a batch of sequences, each growing by one token:
 The contiguous layouts take the same kernel with one "block" per sequence;
 the fp8 decode its fp8 form (kv_append_token_fp8_per_head).
 Four independent replicas of the whole batch (pools, tables, queries) rotate
-so that no step finds its K/V in the 256 MB last-level cache.
+so that no step finds its K/V in the 256 MB last-level cache. Each replica's
+two device launches are marshalled once (kv.bind) and re-issued every step,
+so the host keeps ahead of the GPU. The timed steps queue nothing else; a
+second pass of as many steps brackets each decode op with HIP events for its
+GPU time.
 
 `value` = decode algorithmic bytes of the headline workload (K+V once per KV
 head, q, o, block-table entries, lengths) summed over the timed steps / wall
@@ -85,6 +89,13 @@ DECODE_WORKLOADS = ("llama3_8b_decode", "yi34b_long_decode",
 COW_PREFIX = 4104
 # appends timed on their own after the timed decode steps
 APPEND_TIMING_STEPS = 8
+
+
+def decode_steps_total(steps: int, warmup: int) -> int:
+    """Decode steps a run takes from its replicas: warm-up, the timed
+    steps, the same number again with per-op events, and the cache-write
+    timing."""
+    return warmup + 2 * steps + APPEND_TIMING_STEPS
 # GPU spin before each of them (about 40 us at 2.4 GHz)
 SPIN_CYCLES = 100_000
 
@@ -327,7 +338,43 @@ class DecodeReplica:
         self.uploaded = torch.cuda.Event()
         self.uploaded.record()
         self.scale = 1.0 / float(np.sqrt(w.head_dim))
+        self._bind_launches()
         torch.cuda.synchronize()
+
+    def _bind_launches(self) -> None:
+        """The step's two device launches, marshalled once (kv.bind): the
+        cache write and the decode op re-issue the same native calls every
+        step, as a serving loop in C++ would. The decode's context bound is
+        the replica's capacity, lmax, which holds every length of the run
+        (the bound only clamps lengths)."""
+        kv = self.kv
+        if self.fp8:
+            self._write = kv.bind(
+                kv.kv_append_token_fp8_per_head, self.new_k, self.new_v,
+                self.h_newb, self.a_table, self.d_lens, self.k, self.v,
+                self.k_scales, self.v_scales)
+            self._decode = kv.bind(
+                kv.paged_attn_decode_fp8_per_head, self.out, self.q, self.k,
+                self.v, self.d_table, self.d_lens, self.lmax, self.scale,
+                self.k_scales, self.v_scales, self.ws)
+            return
+        self._write = kv.bind(kv.kv_append_token, self.new_k, self.new_v,
+                              self.h_newb, self.a_table, self.d_lens, self.k,
+                              self.v)
+        if self.shared_op:
+            self._decode = kv.bind(
+                kv.paged_attn_decode_shared_prefix, self.out, self.q, self.k,
+                self.v, self.d_table, self.d_lens, self.lmax, self.g_starts,
+                self.g_shared, self.w.num_seqs, self.shared, self.scale,
+                self.ws)
+        elif self.paged:
+            self._decode = kv.bind(kv.paged_attn_decode, self.out, self.q,
+                                   self.k, self.v, self.d_table, self.d_lens,
+                                   self.lmax, self.scale, self.ws)
+        else:
+            self._decode = kv.bind(kv.contig_attn_decode, self.out, self.q,
+                                   self.k, self.v, self.d_lens, self.lmax,
+                                   self.scale, self.ws)
 
     def host_append(self) -> None:
         """Host part of a step. Paged: kv_seq_append (allocation, slot
@@ -365,39 +412,15 @@ class DecodeReplica:
         """Device part of the append: the new token's row in the cache, the
         table entry and the length on the device. `done` (an event, default
         a new one) is recorded after it and marks the pinned buffer free."""
-        kv = self.kv
-        if self.fp8:
-            kv.kv_append_token_fp8_per_head(
-                self.new_k, self.new_v, self.h_newb, self.a_table,
-                self.d_lens, self.k, self.v, self.k_scales, self.v_scales)
-        else:
-            kv.kv_append_token(self.new_k, self.new_v, self.h_newb,
-                               self.a_table, self.d_lens, self.k, self.v)
+        self._write()
         self.uploaded = done if done is not None else self.torch.cuda.Event()
         self.uploaded.record()
 
     def device_step(self, ev=None) -> None:
         """Cache write, then the decode op, bracketed by ev[0], ev[1]; ev[0]
         also marks the end of the cache write."""
-        kv = self.kv
         self.cache_write(ev[0] if ev is not None else None)
-        max_ctx = int(self.h_lens.max())
-        if self.fp8:
-            kv.paged_attn_decode_fp8_per_head(
-                self.out, self.q, self.k, self.v, self.d_table, self.d_lens,
-                max_ctx, self.scale, self.k_scales, self.v_scales, self.ws)
-        elif self.shared_op:
-            kv.paged_attn_decode_shared_prefix(
-                self.out, self.q, self.k, self.v, self.d_table, self.d_lens,
-                max_ctx, self.g_starts, self.g_shared, self.w.num_seqs,
-                self.shared, self.scale, self.ws)
-        elif self.paged:
-            kv.paged_attn_decode(self.out, self.q, self.k, self.v,
-                                 self.d_table, self.d_lens, max_ctx,
-                                 self.scale, self.ws)
-        else:
-            kv.contig_attn_decode(self.out, self.q, self.k, self.v,
-                                  self.d_lens, max_ctx, self.scale, self.ws)
+        self._decode()
         if ev is not None:
             ev[1].record()
 
@@ -429,7 +452,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     k_dev, v_dev = inp.k.to(device), inp.v.to(device)
     scales = fp8_head_scales(k_dev, v_dev) if fp8 else None
     reps_ = [DecodeReplica(inp, k_dev, v_dev, new_k, new_v, paged,
-                           steps + warmup + APPEND_TIMING_STEPS, device,
+                           decode_steps_total(steps, warmup), device,
                            shared_op, vmm_page_tokens, scales)
              for _ in range(reps)]
     del k_dev, v_dev
@@ -438,21 +461,40 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         r.host_append()
         r.device_step()
     torch.cuda.synchronize()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-           for _ in range(steps)]
+    kv_es = 1 if fp8 else 0
+
+    def step_bytes(r):
+        args = (r.h_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                w.block_size, paged)
+        return (decode_bytes(*args, shared=r.shared, kv_esize=kv_es),
+                decode_bytes(*args, kv_esize=kv_es))
+
+    # The timed steps: host append, cache write and decode op, nothing else
+    # queued (the per-op events are a second pass below).
     total_bytes = logical_bytes = 0
     t0 = time.perf_counter()
     for i in range(steps):
         r = reps_[i % reps]
         r.host_append()
-        args = (r.h_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                w.block_size, paged)
-        kv_es = 1 if fp8 else 0
-        total_bytes += decode_bytes(*args, shared=r.shared, kv_esize=kv_es)
-        logical_bytes += decode_bytes(*args, kv_esize=kv_es)
-        r.device_step(evs[i])
+        b, lb = step_bytes(r)
+        total_bytes += b
+        logical_bytes += lb
+        r.device_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # The same steps again (the contexts one token per replica round
+    # longer), each decode op bracketed by events: its GPU time.
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+           for _ in range(steps)]
+    op_bytes = op_logical = 0
+    for i in range(steps):
+        r = reps_[i % reps]
+        r.host_append()
+        b, lb = step_bytes(r)
+        op_bytes += b
+        op_logical += lb
+        r.device_step(evs[i])
+    torch.cuda.synchronize()
     op = stats_ms([a.elapsed_time(b) for a, b in evs])
     # The cache write alone (the append kernel),
     # timed after the timed steps so that its events stay out of them. A
@@ -482,10 +524,11 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
                        "kv_append_token_fp8_per_head",
         "cache_write_us_median": 1e3 * rc["median"],
     }
-    res["decode_op_GBps"] = res["bytes_per_step"] / (op["mean"] * 1e-3) / 1e9
+    res["op_bytes_per_step"] = op_bytes / steps
+    res["decode_op_GBps"] = res["op_bytes_per_step"] / (op["mean"] * 1e-3) / 1e9
     if logical_bytes != total_bytes:
         res["logical_bytes_per_step"] = logical_bytes / steps
-        res["decode_op_effective_GBps"] = (logical_bytes / steps) / (
+        res["decode_op_effective_GBps"] = (op_logical / steps) / (
             op["mean"] * 1e-3) / 1e9
     # the new rows: K and V, read once (bf16) and written once
     tok_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * (
@@ -1001,7 +1044,7 @@ SHARED_KERNEL = ("paged_attn_decode_shared_prefix (prefill_pp_kernel<true,"
 def decode_roofline(res: dict, kernel: str, traffic=None) -> dict:
     return roofline_record(
         "hbm", res["decode_op_GBps"], HBM_PEAK_GBPS, "GB/s", traffic,
-        kernel=kernel, bytes_per_launch=int(res["bytes_per_step"]),
+        kernel=kernel, bytes_per_launch=int(res["op_bytes_per_step"]),
         ms_per_launch=round(res["decode_op_ms_mean"], 4))
 
 
@@ -1030,8 +1073,8 @@ def bench_decode_config(name: str, args, device) -> dict:
     from paged_kv_cache_191_amd import kvpaged as kv
     from paged_kv_cache_191_amd import workloads as W
     wd = W.WORKLOADS[name]
-    headroom = wd.num_seqs * (-(-(args.steps + args.warmup +
-                                  APPEND_TIMING_STEPS) // wd.block_size) + 1)
+    headroom = wd.num_seqs * (-(-decode_steps_total(args.steps, args.warmup)
+                                // wd.block_size) + 1)
     log(f"{name}: drawing")
     inp = W.draw(wd, lambda L: pool_blocks(kv, wd, L, headroom))
     runs = {}

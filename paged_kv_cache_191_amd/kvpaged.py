@@ -442,6 +442,55 @@ def _attn_shapes(out, q, k, v, head_dim_of_k: int, S: int,
         _rows(t, S, name)
 
 
+# While bind() records a launch, _invoke notes the native call instead of
+# making it.
+_RECORD: Optional[list] = None
+
+
+def _invoke(name: str, *args):
+    if _RECORD is not None:
+        _RECORD.append((name, args))
+        return KV_OK
+    return getattr(lib(), name)(*args)
+
+
+def bind(wrapper, *args, **kwargs):
+    """Marshals one device launch once and returns a callable that issues it
+    again (same pointers, sizes, scale and stream: the stream current at bind
+    time unless `stream` is given) with no further Python-side checks, for
+    loops that run an op many times on the same buffers. The callable keeps
+    the arguments alive. A wrapper that would allocate its own workspace is
+    refused (the buffer would not outlive this call)."""
+    import inspect
+    global _RECORD
+    sig = inspect.signature(wrapper)
+    given = sig.bind(*args, **kwargs).arguments
+    if "workspace" in sig.parameters and given.get("workspace") is None:
+        raise ValueError(f"bind({wrapper.__name__}) needs a workspace")
+    if _RECORD is not None:
+        raise RuntimeError("bind() is not reentrant")
+    _RECORD = []
+    try:
+        wrapper(*args, **kwargs)
+        rec = _RECORD
+    finally:
+        _RECORD = None
+    if len(rec) != 1:
+        raise ValueError(f"{wrapper.__name__} is not a single launch")
+    name, cargs = rec[0]
+    fn = getattr(lib(), name)
+    # arguments converted to their ctypes types once
+    cargs = tuple(t(a) if a is not None and not isinstance(a, t) else a
+                  for t, a in zip(fn.argtypes, cargs))
+
+    def call() -> None:
+        st = fn(*cargs)
+        if st != KV_OK:
+            raise KVError(st, name)
+    call.keep = (args, kwargs)
+    return call
+
+
 def _stream(stream=None):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -460,7 +509,7 @@ def kv_reshape_and_cache(k, v, slots, k_cache, v_cache, stream=None) -> None:
     _same(v_cache, k_cache, "v_cache", "k_cache")
     _ndim(slots, 1, "slots")
     _rows(slots, n, "slots")
-    st = lib().kv_reshape_and_cache(
+    st = _invoke("kv_reshape_and_cache",
         _dev(k, "k"), _dev(v, "v", k.dtype), _dev(slots, "slots", torch.int64),
         n, _dev(k_cache, "k_cache", k.dtype), _dev(v_cache, "v_cache", k.dtype),
         nb * bs, bs, hkv, d, _dtype_code(k), _stream(stream))
@@ -488,7 +537,7 @@ def kv_reshape_and_cache_fp8(k, v, slots, k_cache, v_cache, k_scale: float,
     _same(v, k, "v", "k")
     _ndim(slots, 1, "slots")
     _rows(slots, n, "slots")
-    st = lib().kv_reshape_and_cache_fp8(
+    st = _invoke("kv_reshape_and_cache_fp8",
         _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
         _dev(slots, "slots", torch.int64), n, _fp8_cache(k_cache, "k_cache"),
         _fp8_cache(v_cache, "v_cache"), nb * bs, bs, hkv, d, float(k_scale),
@@ -518,7 +567,7 @@ def kv_reshape_and_cache_fp8_per_head(k, v, slots, k_cache, v_cache,
     _same(v, k, "v", "k")
     _ndim(slots, 1, "slots")
     _rows(slots, n, "slots")
-    st = lib().kv_reshape_and_cache_fp8_per_head(
+    st = _invoke("kv_reshape_and_cache_fp8_per_head",
         _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
         _dev(slots, "slots", torch.int64), n, _fp8_cache(k_cache, "k_cache"),
         _fp8_cache(v_cache, "v_cache"), nb * bs, bs, hkv, d,
@@ -533,7 +582,7 @@ def kv_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
     _same(v_cache, k_cache, "v_cache", "k_cache")
     if len(src_dst.shape) != 2 or src_dst.shape[1] != 2:
         raise ValueError("src_dst must be [n, 2]")
-    st = lib().kv_copy_blocks(
+    st = _invoke("kv_copy_blocks",
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache", k_cache.dtype),
         _dev(src_dst, "src_dst", torch.int32), src_dst.shape[0], nb, bs, hkv,
         d, _dtype_code(k_cache), _stream(stream))
@@ -563,7 +612,7 @@ def kv_append_token(k, v, new_blocks, block_tables, context_lens, k_cache,
     _ndim(new_blocks, 1, "new_blocks")
     _ndim(block_tables, 2, "block_tables")
     _ndim(context_lens, 1, "context_lens")
-    st = lib().kv_append_token(
+    st = _invoke("kv_append_token",
         _dev(k, "k"), _dev(v, "v", k.dtype), new_blocks.data_ptr(),
         _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
@@ -593,7 +642,7 @@ def kv_append_token_fp8(k, v, new_blocks, block_tables, context_lens,
     _ndim(new_blocks, 1, "new_blocks")
     _ndim(block_tables, 2, "block_tables")
     _ndim(context_lens, 1, "context_lens")
-    st = lib().kv_append_token_fp8(
+    st = _invoke("kv_append_token_fp8",
         _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
         new_blocks.data_ptr(), _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
@@ -623,7 +672,7 @@ def kv_append_token_fp8_per_head(k, v, new_blocks, block_tables,
     _ndim(new_blocks, 1, "new_blocks")
     _ndim(block_tables, 2, "block_tables")
     _ndim(context_lens, 1, "context_lens")
-    st = lib().kv_append_token_fp8_per_head(
+    st = _invoke("kv_append_token_fp8_per_head",
         _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
         new_blocks.data_ptr(), _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
@@ -654,7 +703,7 @@ def kv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:
     torch = _torch()
     if pairs.dtype != torch.int32:
         raise TypeError("pairs must be int32")
-    st = lib().kv_swap_blocks(src_k.data_ptr(), src_v.data_ptr(), sb,
+    st = _invoke("kv_swap_blocks", src_k.data_ptr(), src_v.data_ptr(), sb,
                               dst_k.data_ptr(), dst_v.data_ptr(), db,
                               pairs.data_ptr(), pairs.shape[0], bs, hkv, d,
                               _dtype_code(src_k), _stream(stream))
@@ -693,7 +742,7 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _ndim(block_tables, 2, "block_tables")
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
-    st = lib().paged_attn_decode(
+    st = _invoke("paged_attn_decode",
         _dev(out, "out", q.dtype), _dev(q, "q"),
         _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
         nb, _dev(block_tables, "block_tables", torch.int32),
@@ -716,7 +765,7 @@ def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables,
                  ((block_tables, "block_tables"),
                   (context_lens, "context_lens")))
     _ndim(block_tables, 2, "block_tables")
-    st = lib().paged_attn_decode_noalloc(
+    st = _invoke("paged_attn_decode_noalloc",
         _dev(out, "out", q.dtype), _dev(q, "q"),
         _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
         nb, _dev(block_tables, "block_tables", torch.int32),
@@ -740,7 +789,7 @@ def paged_attn_decode_fp8(out, q, k_cache, v_cache, block_tables,
     _ndim(block_tables, 2, "block_tables")
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
-    st = lib().paged_attn_decode_fp8(
+    st = _invoke("paged_attn_decode_fp8",
         _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
         _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"), nb,
         _dev(block_tables, "block_tables", torch.int32),
@@ -762,7 +811,7 @@ def contig_attn_decode_fp8(out, q, k, v, context_lens, max_context: int,
                  ((k, "k"), (context_lens, "context_lens")))
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
-    st = lib().contig_attn_decode_fp8(
+    st = _invoke("contig_attn_decode_fp8",
         _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
         _fp8_cache(k, "k"), _fp8_cache(v, "v"), lmax,
         _dev(context_lens, "context_lens", torch.int32), int(max_context), S,
@@ -786,7 +835,7 @@ def paged_attn_decode_fp8_per_head(out, q, k_cache, v_cache, block_tables,
     _ndim(block_tables, 2, "block_tables")
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
-    st = lib().paged_attn_decode_fp8_per_head(
+    st = _invoke("paged_attn_decode_fp8_per_head",
         _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
         _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"), nb,
         _dev(block_tables, "block_tables", torch.int32),
@@ -810,7 +859,7 @@ def contig_attn_decode_fp8_per_head(out, q, k, v, context_lens,
                  ((k, "k"), (context_lens, "context_lens")))
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
-    st = lib().contig_attn_decode_fp8_per_head(
+    st = _invoke("contig_attn_decode_fp8_per_head",
         _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
         _fp8_cache(k, "k"), _fp8_cache(v, "v"), lmax,
         _dev(context_lens, "context_lens", torch.int32), int(max_context), S,
@@ -824,7 +873,7 @@ def kv_decode_clamped_count(workspace, stream=None) -> int:
     """Sequences whose context length the last decode call on `workspace`
     clamped (waits for the stream)."""
     n = ctypes.c_int32(0)
-    st = lib().kv_decode_clamped_count(_dev(workspace, "workspace"),
+    st = _invoke("kv_decode_clamped_count", _dev(workspace, "workspace"),
                                        _stream(stream), ctypes.byref(n))
     _check(st, "kv_decode_clamped_count")
     return int(n.value)
@@ -869,7 +918,7 @@ def paged_attn_decode_shared_prefix(out, q, k_cache, v_cache, block_tables,
     if workspace is None:
         workspace = decode_shared_prefix_workspace(S, hq, hkv, d, max_context,
                                                    max_shared_len, q.device)
-    st = lib().paged_attn_decode_shared_prefix(
+    st = _invoke("paged_attn_decode_shared_prefix",
         _dev(out, "out", q.dtype), _dev(q, "q"),
         _dev(k_cache, "k_cache", q.dtype), _dev(v_cache, "v_cache", q.dtype),
         nb, _dev(block_tables, "block_tables", torch.int32),
@@ -892,7 +941,7 @@ def contig_attn_decode(out, q, k, v, context_lens, max_context: int,
                  ((k, "k"), (context_lens, "context_lens")))
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
-    st = lib().contig_attn_decode(
+    st = _invoke("contig_attn_decode",
         _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k, "k", q.dtype),
         _dev(v, "v", q.dtype), lmax,
         _dev(context_lens, "context_lens", torch.int32), int(max_context), S,
@@ -914,7 +963,7 @@ def paged_attn_prefill(out, q, cu_q_lens, q_start_pos, max_q_len: int,
                   (context_lens, "context_lens"),
                   (q_start_pos, "q_start_pos")))
     _ndim(block_tables, 2, "block_tables")
-    st = lib().paged_attn_prefill(
+    st = _invoke("paged_attn_prefill",
         _dev(out, "out", q.dtype), _dev(q, "q"),
         _dev(cu_q_lens, "cu_q_lens", torch.int32),
         _dev(q_start_pos, "q_start_pos", torch.int32), int(max_q_len),
@@ -937,7 +986,7 @@ def contig_attn_prefill(out, q, cu_q_lens, q_start_pos, max_q_len: int, k, v,
     _attn_shapes(out, q, k, v, dk, S,
                  ((k, "k"), (context_lens, "context_lens"),
                   (q_start_pos, "q_start_pos")))
-    st = lib().contig_attn_prefill(
+    st = _invoke("contig_attn_prefill",
         _dev(out, "out", q.dtype), _dev(q, "q"),
         _dev(cu_q_lens, "cu_q_lens", torch.int32),
         _dev(q_start_pos, "q_start_pos", torch.int32), int(max_q_len),

@@ -242,6 +242,61 @@ def test_decode_step_appends_through_native_path():
     _check(outs, want, w)
 
 
+def test_bound_launches_match_wrappers():
+    # kv.bind marshals a launch once; re-issuing it must give the wrapper's
+    # result bit for bit, also after the buffers' contents change between
+    # calls (the lengths grow through the bound cache write).
+    w = W.WORKLOADS["llama3_8b_decode"].replace(num_seqs=8)
+    inp = _draw(w, headroom=16)
+    ctx = W.context_lengths(inp)
+    B = w.block_size
+    cap = H.tables_capacity(int(ctx.max()) + 3, B)
+    scale = H.scale_of(w)
+    q = inp.q.cuda()
+    ws = kv.decode_workspace(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                             w.head_dim, cap * B, q.device)
+    outs = []
+    for bound in (False, True):
+        nat = H.build_native(inp, B, cap, upto=ctx - 1)
+        g = torch.Generator().manual_seed(7)
+        newk = torch.randn(w.num_seqs, w.num_kv_heads, w.head_dim,
+                           generator=g).to(torch.bfloat16).cuda()
+        newv = torch.randn(newk.shape, generator=g).to(torch.bfloat16).cuda()
+        newb = torch.full((w.num_seqs,), -1, dtype=torch.int32,
+                          pin_memory=True)
+        lens = torch.from_numpy(nat.lens.copy()).cuda()
+        bt = torch.from_numpy(nat.tables).cuda()
+        out = torch.full_like(q, float("nan"))
+        wr = (newk, newv, newb, bt, lens, nat.k_cache, nat.v_cache)
+        dec = (out, q, nat.k_cache, nat.v_cache, bt, lens, cap * B, scale,
+               ws)
+        if bound:
+            write = kv.bind(kv.kv_append_token, *wr)
+            decode = kv.bind(kv.paged_attn_decode, *dec)
+        else:
+            def write(wr=wr):
+                kv.kv_append_token(*wr)
+
+            def decode(dec=dec):
+                kv.paged_attn_decode(*dec)
+        got = []
+        for step in range(3):
+            before = nat.tables[np.arange(w.num_seqs), nat.lens // B].copy()
+            _, pairs = nat.pool.seq_append(nat.tables, nat.lens)
+            assert len(pairs) == 0
+            after = nat.tables[np.arange(w.num_seqs), (nat.lens - 1) // B]
+            newb.numpy()[:] = np.where(after != before, after, -1)
+            write()
+            decode()
+            torch.cuda.synchronize()
+            got.append(out.float().cpu().numpy())
+        assert lens.cpu().numpy().tolist() == nat.lens.tolist()
+        outs.append(got)
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    _log("bound launches: 3 steps bit-identical to the wrappers")
+
+
 def test_decode_physical_permutation_is_bit_identical():
     w = W.WORKLOADS["llama3_8b_decode"].replace(num_seqs=8)
     a = _draw(w)
