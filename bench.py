@@ -121,11 +121,13 @@ TRAFFIC_PROFILES = {
 }
 
 
-def recorded_traffic(workload: str = "llama3_8b_decode", fp8: bool = False):
+def recorded_traffic(workload: str = "llama3_8b_decode", fp8: bool = False,
+                     fused: bool = False):
     """HBM bytes per decode launch from the committed counter summary
-    (FETCH_SIZE/WRITE_SIZE, calibrated on a plain copy; the fp8 op's line
-    when `fp8`), or None when no summary exists for the workload or the
-    decode sources differ from the ones the counters were taken on."""
+    (FETCH_SIZE/WRITE_SIZE, calibrated on a plain copy; the fp8 op's or the
+    fused op's line when asked), or None when no summary exists for the
+    workload or the decode sources differ from the ones the counters were
+    taken on."""
     import hashlib
     path = TRAFFIC_PROFILES.get(workload)
     if path is None:
@@ -136,6 +138,7 @@ def recorded_traffic(workload: str = "llama3_8b_decode", fp8: bool = False):
         return None
     value = None
     key = ("fp8_traffic_bytes_per_launch:" if fp8 else
+           "fused_traffic_bytes_per_launch:" if fused else
            "traffic_bytes_per_launch:")
     for line in text:
         if line.startswith(key):
@@ -199,7 +202,8 @@ class DecodeReplica:
 
     def __init__(self, inp, k_dev, v_dev, new_k, new_v, paged: bool,
                  steps: int, device, shared_op: bool = False,
-                 vmm_page_tokens: int = 0, fp8_scales=None):
+                 vmm_page_tokens: int = 0, fp8_scales=None,
+                 fused: bool = False):
         import torch
         from paged_kv_cache_191_amd import kvpaged as kv
         from paged_kv_cache_191_amd import workloads as W
@@ -208,6 +212,8 @@ class DecodeReplica:
         w = inp.workload
         self.w = w
         self.paged = paged
+        # the step's append fused into the decode op (paged bf16)
+        self.fused = fused and paged and fp8_scales is None and not shared_op
         S, B = w.num_seqs, w.block_size
         ctx = W.context_lengths(inp).astype(np.int64)
         self.lmax = int(ctx.max()) + steps + 1
@@ -348,6 +354,13 @@ class DecodeReplica:
         the replica's capacity, lmax, which holds every length of the run
         (the bound only clamps lengths)."""
         kv = self.kv
+        if self.fused:
+            self._write = None
+            self._decode = kv.bind(
+                kv.paged_attn_decode_append, self.out, self.q, self.new_k,
+                self.new_v, self.h_newb, self.k, self.v, self.d_table,
+                self.d_lens, self.lmax, self.scale, self.ws)
+            return
         if self.fp8:
             self._write = kv.bind(
                 kv.kv_append_token_fp8_per_head, self.new_k, self.new_v,
@@ -418,7 +431,17 @@ class DecodeReplica:
 
     def device_step(self, ev=None) -> None:
         """Cache write, then the decode op, bracketed by ev[0], ev[1]; ev[0]
-        also marks the end of the cache write."""
+        also marks the end of the cache write. Fused: the one op (append and
+        decode), bracketed by ev[0], ev[1]; its end frees the pinned
+        buffer."""
+        if self.fused:
+            if ev is not None:
+                ev[0].record()
+            self._decode()
+            self.uploaded = ev[1] if ev is not None else \
+                self.torch.cuda.Event()
+            self.uploaded.record()
+            return
         self.cache_write(ev[0] if ev is not None else None)
         self._decode()
         if ev is not None:
@@ -445,7 +468,7 @@ def fp8_head_scales(k_dev, v_dev):
 
 def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
                device, shared_op: bool = False, vmm_page_tokens: int = 0,
-               fp8: bool = False):
+               fp8: bool = False, fused: bool = False):
     import torch
     w = inp.workload
     new_k, new_v = new_token_kv(w, device)
@@ -453,7 +476,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     scales = fp8_head_scales(k_dev, v_dev) if fp8 else None
     reps_ = [DecodeReplica(inp, k_dev, v_dev, new_k, new_v, paged,
                            decode_steps_total(steps, warmup), device,
-                           shared_op, vmm_page_tokens, scales)
+                           shared_op, vmm_page_tokens, scales, fused)
              for _ in range(reps)]
     del k_dev, v_dev
     for i in range(warmup):
@@ -500,8 +523,9 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     # timed after the timed steps so that its events stay out of them. A
     # short spin kernel keeps the GPU busy while the host queues the events
     # and the write, so the interval is GPU time, not launch latency.
+    # (The fused op has no separate cache write.)
     rc_ev = []
-    for i in range(APPEND_TIMING_STEPS):
+    for i in range(0 if fused else APPEND_TIMING_STEPS):
         r = reps_[i % reps]
         r.host_append()
         e = tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
@@ -510,7 +534,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         r.cache_write(e[1])
         rc_ev.append(e)
     torch.cuda.synchronize()
-    rc = stats_ms([a.elapsed_time(b) for a, b in rc_ev])
+    rc = stats_ms([a.elapsed_time(b) for a, b in rc_ev]) if rc_ev else None
     res = {
         "wall_s": wall,
         "ms_per_step": 1e3 * wall / steps,
@@ -520,10 +544,12 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         "decode_op_ms_p10": op["p10"],
         "decode_op_ms_p90": op["p90"],
         "bytes_per_step": total_bytes / steps,
-        "cache_write": "kv_append_token" if not fp8 else
-                       "kv_append_token_fp8_per_head",
-        "cache_write_us_median": 1e3 * rc["median"],
+        "cache_write": ("fused into paged_attn_decode_append" if fused else
+                        "kv_append_token" if not fp8 else
+                        "kv_append_token_fp8_per_head"),
     }
+    if rc is not None:
+        res["cache_write_us_median"] = 1e3 * rc["median"]
     res["op_bytes_per_step"] = op_bytes / steps
     res["decode_op_GBps"] = res["op_bytes_per_step"] / (op["mean"] * 1e-3) / 1e9
     if logical_bytes != total_bytes:
@@ -533,7 +559,8 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     # the new rows: K and V, read once (bf16) and written once
     tok_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * (
         2 + (1 if fp8 else 2))
-    res["cache_write_GBps"] = tok_bytes / (rc["median"] * 1e-3) / 1e9
+    if rc is not None:
+        res["cache_write_GBps"] = tok_bytes / (rc["median"] * 1e-3) / 1e9
     if vmm_page_tokens and not paged:
         P = vmm_page_tokens
         r0 = reps_[0]
@@ -1037,6 +1064,8 @@ def roofline_record(bound: str, achieved: float, peak: float, unit: str,
 
 
 DECODE_KERNEL = "paged_attn_decode (decode_sk_kernel + decode_combine_kernel)"
+FUSED_KERNEL = ("paged_attn_decode_append (decode_sk_kernel + "
+                "decode_combine_kernel, the step's append fused)")
 SHARED_KERNEL = ("paged_attn_decode_shared_prefix (prefill_pp_kernel<true,"
                  "true> + decode_sk_kernel + decode_combine_kernel)")
 
@@ -1105,6 +1134,10 @@ def bench_decode_config(name: str, args, device) -> dict:
             except kv.KVError as e:
                 log(f"demand-mapped decode failed: {e}")
                 runs["contig_demand_mapped"] = {"error": str(e)}
+    if not prefix:
+        log(f"{name}: paged decode steps, append fused into the decode op")
+        runs["paged_fused"] = run_decode(inp, True, args.steps, args.warmup,
+                                         args.replicas, device, fused=True)
     if not args.no_fp8 and not prefix:
         log(f"{name}: paged decode steps over fp8 caches (per-head scales)")
         runs["paged_fp8"] = run_decode(inp, True, args.steps, args.warmup,
@@ -1128,6 +1161,10 @@ def bench_decode_config(name: str, args, device) -> dict:
     if vm and "error" not in vm:
         rl[name + "_contig_demand_mapped"] = decode_roofline(
             vm, "contig_attn_decode on demand-mapped memory")
+    if "paged_fused" in runs:
+        rl[name + "_fused"] = decode_roofline(
+            runs["paged_fused"], FUSED_KERNEL,
+            recorded_traffic(name, fused=True))
     if "paged_fp8" in runs:
         rl[name + "_fp8"] = decode_roofline(
             runs["paged_fp8"], "paged_attn_decode_fp8_per_head "
@@ -1364,7 +1401,9 @@ def main() -> int:
         return 0
     head = "llama3_8b_decode" if "llama3_8b_decode" in decoded else \
         next(iter(decoded))
-    hp = decoded[head]["runs"]["paged"]
+    runs_h = decoded[head]["runs"]
+    fused_h = "paged_fused" in runs_h
+    hp = runs_h["paged_fused"] if fused_h else runs_h["paged"]
     wd = __import__("paged_kv_cache_191_amd.workloads",
                     fromlist=["WORKLOADS"]).WORKLOADS[head]
     line = {
@@ -1385,13 +1424,14 @@ def main() -> int:
             "num_seqs": wd.num_seqs, "num_q_heads": wd.num_q_heads,
             "num_kv_heads": wd.num_kv_heads, "head_dim": wd.head_dim,
             "block_size": wd.block_size, "context": CTX_DESC[wd.name],
-            "step": "append+kv_append_token+" + (
-                "paged_attn_decode_shared_prefix" if wd.kind == "prefix"
-                else "paged_attn_decode"),
+            "step": ("append+paged_attn_decode_append" if fused_h else
+                     "append+kv_append_token+" + (
+                         "paged_attn_decode_shared_prefix"
+                         if wd.kind == "prefix" else "paged_attn_decode")),
             "replicas": args.replicas,
             "configs_run": configs,
         },
-        "roofline": rooflines[head],
+        "roofline": rooflines[head + "_fused" if fused_h else head],
     }
     if prefill and "paged_b16" in prefill["layouts"]:
         p16 = dict(rooflines["yi6b_chunked_prefill_paged_b16"])

@@ -232,6 +232,35 @@ size_t kv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_context);
 
+/* One decode step with the step's token appended, in one op: the same
+ * result and the same cache, table and length updates as kv_append_token
+ * (k_new, v_new, new_blocks, block_tables, context_lens, ...) followed by
+ * paged_attn_decode over the lengths it advanced ["PagedAttention Nedir?"
+ * (bitcanli.com), "PagedAttention Nasıl Çalışır?", steps 2-4: the new
+ * token's K/V take the slot its table assigns, then the query attends to
+ * the whole context]. The attention reads the new token from k_new / v_new
+ * rather than from the cache, so the cache write (the K and V rows, the
+ * table entry when new_blocks[s] >= 0, context_lens[s] + 1) is done by the
+ * merge kernel after the attention and no separate append launch is made.
+ * Arguments as in kv_append_token and paged_attn_decode; context_lens
+ * holds the lengths before the token and is advanced in place; the
+ * workspace is kv_decode_workspace_bytes(). A sequence whose token
+ * position lies outside [0, bt_stride * block_size) is not advanced and
+ * attends to its stored context only. A position inside the table whose
+ * block is invalid (new_blocks[s] < 0 and an entry outside
+ * [0, num_blocks)) is a caller error: the token is attended to but not
+ * stored, and the length is not advanced. Shapes other than bf16,
+ * head_dim 128, block_size % 16 == 0 (or rows not 16-byte aligned) run the
+ * two calls in order. */
+kv_status paged_attn_decode_append(
+    void* out, const void* q, const void* k_new, const void* v_new,
+    const int32_t* new_blocks, void* k_cache, void* v_cache,
+    int32_t num_blocks, int32_t* block_tables, int32_t bt_stride,
+    int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, kv_dtype dtype, void* workspace,
+    size_t workspace_bytes, void* stream);
+
 /* Number of sequences whose context_lens entry the last decode call on this
  * workspace clamped (see above): waits for `stream`, then copies the count
  * from the workspace header into *count. KV_EHIP if the copy fails. */

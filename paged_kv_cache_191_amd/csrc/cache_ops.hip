@@ -430,9 +430,9 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(
   }
 }
 
-// Device address of a pointer the device can use: device memory as is,
-// pinned host memory through its device mapping. NULL otherwise.
-void* device_view(const void* p) {
+}  // namespace
+
+void* kvp_device_view(const void* p) {
   hipPointerAttribute_t a;
   if (hipPointerGetAttributes(&a, p) != hipSuccess) {
     (void)hipGetLastError();  // pageable host memory: clear the error
@@ -443,7 +443,6 @@ void* device_view(const void* p) {
   if (a.type == hipMemoryTypeHost) return a.devicePointer;
   return nullptr;
 }
-}  // namespace
 
 extern "C" kv_status kv_swap_blocks(const void* src_k, const void* src_v,
                                     int32_t src_blocks, void* dst_k,
@@ -463,7 +462,7 @@ extern "C" kv_status kv_swap_blocks(const void* src_k, const void* src_v,
   const void* ptrs[5] = {src_k, src_v, dst_k, dst_v, pairs};
   void* dev[5];
   for (int i = 0; i < 5; ++i) {
-    dev[i] = device_view(ptrs[i]);
+    dev[i] = kvp_device_view(ptrs[i]);
     if (!dev[i])
       return kvp_fail(KV_EINVAL,
                       "kv_swap_blocks: %s is not device or pinned host memory",
@@ -511,7 +510,7 @@ extern "C" kv_status kv_append_token(const void* k, const void* v,
   if (!k || !v || !new_blocks || !block_tables || !context_lens || !k_cache ||
       !v_cache)
     return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
-  const int32_t* nb = (const int32_t*)device_view(new_blocks);
+  const int32_t* nb = (const int32_t*)kvp_device_view(new_blocks);
   if (!nb)
     return kvp_fail(KV_EINVAL, "%s: new_blocks is not device or pinned host "
                     "memory", name);
@@ -566,7 +565,7 @@ kv_status append_token_fp8(const char* name, const void* k, const void* v,
       ((uintptr_t)k_cache | (uintptr_t)v_cache) % 8)
     return kvp_fail(KV_EINVAL, "%s: k/v must be 16-byte and the caches "
                     "8-byte aligned", name);
-  const int32_t* nb = (const int32_t*)device_view(new_blocks);
+  const int32_t* nb = (const int32_t*)kvp_device_view(new_blocks);
   if (!nb)
     return kvp_fail(KV_EINVAL, "%s: new_blocks is not device or pinned host "
                     "memory", name);

@@ -113,6 +113,14 @@ struct DecodeArgs {
   int32_t pre_stride;   // sequences between two pieces of pre_o / pre_ml
   float* whole_o;       // [S, Hq, D] own part of a sequence in one chunk
   float* whole_ml;      // [S, Hq, 2]
+  // decode with this step's token appended (k_new NULL: plain decode)
+  const void* k_new;    // [S, Hkv, D] the token's K and V (bf16)
+  const void* v_new;
+  const int32_t* new_blocks;  // [S] block for table[s][L / B] (-1: keep)
+  int32_t* bt_w;        // the table, lengths and caches, written by the
+  int32_t* ctx_w;       // merge kernel once the attention is done
+  void* k_cache_w;
+  void* v_cache_w;
 };
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int c,
@@ -131,6 +139,16 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int c,
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s,
                                          bool paged) {
   return clamp_len(a, a.ctx[s], paged);
+}
+
+// A stored length as the attention sees it: with this step's token
+// appended (k_new set), one more when the token's position lies inside the
+// table (the condition under which it is stored).
+template <bool APPEND>
+__device__ __forceinline__ int with_new(const DecodeArgs& a, int stored) {
+  if (!APPEND) return stored;
+  const int64_t cap = (int64_t)a.bt_stride * a.block_size;
+  return stored + (stored >= 0 && stored < cap ? 1 : 0);
 }
 
 // Workgroup 0 of a launch records how many of its sequences were clamped.
@@ -195,7 +213,8 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
 
 // KV8: K/V cache in fp8 E4M3 (one byte per value, converted to bf16 in
 // registers; K's scale is folded into scale_log2, V's applied to outputs).
-template <bool PAGED, bool KV8>
+// APPEND: this step's token is read from k_new / v_new (paged bf16 only).
+template <bool PAGED, bool KV8, bool APPEND = false>
 __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     DecodeArgs a) {
   constexpr int ES = KV8 ? 1 : 2;  // bytes per K/V value
@@ -203,6 +222,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   __shared__ int s_cs[kMaxSeqs + 1];
   __shared__ int s_part[kWaves];
   __shared__ int s_clamped;
+  __shared__ u32x4 s_newrow[2 * kD * 2 / 16];  // this step's K and V rows
   __shared__ float sm_o[kWaves][kHeadBlk][kD];
   __shared__ float sm_ml[kWaves][kHeadBlk][2];
 
@@ -229,7 +249,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     const int hi = min(S, lo + per);
     int sum = 0, clamped = 0;
     for (int i = lo; i < hi; ++i) {
-      const int raw = a.ctx[i];
+      const int raw = with_new<APPEND>(a, a.ctx[i]);
       const int L = clamp_len(a, raw, PAGED);
       clamped += L != raw;
       const int n = tiles_of(L - shared_of(a, i, L));
@@ -296,10 +316,17 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     const int lo_t = pos - seq_lo;
     const int hi_t = min(c1 - seq_lo, nt);
     pos = seq_lo + hi_t;
-    const int L = clamp_ctx(a, s, PAGED);
+    const int stored = a.ctx[s];
+    const int raw = with_new<APPEND>(a, stored);
+    const int L = clamp_len(a, raw, PAGED);
+    // this step's token (position `stored`) is read from k_new / v_new,
+    // not from the cache
+    const bool new_in = APPEND && raw != stored && L == raw;
+    const int L_cache = new_in ? L - 1 : L;
     const int P = shared_of(a, s, L);  // tokens before the own tiles
     const int lo = P + kTile * lo_t;
     const int hi = min(P + kTile * hi_t, L);
+    const int hi_c = min(hi, L_cache);  // end of the cached tokens
 
     const int qh = g * a.group + (h_valid ? h_in_group : 0);
     // Q^T: B operand, head r16; d = 32 i + 8 grp + e (bf16 K) or
@@ -322,10 +349,26 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
 #pragma unroll
     for (int m = 0; m < 8; ++m) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // This step's token is folded in by the last wave (the one with the
+    // fewest of the segment's tiles) after its tiles; its K and V rows
+    // (16 + 16 units of 16 bytes) are read now, one unit per lane, so that
+    // they arrive while the tiles stream.
+    const bool fold_new = APPEND && new_in && hi_t == nt && w == kWaves - 1;
+    u32x4 new_unit = u32x4{0, 0, 0, 0};
+    if (fold_new && lane < 2 * kD * 2 / 16) {
+      const int64_t row = ((int64_t)s * a.hkv + g) * kD;
+      const bf16* src = lane < kD * 2 / 16
+                            ? (const bf16*)a.k_new + row + 8 * lane
+                            : (const bf16*)a.v_new + row + 8 * (lane - 16);
+      new_unit = ld16(src);
+    }
+
     // tiles covering [lo, hi); wave w takes tiles w, w+4, ...
     const int t_al = lo;
-    const int n_tiles = hi_t - lo_t;
-    const int last_grp_pos = (hi - 1) & ~15;  // start of the last valid group
+    // tiles holding cached tokens (this step's token alone needs none)
+    const int n_tiles = (max(hi_c - lo, 0) + kTile - 1) / kTile;
+    // start of the last cached group (the first group when none is)
+    const int last_grp_pos = max(hi_c - 1, 0) & ~15;
     const int64_t seq_row0 = ((int64_t)s * a.hkv + g) * a.seq_stride;
 
     for (int kb0 = 0; kb0 < n_tiles; kb0 += kWaves * (kGroupsPerLoad / 2)) {
@@ -358,7 +401,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
         return base + row * (kD * ES);
       };
       auto lane_off = [&](int j, int hf, int off, int chunk) -> uint32_t {
-        const int r = PAGED ? off : min(off, hi - 1 - half_start(j, hf));
+        const int r = PAGED ? off : min(off, hi_c - 1 - half_start(j, hf));
         return (uint32_t)(r * (kD * ES) + 8 * ES * chunk);
       };
       // 8 consecutive K/V values of a row, as stored; to_bf16 widens them
@@ -428,7 +471,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
             sc[hf] = mfma16(k_op(kraw, hf, i), qop[i], sc[hf]);
         }
 
-        const bool full = t + kTile <= hi;
+        const bool full = t + kTile <= hi_c;
         float x[2][4];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -436,7 +479,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
           for (int r = 0; r < 4; ++r) {
             const float v = sc[hf][r] * scale_log2;
             const int p = t + 16 * hf + 4 * grp + r;
-            x[hf][r] = (full || p < hi) ? v : -INFINITY;
+            x[hf][r] = (full || p < hi_c) ? v : -INFINITY;
           }
         float mx =
             fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
@@ -479,7 +522,7 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int pe = t + 16 * (e >> 2) + 4 * grp + (e & 3);
-            if (pe >= hi) vr[e] = u32x4{0, 0, 0, 0};
+            if (pe >= hi_c) vr[e] = u32x4{0, 0, 0, 0};
           }
         }
         // V^T rows d = 8 r16 + m: element e of A_m is V[tau(grp, e)][8r16+m]
@@ -505,6 +548,54 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
         // issue the V loads late, halving the bytes in flight).
         __builtin_amdgcn_sched_barrier(0);
         compute_tile(j, kraw, vraw);
+      }
+    }
+
+    // This step's token, at the sequence's end (one key): its rows go
+    // through LDS into the lanes' layouts, then a dot product per head and
+    // p V.
+    if constexpr (APPEND) {
+      if (fold_new) {
+        if (lane < 2 * kD * 2 / 16) s_newrow[lane] = new_unit;
+        // the same wave reads what it wrote
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // K at d = 32 i + 8 grp + e, as in qop[i]: unit 4 i + grp
+          const u32x4 kr = s_newrow[4 * i + grp];
+          const u32x4 qr = as_u32x4(qop[i]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dot = __builtin_fmaf(bf16_lo(qr[e]), bf16_lo(kr[e]), dot);
+            dot = __builtin_fmaf(bf16_hi(qr[e]), bf16_hi(kr[e]), dot);
+          }
+        }
+        dot += __shfl_xor(dot, 16);
+        dot += __shfl_xor(dot, 32);
+        const float x = dot * scale_log2;
+        if (__any(x > m_run + kRescaleLog2)) {
+          const float m_new = fmaxf(m_run, x);
+          const float alpha = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_part *= alpha;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) o[m] *= alpha;
+        }
+        const float pn = fast_exp2(x - m_run);
+        if (grp == 0) l_part += pn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // V at d = 32 grp + 8 r + m, as in o[m][r]: unit 16 + 4 grp + r
+          const u32x4 vr = s_newrow[16 + 4 * grp + r];
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t wv = vr[m >> 1];
+            o[m][r] += pn * ((m & 1) ? bf16_hi(wv) : bf16_lo(wv));
+          }
+        }
       }
     }
 
@@ -601,11 +692,72 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
 // values) with a running max; the four lane groups are then merged by
 // shuffles. Also writes zeros for empty contexts.
 constexpr int kCombineThreads = kWave;
+
+// This step's token of sequence s (decode with append), stored as
+// kv_append_token stores it: the K and V rows of every KV head into the
+// slot of position context_lens[s], the table entry when new_blocks[s] >= 0,
+// then the length + 1; nothing when the position lies outside the table or
+// names no valid block. One wave per sequence (an extra column of the
+// merge grid), after the attention: no other workgroup of the op reads
+// these entries any more.
+__device__ void append_token_of(const DecodeArgs& a, int s, int lane) {
+  constexpr int kUnits = kD * 2 / 16;  // 16-byte units of a head row
+  constexpr int kAhead = 4;            // units per lane read up front
+  const int per_tensor = a.hkv * kUnits;
+  const int stored = a.ctx_w[s];
+  const int64_t cap = (int64_t)a.bt_stride * a.block_size;
+  const bool ok_pos = stored >= 0 && stored < cap;
+  const int idx = ok_pos ? stored / a.block_size : 0;
+  int32_t* entry = a.bt_w + (int64_t)s * a.bt_stride + idx;
+  // the block id (host memory, possibly) and the current entry, and the
+  // first rows, all in flight together
+  const int nb = a.new_blocks[s];
+  const int old = ok_pos ? *entry : -1;
+  auto src_of = [&](int i) {
+    const bool is_v = i >= per_tensor;
+    const int r = is_v ? i - per_tensor : i;
+    return (const u32x4*)(is_v ? a.v_new : a.k_new) + (int64_t)s * per_tensor +
+           r;
+  };
+  auto dst_of = [&](int i, int blk, int off) {
+    const bool is_v = i >= per_tensor;
+    const int r = is_v ? i - per_tensor : i;
+    const int hh = r / kUnits;
+    return (u32x4*)(is_v ? a.v_cache_w : a.k_cache_w) +
+           (((int64_t)blk * a.hkv + hh) * a.block_size + off) * kUnits +
+           (r - hh * kUnits);
+  };
+  u32x4 x[kAhead];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    const int i = lane + k * kWave;
+    if (i < 2 * per_tensor) x[k] = *src_of(i);
+  }
+  const int blk = nb >= 0 ? nb : old;
+  if (!(ok_pos && blk >= 0 && blk < a.num_blocks)) return;
+  const int off = stored - idx * a.block_size;
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    const int i = lane + k * kWave;
+    if (i < 2 * per_tensor) *dst_of(i, blk, off) = x[k];
+  }
+  for (int i = lane + kAhead * kWave; i < 2 * per_tensor; i += kWave)
+    *dst_of(i, blk, off) = *src_of(i);
+  if (lane == 0) {
+    if (nb >= 0) *entry = nb;
+    a.ctx_w[s] = stored + 1;
+  }
+}
+
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     DecodeArgs a) {
   const int s = blockIdx.x;
   const int h = blockIdx.y;
   const int lane = threadIdx.x;
+  if (h == a.hq) {  // the extra column of a decode with append
+    append_token_of(a, s, lane);
+    return;
+  }
   const int c = lane & 15;
   const int j = lane >> 4;
   const int* cs = a.ws_cs;
@@ -910,6 +1062,13 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
       b.out = (bf16*)a.out + (size_t)s0 * a.hq * kD;
       b.q = (const bf16*)a.q + (size_t)s0 * a.hq * kD;
       b.ctx = a.ctx + s0;
+      if (a.k_new) {
+        b.k_new = (const bf16*)a.k_new + (size_t)s0 * a.hkv * kD;
+        b.v_new = (const bf16*)a.v_new + (size_t)s0 * a.hkv * kD;
+        b.new_blocks = a.new_blocks + s0;
+        b.bt_w = a.bt_w + (size_t)s0 * a.bt_stride;
+        b.ctx_w = a.ctx_w + s0;
+      }
       if (a.plen) {
         b.plen = a.plen + s0;
         b.pre_o = a.pre_o + (size_t)s0 * a.hq * kD;
@@ -928,6 +1087,9 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
       dim3 grid(a.hkv * a.head_blocks, a.n_chunks);
       if (paged && kv8)
         decode_sk_kernel<true, true><<<grid, kWaves * kWave, 0, st>>>(b);
+      else if (paged && a.k_new)
+        decode_sk_kernel<true, false, true><<<grid, kWaves * kWave, 0, st>>>(
+            b);
       else if (paged)
         decode_sk_kernel<true, false><<<grid, kWaves * kWave, 0, st>>>(b);
       else if (kv8)
@@ -935,7 +1097,8 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
       else
         decode_sk_kernel<false, false><<<grid, kWaves * kWave, 0, st>>>(b);
       KVP_LAUNCH_CHECK(name);
-      dim3 g2(b.num_seqs, a.hq);
+      // (with append, one more column per sequence stores its token)
+      dim3 g2(b.num_seqs, a.hq + (a.k_new ? 1 : 0));
       decode_combine_kernel<<<g2, kCombineThreads, 0, st>>>(b);
       KVP_LAUNCH_CHECK(name);
     }
@@ -1174,6 +1337,66 @@ extern "C" kv_status paged_attn_decode(
   a.scale_log2 = scale * kLog2e;
   return run_decode("paged_attn_decode", true, a, dtype, workspace,
                     workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" kv_status paged_attn_decode_append(
+    void* out, const void* q, const void* k_new, const void* v_new,
+    const int32_t* new_blocks, void* k_cache, void* v_cache,
+    int32_t num_blocks, int32_t* block_tables, int32_t bt_stride,
+    int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, kv_dtype dtype, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* name = "paged_attn_decode_append";
+  if (num_seqs < 0)
+    return kvp_fail(KV_EINVAL, "%s: num_seqs must be >= 0", name);
+  if (num_seqs == 0) return KV_OK;
+  const bool aligned = (((uintptr_t)k_new | (uintptr_t)v_new) & 15) == 0;
+  if (!fast_path_ok(dtype, head_dim, block_size, true) || !aligned) {
+    // shapes the stream-K kernel does not cover (or rows not 16-byte
+    // aligned): the two calls it fuses
+    const kv_status st = kv_append_token(
+        k_new, v_new, new_blocks, block_tables, bt_stride, context_lens,
+        num_seqs, k_cache, v_cache, num_blocks, block_size, num_kv_heads,
+        head_dim, dtype, stream);
+    if (st != KV_OK) return st;
+    return paged_attn_decode(out, q, k_cache, v_cache, num_blocks,
+                             block_tables, bt_stride, context_lens,
+                             max_context, num_seqs, num_q_heads, num_kv_heads,
+                             head_dim, block_size, scale, dtype, workspace,
+                             workspace_bytes, stream);
+  }
+  if (!k_new || !v_new || !new_blocks)
+    return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
+  const int32_t* nb = (const int32_t*)kvp_device_view(new_blocks);
+  if (!nb)
+    return kvp_fail(KV_EINVAL, "%s: new_blocks is not device or pinned host "
+                    "memory", name);
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.ctx = context_lens;
+  a.max_ctx = max_context;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale_log2 = scale * kLog2e;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_blocks = nb;
+  a.bt_w = block_tables;
+  a.ctx_w = context_lens;
+  a.k_cache_w = k_cache;
+  a.v_cache_w = v_cache;
+  return run_decode(name, true, a, dtype, workspace, workspace_bytes,
+                    (hipStream_t)stream);
 }
 
 extern "C" kv_status paged_attn_decode_fp8(

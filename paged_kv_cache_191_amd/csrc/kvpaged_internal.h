@@ -7,12 +7,16 @@ kv_status kvp_fail(kv_status st, const char* fmt, ...);
 
 #include <hip/hip_runtime.h>
 
+// Device address of a pointer the device can use: device memory as is,
+// pinned host memory through its device mapping; NULL otherwise.
+void* kvp_device_view(const void* p);
+
 // One launch of the shared-prefix partial attention (prefill.hip): the
 // decode queries of the members of each group against the group's shared
 // tokens, read through the first member's table, split into nsplit pieces
 // of ksplit keys. Writes plen[member] (shared tokens the member's own pass
-// skips) and the partials po/pml. bf16, head_dim 128, (Hq/Hkv) % 4 == 0,
-// block_size % 16 == 0.
+// skips) and the partials po/pml. bf16, head_dim 128, block_size % 16 ==
+// 0 (any Hq / Hkv).
 struct KvpPrefixJob {
   const void* q;
   const void* k;

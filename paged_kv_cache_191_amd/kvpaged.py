@@ -93,6 +93,9 @@ SIGNATURES = {
     "paged_attn_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P, _I32,
                                  _I32, _I32, _I32, _I32, _I32, _F, _I32, _P,
                                  _SZ, _P]),
+    "paged_attn_decode_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32,
+                                        _P, _I32, _P, _I32, _I32, _I32, _I32,
+                                        _I32, _I32, _F, _I32, _P, _SZ, _P]),
     "paged_attn_decode_noalloc": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P,
                                          _I32, _I32, _I32, _I32, _I32, _I32,
                                          _F, _I32, _P]),
@@ -750,6 +753,40 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         int(max_context), S, hq, hkv, d, bs, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "paged_attn_decode")
+
+
+def paged_attn_decode_append(out, q, k_new, v_new, new_blocks, k_cache,
+                             v_cache, block_tables, context_lens,
+                             max_context: int, scale: float, workspace=None,
+                             stream=None) -> None:
+    """kv_append_token(k_new, v_new, new_blocks, block_tables, context_lens,
+    k_cache, v_cache) then paged_attn_decode over the advanced lengths, as
+    one op (the attention reads the new token from k_new / v_new; the merge
+    kernel stores it). context_lens is advanced in place."""
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, hkv, bs, dk = k_cache.shape
+    _attn_shapes(out, q, k_cache, v_cache, dk, S,
+                 ((block_tables, "block_tables"),
+                  (context_lens, "context_lens")))
+    _ndim(block_tables, 2, "block_tables")
+    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d):
+        raise ValueError("k_new and v_new must be [num_seqs, Hkv, D]")
+    if new_blocks.shape[0] != S or not new_blocks.is_contiguous() or \
+            new_blocks.dtype != torch.int32:
+        raise ValueError("new_blocks must be a contiguous int32 [num_seqs]")
+    if workspace is None:
+        workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
+    st = _invoke("paged_attn_decode_append",
+        _dev(out, "out", q.dtype), _dev(q, "q"),
+        _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype),
+        new_blocks.data_ptr(), _dev(k_cache, "k_cache", q.dtype),
+        _dev(v_cache, "v_cache", q.dtype), nb,
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context), S, hq, hkv, d, bs, float(scale), _dtype_code(q),
+        _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "paged_attn_decode_append")
 
 
 def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables,
