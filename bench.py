@@ -1168,7 +1168,7 @@ def bench_decode_config(name: str, args, device) -> dict:
     if "paged_fp8" in runs:
         rl[name + "_fp8"] = decode_roofline(
             runs["paged_fp8"], "paged_attn_decode_fp8_per_head "
-            "(decode_sk_kernel<true,true> + decode_combine_kernel)",
+            "(decode_sk_kernel<true,true,false> + decode_combine_kernel)",
             recorded_traffic(name, fp8=True))
     if prefix:
         # headline bytes: the shared prefix once (unique); the plain decode
