@@ -118,7 +118,13 @@ TRAFFIC_PROFILES = {
                                       "hbm_traffic_decode_yi34b.txt"),
     "prefix_share_decode": os.path.join(ROOT, "profiles",
                                         "hbm_traffic_decode_prefix_share.txt"),
+    "yi6b_chunked_prefill_paged_b16": os.path.join(
+        ROOT, "profiles", "hbm_traffic_prefill_yi6b_paged_b16.txt"),
 }
+
+
+# profiles that count a whole prefill pass (16 chunk launches)
+PASS_PROFILES = ("yi6b_chunked_prefill_paged_b16",)
 
 
 def recorded_traffic(workload: str = "llama3_8b_decode", fp8: bool = False,
@@ -139,6 +145,7 @@ def recorded_traffic(workload: str = "llama3_8b_decode", fp8: bool = False,
     value = None
     key = ("fp8_traffic_bytes_per_launch:" if fp8 else
            "fused_traffic_bytes_per_launch:" if fused else
+           "traffic_bytes_per_pass:" if workload in PASS_PROFILES else
            "traffic_bytes_per_launch:")
     for line in text:
         if line.startswith(key):
@@ -1235,6 +1242,7 @@ def bench_prefill(args, device) -> dict:
     for lay, r in layouts.items():
         rl["yi6b_chunked_prefill_" + lay] = roofline_record(
             "mfma", r["TFLOPs"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
+            recorded_traffic("yi6b_chunked_prefill_" + lay),
             kernel=kernels[lay], tflop_per_pass=round(r["tflop"], 4),
             ms_per_pass=round(r["attn_ms"], 4))
         # the chunk's cache write: 2 x (read + write) of the new rows

@@ -240,6 +240,22 @@ def test_decode_append_many_steps():
     _log(f"40 fused steps: states bit-identical, outputs max-abs {worst:.2e}")
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (40, 2), (12, 4)])
+def test_decode_append_head_groups(hq, hkv):
+    # one query head per KV head, a group of 20 (two 16-head column blocks,
+    # so two workgroups fold the token for each KV head), a group of 3
+    lengths = (1, 31, 32, 33, 500, 64)
+    w = W.WORKLOADS["llama3_8b_decode"].replace(
+        num_seqs=len(lengths), lengths=lengths, length_range=None,
+        num_q_heads=hq, num_kv_heads=hkv, name=f"append_g{hq // hkv}")
+    inp = W.draw(w, lambda L: H.pool_blocks_for(w, L, 8))
+    ctx = np.array(lengths, dtype=np.int32)
+    B = w.block_size
+    cap = H.tables_capacity(int(ctx.max()), B)
+    _compare(inp, B, cap, ctx - 1, np.ones(len(lengths), dtype=np.int32),
+             int(ctx.max()), ctx)
+
+
 @pytest.mark.parametrize("variant", ["f32", "b8"])
 def test_decode_append_fallback_shapes(variant):
     # shapes outside the stream-K kernel run the two calls: identical
