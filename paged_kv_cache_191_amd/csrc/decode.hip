@@ -337,9 +337,9 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
                        (KV8 ? 32 : 8) * grp;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        u32x4 raw = ld16(qp + (KV8 ? 8 : 32) * i);
-        if (!h_valid) raw = u32x4{0, 0, 0, 0};
-        qop[i] = as_bf16x8(raw);
+        u32x4 qraw = ld16(qp + (KV8 ? 8 : 32) * i);
+        if (!h_valid) qraw = u32x4{0, 0, 0, 0};
+        qop[i] = as_bf16x8(qraw);
       }
     }
 
