@@ -1162,7 +1162,7 @@ bool shared_fast_ok(kv_dtype dtype, int hq, int hkv, int head_dim,
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// [plen: S int32][pre_o, pre_ml: nsplit pieces][whole_o, whole_ml]
+// [plen: S int32][pre_o: nsplit pieces][whole_o][pre_ml][whole_ml]
 size_t shared_extra_bytes(int num_seqs, int hq, int nsplit) {
   return align256((size_t)num_seqs * sizeof(int32_t)) +
          (size_t)(nsplit + 1) * num_seqs * hq * (kD + 2) * sizeof(float);
@@ -1242,10 +1242,12 @@ extern "C" kv_status paged_attn_decode_shared_prefix(
       num_seqs, num_q_heads, num_kv_heads, head_dim, max_context));
   char* wp = (char*)workspace + base;
   int32_t* plen = (int32_t*)wp;
+  // outputs first (rows of kD floats stay 16-byte aligned), then the
+  // (max, sum) pairs
   float* pre_o = (float*)(wp + align256((size_t)num_seqs * sizeof(int32_t)));
-  float* pre_ml = pre_o + (size_t)nsplit * num_seqs * num_q_heads * kD;
-  float* whole_o = pre_ml + (size_t)nsplit * num_seqs * num_q_heads * 2;
-  float* whole_ml = whole_o + (size_t)num_seqs * num_q_heads * kD;
+  float* whole_o = pre_o + (size_t)nsplit * num_seqs * num_q_heads * kD;
+  float* pre_ml = whole_o + (size_t)num_seqs * num_q_heads * kD;
+  float* whole_ml = pre_ml + (size_t)nsplit * num_seqs * num_q_heads * 2;
   if (block_size <= 0 || bt_stride <= 0 || num_blocks <= 0 || !block_tables ||
       !context_lens || !q || !k_cache || !v_cache || !out)
     return kvp_fail(KV_EINVAL, "%s: bad paging arguments or NULL pointer",
