@@ -350,6 +350,10 @@ class DecodeReplica:
         # (the decode op's start event in a step).
         self.uploaded = torch.cuda.Event()
         self.uploaded.record()
+        # the replica's own event for steps without timing events (recorded
+        # again each step: the next host_append of this replica has waited
+        # on it by then)
+        self.done_ev = torch.cuda.Event()
         self.scale = 1.0 / float(np.sqrt(w.head_dim))
         self._bind_launches()
         torch.cuda.synchronize()
@@ -433,7 +437,7 @@ class DecodeReplica:
         table entry and the length on the device. `done` (an event, default
         a new one) is recorded after it and marks the pinned buffer free."""
         self._write()
-        self.uploaded = done if done is not None else self.torch.cuda.Event()
+        self.uploaded = done if done is not None else self.done_ev
         self.uploaded.record()
 
     def device_step(self, ev=None) -> None:
@@ -445,8 +449,7 @@ class DecodeReplica:
             if ev is not None:
                 ev[0].record()
             self._decode()
-            self.uploaded = ev[1] if ev is not None else \
-                self.torch.cuda.Event()
+            self.uploaded = ev[1] if ev is not None else self.done_ev
             self.uploaded.record()
             return
         self.cache_write(ev[0] if ev is not None else None)
@@ -493,25 +496,30 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     torch.cuda.synchronize()
     kv_es = 1 if fp8 else 0
 
-    def step_bytes(r):
-        args = (r.h_lens, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                w.block_size, paged)
+    def step_bytes(r, lens=None):
+        args = (r.h_lens if lens is None else lens, w.num_q_heads,
+                w.num_kv_heads, w.head_dim, w.block_size, paged)
         return (decode_bytes(*args, shared=r.shared, kv_esize=kv_es),
                 decode_bytes(*args, kv_esize=kv_es))
 
     # The timed steps: host append, cache write and decode op, nothing else
-    # queued (the per-op events are a second pass below).
-    total_bytes = logical_bytes = 0
+    # queued (the per-op events are a second pass below). The lengths each
+    # step attends over are copied aside; their bytes are counted after the
+    # timed region.
+    lens_seen = []
     t0 = time.perf_counter()
     for i in range(steps):
         r = reps_[i % reps]
         r.host_append()
-        b, lb = step_bytes(r)
-        total_bytes += b
-        logical_bytes += lb
+        lens_seen.append((r, r.h_lens.copy()))
         r.device_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    total_bytes = logical_bytes = 0
+    for r, lens in lens_seen:
+        b, lb = step_bytes(r, lens)
+        total_bytes += b
+        logical_bytes += lb
     # The same steps again (the contexts one token per replica round
     # longer), each decode op bracketed by events: its GPU time.
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
