@@ -143,7 +143,8 @@ def recorded_traffic(workload: str = "llama3_8b_decode", fp8: bool = False,
     except OSError:
         return None
     value = None
-    key = ("fp8_traffic_bytes_per_launch:" if fp8 else
+    key = ("fp8_fused_traffic_bytes_per_launch:" if fp8 and fused else
+           "fp8_traffic_bytes_per_launch:" if fp8 else
            "fused_traffic_bytes_per_launch:" if fused else
            "traffic_bytes_per_pass:" if workload in PASS_PROFILES else
            "traffic_bytes_per_launch:")
@@ -219,8 +220,8 @@ class DecodeReplica:
         w = inp.workload
         self.w = w
         self.paged = paged
-        # the step's append fused into the decode op (paged bf16)
-        self.fused = fused and paged and fp8_scales is None and not shared_op
+        # the step's append fused into the decode op (paged, bf16 or fp8)
+        self.fused = fused and paged and not shared_op
         S, B = w.num_seqs, w.block_size
         ctx = W.context_lengths(inp).astype(np.int64)
         self.lmax = int(ctx.max()) + steps + 1
@@ -365,6 +366,14 @@ class DecodeReplica:
         the replica's capacity, lmax, which holds every length of the run
         (the bound only clamps lengths)."""
         kv = self.kv
+        if self.fused and self.fp8:
+            self._write = None
+            self._decode = kv.bind(
+                kv.paged_attn_decode_append_fp8_per_head, self.out, self.q,
+                self.new_k, self.new_v, self.h_newb, self.k, self.v,
+                self.d_table, self.d_lens, self.lmax, self.scale,
+                self.k_scales, self.v_scales, self.ws)
+            return
         if self.fused:
             self._write = None
             self._decode = kv.bind(
@@ -559,8 +568,9 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         "decode_op_ms_p10": op["p10"],
         "decode_op_ms_p90": op["p90"],
         "bytes_per_step": total_bytes / steps,
-        "cache_write": ("fused into paged_attn_decode_append" if fused else
-                        "kv_append_token" if not fp8 else
+        "cache_write": (("fused into paged_attn_decode_append_fp8_per_head"
+                         if fp8 else "fused into paged_attn_decode_append")
+                        if fused else "kv_append_token" if not fp8 else
                         "kv_append_token_fp8_per_head"),
     }
     if rc is not None:
@@ -1157,6 +1167,10 @@ def bench_decode_config(name: str, args, device) -> dict:
         log(f"{name}: paged decode steps over fp8 caches (per-head scales)")
         runs["paged_fp8"] = run_decode(inp, True, args.steps, args.warmup,
                                        args.replicas, device, fp8=True)
+        log(f"{name}: the same, append fused into the fp8 decode op")
+        runs["paged_fp8_fused"] = run_decode(
+            inp, True, args.steps, args.warmup, args.replicas, device,
+            fp8=True, fused=True)
     cow = None
     if prefix and not args.no_cow:
         log(f"{name}: copy-on-write step")
@@ -1185,6 +1199,11 @@ def bench_decode_config(name: str, args, device) -> dict:
             runs["paged_fp8"], "paged_attn_decode_fp8_per_head "
             "(decode_sk_kernel<true,true,false> + decode_combine_kernel)",
             recorded_traffic(name, fp8=True))
+    if "paged_fp8_fused" in runs:
+        rl[name + "_fp8_fused"] = decode_roofline(
+            runs["paged_fp8_fused"], "paged_attn_decode_append_fp8_per_head "
+            "(decode_sk_kernel<true,true,true> + decode_combine_kernel)",
+            recorded_traffic(name, fp8=True, fused=True))
     if prefix:
         # headline bytes: the shared prefix once (unique); the plain decode
         # reads it once per sequence, mostly from cache

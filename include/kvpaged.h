@@ -500,6 +500,36 @@ kv_status contig_attn_decode_fp8_per_head(
     const float* k_scales, const float* v_scales, void* workspace,
     size_t workspace_bytes, void* stream);
 
+/* paged_attn_decode_append on fp8 E4M3 caches: the same result and the
+ * same cache, table and length updates as kv_append_token_fp8 (or
+ * kv_append_token_fp8_per_head) followed by paged_attn_decode_fp8 (or
+ * _per_head) over the advanced lengths, in one op. k_new / v_new are bf16;
+ * the attention takes the new token as the codes the cache will hold (its
+ * rows quantised with the head's 1 / scale, then widened back), so the
+ * result is that of the two calls; the merge kernel stores those codes,
+ * the table entry and the length after the attention. Scales, arguments
+ * and errors as in those calls; head_dim 128 and block_size % 16 == 0
+ * only (others: KV_EUNSUPPORTED, nothing written); k_new / v_new 16-byte
+ * and the caches 8-byte aligned (else KV_EINVAL). */
+kv_status paged_attn_decode_append_fp8(
+    void* out, const void* q, const void* k_new, const void* v_new,
+    const int32_t* new_blocks, void* k_cache, void* v_cache,
+    int32_t num_blocks, int32_t* block_tables, int32_t bt_stride,
+    int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, float k_scale, float v_scale,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+kv_status paged_attn_decode_append_fp8_per_head(
+    void* out, const void* q, const void* k_new, const void* v_new,
+    const int32_t* new_blocks, void* k_cache, void* v_cache,
+    int32_t num_blocks, int32_t* block_tables, int32_t bt_stride,
+    int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, const float* k_scales,
+    const float* v_scales, void* workspace, size_t workspace_bytes,
+    void* stream);
+
 /* ---------------------------------------------------------------------
  * Prefix cache over a block pool ["PagedAttention Nedir?" (bitcanli.com),
  * section "Prefix Sharing Nasıl Çalışır?"]: the K/V of a prompt's leading

@@ -121,6 +121,10 @@ struct DecodeArgs {
   int32_t* ctx_w;       // merge kernel once the attention is done
   void* k_cache_w;
   void* v_cache_w;
+  int32_t kv8;          // the caches hold fp8 E4M3 codes
+  float k_inv, v_inv;   // fp8 K/V with append: 1 / scale of the tensor (the
+                        // token is stored as codes; k_scales / v_scales per
+                        // head when given)
 };
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int c,
@@ -213,7 +217,8 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
 
 // KV8: K/V cache in fp8 E4M3 (one byte per value, converted to bf16 in
 // registers; K's scale is folded into scale_log2, V's applied to outputs).
-// APPEND: this step's token is read from k_new / v_new (paged bf16 only).
+// APPEND: this step's token is read from k_new / v_new (bf16; paged only).
+// With KV8 it enters the attention as the codes the cache will hold.
 template <bool PAGED, bool KV8, bool APPEND = false>
 __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     DecodeArgs a) {
@@ -302,6 +307,12 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   const float scale_log2 = a.k_scales ? a.scale_log2 * a.k_scales[g]
                                       : a.scale_log2;
   const float v_scale = a.v_scales ? a.v_scales[g] : a.v_scale;
+  // fp8 with append: the reciprocals the token's codes are made with
+  float k_inv = 0.f, v_inv = 0.f;
+  if constexpr (KV8 && APPEND) {
+    k_inv = fp8_inv(a.k_scales, a.k_inv, g);
+    v_inv = fp8_inv(a.v_scales, a.v_inv, g);
+  }
   const int h_in_group = hblk * kHeadBlk + r16;
   const bool h_valid = h_in_group < a.group;
   const int nh = min(kHeadBlk, a.group - hblk * kHeadBlk);
@@ -556,7 +567,17 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
     // p V.
     if constexpr (APPEND) {
       if (fold_new) {
-        if (lane < 2 * kD * 2 / 16) s_newrow[lane] = new_unit;
+        if (lane < 2 * kD * 2 / 16) {
+          if constexpr (KV8) {
+            // the values the cache will hold: the unit's codes, widened
+            // back to bf16 as the tiles widen theirs (scales stay folded
+            // into scale_log2 and the output)
+            const float inv = lane < kD * 2 / 16 ? k_inv : v_inv;
+            new_unit = fp8x8_to_bf16(u32x2{fp8_pack4(new_unit[0], new_unit[1], inv),
+                                           fp8_pack4(new_unit[2], new_unit[3], inv)});
+          }
+          s_newrow[lane] = new_unit;
+        }
         // the same wave reads what it wrote
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
         __builtin_amdgcn_wave_barrier();
@@ -564,8 +585,9 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
         float dot = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          // K at d = 32 i + 8 grp + e, as in qop[i]: unit 4 i + grp
-          const u32x4 kr = s_newrow[4 * i + grp];
+          // K at d = 32 i + 8 grp + e (bf16 K) or 32 grp + 8 i + e (fp8
+          // K), as in qop[i]
+          const u32x4 kr = s_newrow[KV8 ? 4 * grp + i : 4 * i + grp];
           const u32x4 qr = as_u32x4(qop[i]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -694,7 +716,8 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
 constexpr int kCombineThreads = kWave;
 
 // This step's token of sequence s (decode with append), stored as
-// kv_append_token stores it: the K and V rows of every KV head into the
+// kv_append_token (fp8 caches: kv_append_token_fp8) stores it: the K and V
+// rows of every KV head into the
 // slot of position context_lens[s], the table entry when new_blocks[s] >= 0,
 // then the length + 1; nothing when the position lies outside the table or
 // names no valid block. One wave per sequence (an extra column of the
@@ -719,19 +742,39 @@ __device__ void append_token_of(const DecodeArgs& a, int s, int lane) {
     return (const u32x4*)(is_v ? a.v_new : a.k_new) + (int64_t)s * per_tensor +
            r;
   };
-  auto dst_of = [&](int i, int blk, int off) {
+  // 1 / scale of unit i's head (fp8 caches), as kv_append_token_fp8 takes
+  // it
+  auto inv_of = [&](int i) -> float {
+    const bool is_v = i >= per_tensor;
+    const int hh = (is_v ? i - per_tensor : i) / kUnits;
+    return is_v ? fp8_inv(a.v_scales, a.v_inv, hh)
+                : fp8_inv(a.k_scales, a.k_inv, hh);
+  };
+  // unit i (8 values) into its row: as is, or (fp8 caches) as 8 codes made
+  // with inv
+  auto put = [&](int i, int blk, int off, u32x4 x, float inv) {
     const bool is_v = i >= per_tensor;
     const int r = is_v ? i - per_tensor : i;
     const int hh = r / kUnits;
-    return (u32x4*)(is_v ? a.v_cache_w : a.k_cache_w) +
-           (((int64_t)blk * a.hkv + hh) * a.block_size + off) * kUnits +
-           (r - hh * kUnits);
+    const int64_t at =
+        (((int64_t)blk * a.hkv + hh) * a.block_size + off) * kUnits +
+        (r - hh * kUnits);
+    void* base = is_v ? a.v_cache_w : a.k_cache_w;
+    if (a.kv8)
+      ((u32x2*)base)[at] =
+          u32x2{fp8_pack4(x[0], x[1], inv), fp8_pack4(x[2], x[3], inv)};
+    else
+      ((u32x4*)base)[at] = x;
   };
   u32x4 x[kAhead];
+  float xinv[kAhead];
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) {
     const int i = lane + k * kWave;
-    if (i < 2 * per_tensor) x[k] = *src_of(i);
+    if (i < 2 * per_tensor) {
+      x[k] = *src_of(i);
+      xinv[k] = a.kv8 ? inv_of(i) : 0.f;
+    }
   }
   const int blk = nb >= 0 ? nb : old;
   if (!(ok_pos && blk >= 0 && blk < a.num_blocks)) return;
@@ -739,10 +782,10 @@ __device__ void append_token_of(const DecodeArgs& a, int s, int lane) {
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) {
     const int i = lane + k * kWave;
-    if (i < 2 * per_tensor) *dst_of(i, blk, off) = x[k];
+    if (i < 2 * per_tensor) put(i, blk, off, x[k], xinv[k]);
   }
   for (int i = lane + kAhead * kWave; i < 2 * per_tensor; i += kWave)
-    *dst_of(i, blk, off) = *src_of(i);
+    put(i, blk, off, *src_of(i), a.kv8 ? inv_of(i) : 0.f);
   if (lane == 0) {
     if (nb >= 0) *entry = nb;
     a.ctx_w[s] = stored + 1;
@@ -1031,6 +1074,7 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
   if (!a.out || !a.q || !a.k || !a.v || !a.ctx || (paged && !a.bt))
     return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
   a.group = a.hq / a.hkv;
+  a.kv8 = kv8;
 
   const bool fast = fast_path_ok(dtype, a.head_dim, a.block_size, paged);
   if (kv8 && !fast)
@@ -1085,7 +1129,10 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
         b.v = (const char*)a.v + (size_t)s0 * seq_bytes;
       }
       dim3 grid(a.hkv * a.head_blocks, a.n_chunks);
-      if (paged && kv8)
+      if (paged && kv8 && a.k_new)
+        decode_sk_kernel<true, true, true><<<grid, kWaves * kWave, 0, st>>>(
+            b);
+      else if (paged && kv8)
         decode_sk_kernel<true, true><<<grid, kWaves * kWave, 0, st>>>(b);
       else if (paged && a.k_new)
         decode_sk_kernel<true, false, true><<<grid, kWaves * kWave, 0, st>>>(
@@ -1399,6 +1446,114 @@ extern "C" kv_status paged_attn_decode_append(
   a.v_cache_w = v_cache;
   return run_decode(name, true, a, dtype, workspace, workspace_bytes,
                     (hipStream_t)stream);
+}
+
+namespace {
+// paged_attn_decode_append on fp8 E4M3 caches: per-tensor scales (k_scales
+// NULL) or one per KV head.
+kv_status decode_append_fp8(const char* name, void* out, const void* q,
+                            const void* k_new, const void* v_new,
+                            const int32_t* new_blocks, void* k_cache,
+                            void* v_cache, int32_t num_blocks,
+                            int32_t* block_tables, int32_t bt_stride,
+                            int32_t* context_lens, int32_t max_context,
+                            int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, float scale, float k_scale,
+                            float v_scale, const float* k_scales,
+                            const float* v_scales, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0)
+    return kvp_fail(KV_EINVAL, "%s: num_seqs must be >= 0", name);
+  if (num_seqs == 0) return KV_OK;
+  if (!k_scales && (!(k_scale > 0.f) || !(k_scale < INFINITY) ||
+                    !(v_scale > 0.f) || !(v_scale < INFINITY)))
+    return kvp_fail(KV_EINVAL, "%s: k_scale and v_scale must be finite and "
+                    "> 0", name);
+  if (!fast_path_ok(KV_BF16, head_dim, block_size, true))
+    return kvp_fail(KV_EUNSUPPORTED,
+                    "%s: fp8 K/V needs head_dim %d and block_size a multiple "
+                    "of 16 (got D=%d B=%d)", name, kD, head_dim, block_size);
+  if (!k_new || !v_new || !new_blocks || !k_cache || !v_cache)
+    return kvp_fail(KV_EINVAL, "%s: NULL pointer", name);
+  if (((uintptr_t)k_new | (uintptr_t)v_new) % 16 ||
+      ((uintptr_t)k_cache | (uintptr_t)v_cache) % 8)
+    return kvp_fail(KV_EINVAL, "%s: k_new/v_new must be 16-byte and the "
+                    "caches 8-byte aligned", name);
+  const int32_t* nb = (const int32_t*)kvp_device_view(new_blocks);
+  if (!nb)
+    return kvp_fail(KV_EINVAL, "%s: new_blocks is not device or pinned host "
+                    "memory", name);
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.ctx = context_lens;
+  a.max_ctx = max_context;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  // as the fp8 decode: per-tensor scales fold into the score scale and the
+  // output, per-head ones are applied in the kernel
+  a.scale_log2 = scale * (k_scales ? 1.f : k_scale) * kLog2e;
+  a.v_scale = k_scales ? 1.f : v_scale;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  // the token's codes, as kv_append_token_fp8 computes them
+  a.k_inv = k_scales ? 1.f : 1.f / k_scale;
+  a.v_inv = k_scales ? 1.f : 1.f / v_scale;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_blocks = nb;
+  a.bt_w = block_tables;
+  a.ctx_w = context_lens;
+  a.k_cache_w = k_cache;
+  a.v_cache_w = v_cache;
+  return run_decode(name, true, a, KV_BF16, workspace, workspace_bytes,
+                    (hipStream_t)stream, true);
+}
+}  // namespace
+
+extern "C" kv_status paged_attn_decode_append_fp8(
+    void* out, const void* q, const void* k_new, const void* v_new,
+    const int32_t* new_blocks, void* k_cache, void* v_cache,
+    int32_t num_blocks, int32_t* block_tables, int32_t bt_stride,
+    int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, float k_scale, float v_scale,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_append_fp8(
+      "paged_attn_decode_append_fp8", out, q, k_new, v_new, new_blocks,
+      k_cache, v_cache, num_blocks, block_tables, bt_stride, context_lens,
+      max_context, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+      scale, k_scale, v_scale, nullptr, nullptr, workspace, workspace_bytes,
+      stream);
+}
+
+extern "C" kv_status paged_attn_decode_append_fp8_per_head(
+    void* out, const void* q, const void* k_new, const void* v_new,
+    const int32_t* new_blocks, void* k_cache, void* v_cache,
+    int32_t num_blocks, int32_t* block_tables, int32_t bt_stride,
+    int32_t* context_lens, int32_t max_context, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, float scale, const float* k_scales,
+    const float* v_scales, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  const char* name = "paged_attn_decode_append_fp8_per_head";
+  if (num_seqs > 0 && (!k_scales || !v_scales))
+    return kvp_fail(KV_EINVAL, "%s: NULL scale array", name);
+  return decode_append_fp8(name, out, q, k_new, v_new, new_blocks, k_cache,
+                           v_cache, num_blocks, block_tables, bt_stride,
+                           context_lens, max_context, num_seqs, num_q_heads,
+                           num_kv_heads, head_dim, block_size, scale, 1.f, 1.f,
+                           k_scales, v_scales, workspace, workspace_bytes,
+                           stream);
 }
 
 extern "C" kv_status paged_attn_decode_fp8(

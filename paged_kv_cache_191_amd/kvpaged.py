@@ -96,6 +96,15 @@ SIGNATURES = {
     "paged_attn_decode_append": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32,
                                         _P, _I32, _P, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _F, _I32, _P, _SZ, _P]),
+    "paged_attn_decode_append_fp8": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32,
+                                            _P, _I32, _P, _I32, _I32, _I32,
+                                            _I32, _I32, _I32, _F, _F, _F, _P,
+                                            _SZ, _P]),
+    "paged_attn_decode_append_fp8_per_head": (_I32, [_P, _P, _P, _P, _P, _P,
+                                                     _P, _I32, _P, _I32, _P,
+                                                     _I32, _I32, _I32, _I32,
+                                                     _I32, _I32, _F, _P, _P,
+                                                     _P, _SZ, _P]),
     "paged_attn_decode_noalloc": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _P,
                                          _I32, _I32, _I32, _I32, _I32, _I32,
                                          _F, _I32, _P]),
@@ -769,12 +778,7 @@ def paged_attn_decode_append(out, q, k_new, v_new, new_blocks, k_cache,
     _attn_shapes(out, q, k_cache, v_cache, dk, S,
                  ((block_tables, "block_tables"),
                   (context_lens, "context_lens")))
-    _ndim(block_tables, 2, "block_tables")
-    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d):
-        raise ValueError("k_new and v_new must be [num_seqs, Hkv, D]")
-    if new_blocks.shape[0] != S or not new_blocks.is_contiguous() or \
-            new_blocks.dtype != torch.int32:
-        raise ValueError("new_blocks must be a contiguous int32 [num_seqs]")
+    _append_args(q, k_new, v_new, new_blocks, k_cache, block_tables)
     if workspace is None:
         workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
     st = _invoke("paged_attn_decode_append",
@@ -787,6 +791,80 @@ def paged_attn_decode_append(out, q, k_new, v_new, new_blocks, k_cache,
         int(max_context), S, hq, hkv, d, bs, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "paged_attn_decode_append")
+
+
+def _append_args(q, k_new, v_new, new_blocks, k_cache, block_tables):
+    """Shape checks shared by the decode-with-append wrappers."""
+    torch = _torch()
+    S, hq, d = q.shape
+    hkv = k_cache.shape[1]
+    _ndim(block_tables, 2, "block_tables")
+    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d):
+        raise ValueError("k_new and v_new must be [num_seqs, Hkv, D]")
+    if new_blocks.shape[0] != S or not new_blocks.is_contiguous() or \
+            new_blocks.dtype != torch.int32:
+        raise ValueError("new_blocks must be a contiguous int32 [num_seqs]")
+
+
+def paged_attn_decode_append_fp8(out, q, k_new, v_new, new_blocks, k_cache,
+                                 v_cache, block_tables, context_lens,
+                                 max_context: int, scale: float,
+                                 k_scale: float, v_scale: float,
+                                 workspace=None, stream=None) -> None:
+    """kv_append_token_fp8 then paged_attn_decode_fp8 over the advanced
+    lengths, as one op (k_new / v_new bf16, caches fp8 E4M3 codes).
+    context_lens is advanced in place."""
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, hkv, bs, dk = k_cache.shape
+    _attn_shapes(out, q, k_cache, v_cache, dk, S,
+                 ((block_tables, "block_tables"),
+                  (context_lens, "context_lens")))
+    _append_args(q, k_new, v_new, new_blocks, k_cache, block_tables)
+    if workspace is None:
+        workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
+    st = _invoke("paged_attn_decode_append_fp8",
+        _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+        _dev(k_new, "k_new", torch.bfloat16),
+        _dev(v_new, "v_new", torch.bfloat16), new_blocks.data_ptr(),
+        _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"), nb,
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context), S, hq, hkv, d, bs, float(scale), float(k_scale),
+        float(v_scale), _dev(workspace, "workspace"), workspace.numel(),
+        _stream(stream))
+    _check(st, "paged_attn_decode_append_fp8")
+
+
+def paged_attn_decode_append_fp8_per_head(out, q, k_new, v_new, new_blocks,
+                                          k_cache, v_cache, block_tables,
+                                          context_lens, max_context: int,
+                                          scale: float, k_scales, v_scales,
+                                          workspace=None,
+                                          stream=None) -> None:
+    """paged_attn_decode_append_fp8 with one scale per KV head (device
+    float32 [Hkv])."""
+    torch = _torch()
+    S, hq, d = q.shape
+    nb, hkv, bs, dk = k_cache.shape
+    _attn_shapes(out, q, k_cache, v_cache, dk, S,
+                 ((block_tables, "block_tables"),
+                  (context_lens, "context_lens")))
+    _append_args(q, k_new, v_new, new_blocks, k_cache, block_tables)
+    if workspace is None:
+        workspace = decode_workspace(S, hq, hkv, d, max_context, q.device)
+    st = _invoke("paged_attn_decode_append_fp8_per_head",
+        _dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+        _dev(k_new, "k_new", torch.bfloat16),
+        _dev(v_new, "v_new", torch.bfloat16), new_blocks.data_ptr(),
+        _fp8_cache(k_cache, "k_cache"), _fp8_cache(v_cache, "v_cache"), nb,
+        _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32),
+        int(max_context), S, hq, hkv, d, bs, float(scale),
+        _head_scales(k_scales, hkv, "k_scales"),
+        _head_scales(v_scales, hkv, "v_scales"),
+        _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "paged_attn_decode_append_fp8_per_head")
 
 
 def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables,

@@ -531,3 +531,183 @@ def test_fp8_per_head_errors():
         k.data_ptr(), k.data_ptr(), slots.data_ptr(), 2, kc.data_ptr(),
         kc.data_ptr(), 16, 16, 2, 128, None, good.data_ptr(), None)
     assert st == kv.KV_EINVAL
+
+
+# ------------------------------------------------- decode with the append --
+def _fill_fp8_upto(inp, nat, stored, k_scale, v_scale):
+    """fp8 paged caches holding the first stored[s] rows of each sequence
+    (the native tables were built up to those lengths)."""
+    w = inp.workload
+    B, S = w.block_size, w.num_seqs
+    kc = torch.full(tuple(nat.k_cache.shape), NAN_CODE, dtype=torch.uint8,
+                    device="cuda")
+    vc = torch.full_like(kc, NAN_CODE)
+    n = [int(x) for x in stored]
+    if sum(n):
+        seq_ids = np.concatenate([np.full(c, s, dtype=np.int32)
+                                  for s, c in enumerate(n)])
+        pos = np.concatenate([np.arange(c, dtype=np.int32) for c in n])
+        slots = kv.kv_slot_mapping(nat.tables, seq_ids, pos, B)
+        rows = np.concatenate([W.logical_rows(inp, s)[:c]
+                               for s, c in enumerate(n)])
+        r = torch.from_numpy(rows)
+        _write_fp8(inp.k[r].cuda(), inp.v[r].cuda(),
+                   torch.from_numpy(slots).cuda(), kc, vc, k_scale, v_scale)
+    torch.cuda.synchronize()
+    return kc, vc
+
+
+def _append_fp8_step(inp, stored, ks, vs, fused, max_context=None):
+    """One decode step that appends each sequence's next row (position
+    stored[s] of the draw) to fp8 caches holding stored[s] rows: fused
+    (paged_attn_decode_append_fp8[_per_head]) or as the two calls. Returns
+    (out, k codes, v codes, table, lengths)."""
+    w = inp.workload
+    B, S = w.block_size, w.num_seqs
+    ctx = np.asarray(stored, dtype=np.int32) + 1
+    cap = H.tables_capacity(int(ctx.max()), B)
+    nat = H.build_native(inp, B, cap, upto=stored)
+    kc, vc = _fill_fp8_upto(inp, nat, stored, ks, vs)
+    bt = torch.from_numpy(nat.tables).cuda()
+    lens = torch.from_numpy(nat.lens.copy()).cuda()
+    # the host allocator takes the blocks the new tokens start
+    idx = np.minimum(nat.lens // B, cap - 1)
+    before = nat.tables[np.arange(S), idx].copy()
+    _, pairs = nat.pool.seq_append(nat.tables, nat.lens)
+    assert len(pairs) == 0
+    after = nat.tables[np.arange(S), idx]
+    newb = torch.from_numpy(
+        np.where(after != before, after, -1).astype(np.int32)).pin_memory()
+    rows = torch.from_numpy(np.array(
+        [W.logical_rows(inp, s)[int(stored[s])] for s in range(S)]))
+    k_new = inp.k[rows].cuda().contiguous()
+    v_new = inp.v[rows].cuda().contiguous()
+    q = inp.q.cuda()
+    out = torch.full_like(q, float("nan"))
+    scale = H.scale_of(w)
+    mc = int(ctx.max()) if max_context is None else max_context
+    if _per_head(ks):
+        dks, dvs = _dev_scales(ks), _dev_scales(vs)
+        if fused:
+            kv.paged_attn_decode_append_fp8_per_head(
+                out, q, k_new, v_new, newb, kc, vc, bt, lens, mc, scale, dks,
+                dvs)
+        else:
+            kv.kv_append_token_fp8_per_head(k_new, v_new, newb, bt, lens, kc,
+                                            vc, dks, dvs)
+            kv.paged_attn_decode_fp8_per_head(out, q, kc, vc, bt, lens, mc,
+                                              scale, dks, dvs)
+    else:
+        if fused:
+            kv.paged_attn_decode_append_fp8(out, q, k_new, v_new, newb, kc,
+                                            vc, bt, lens, mc, scale, ks, vs)
+        else:
+            kv.kv_append_token_fp8(k_new, v_new, newb, bt, lens, kc, vc, ks,
+                                   vs)
+            kv.paged_attn_decode_fp8(out, q, kc, vc, bt, lens, mc, scale, ks,
+                                     vs)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), kc, vc, bt, lens
+
+
+def _within_rounding(got, ref):
+    """The fused op and the two calls differ by the output's rounding to
+    bf16 (2^-7 relative allowed) plus the new token's weight taken in fp32
+    rather than as a bf16 MFMA operand (4e-3 absolute allowed)."""
+    bound = 2.0 ** -7 * np.maximum(np.abs(got), np.abs(ref)) + 4e-3
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), (np.argwhere(bad)[:5], got[bad][:5], ref[bad][:5])
+
+
+def _fused_vs_two_calls(inp, stored, ks, vs, seqs=None):
+    w = inp.workload
+    ctx = np.asarray(stored, dtype=np.int32) + 1
+    of, kf, vf, btf, lf = _append_fp8_step(inp, stored, ks, vs, True)
+    ou, ku, vu, btu, lu = _append_fp8_step(inp, stored, ks, vs, False)
+    # the same codes, table and lengths, bit for bit
+    assert torch.equal(kf, ku) and torch.equal(vf, vu)
+    assert torch.equal(btf, btu) and torch.equal(lf, lu)
+    assert lf.cpu().numpy().tolist() == ctx.tolist()
+    _within_rounding(of, ou)
+    # and the oracle over the codes of every context row
+    orc = H.build_oracle(inp, w.block_size)
+    kp, vp = _oracle_codes(inp, orc, ks, vs, seqs=seqs)
+    want = O.decode_paged(inp.q.float().numpy(), _dequant_pool(kp, ks),
+                          _dequant_pool(vp, vs), orc.tables, ctx,
+                          H.scale_of(w), seqs=seqs)
+    sel = slice(None) if seqs is None else list(seqs)
+    err = H.max_abs(of[sel], want[sel])
+    _log(f"{w.name}: fused fp8 vs two calls max-abs "
+         f"{H.max_abs(of, ou):.2e}, vs oracle {err:.2e}")
+    assert err <= 2e-2, err
+
+
+@pytest.mark.parametrize("spec", ["tensor", "head"])
+def test_decode_append_fp8_small(spec):
+    """First token of a sequence, the last and first slots of a block, and
+    longer contexts: the fused fp8 op against the two calls and the
+    oracle, with one scale per tensor or per KV head."""
+    w = _small_workload(seed=17)
+    inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens, 4))
+    stored = W.context_lengths(inp).astype(np.int32) - 1
+    ks, vs = ((0.0123, 0.02) if spec == "tensor"
+              else _head_scales(5, w.num_kv_heads))
+    _fused_vs_two_calls(inp, stored, ks, vs)
+
+
+def test_decode_append_fp8_workload_shape():
+    """The Llama-3-8B batch (64 sequences, 32 / 8 heads, block 16) with
+    per-head scales; the oracle on sampled sequences."""
+    w = W.WORKLOADS["llama3_8b_decode"]
+    inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens, w.num_seqs))
+    stored = W.context_lengths(inp).astype(np.int32) - 1
+    ks, vs = _head_scales(6, w.num_kv_heads)
+    _fused_vs_two_calls(inp, stored, ks, vs, seqs=[0, 17, 40, 63])
+
+
+@pytest.mark.parametrize("hq,hkv", [(56, 8), (8, 8)])
+def test_decode_append_fp8_head_groups(hq, hkv):
+    """Head groups of 7 and of 1 per KV head."""
+    lengths = (1, 31, 32, 33, 400, 64)
+    w = _small_workload(seed=18).replace(
+        num_seqs=len(lengths), lengths=lengths, num_q_heads=hq,
+        num_kv_heads=hkv, name=f"fp8_append_g{hq // hkv}")
+    inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens, 8))
+    stored = np.array(lengths, dtype=np.int32) - 1
+    _fused_vs_two_calls(inp, stored, *_head_scales(7, hkv))
+
+
+def test_decode_append_fp8_errors():
+    """Shapes the fp8 decode does not cover fail before anything is
+    written; a missing scale array is refused."""
+    S, hkv, D = 2, 2, 128
+    q = torch.zeros((S, 4, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    k_new = torch.zeros((S, hkv, D), dtype=torch.bfloat16, device="cuda")
+    newb = torch.tensor([0, 1], dtype=torch.int32).pin_memory()
+    bt = torch.zeros((S, 2), dtype=torch.int32, device="cuda")
+    lens = torch.zeros(S, dtype=torch.int32, device="cuda")
+    kc8 = torch.full((4, hkv, 8, D), NAN_CODE, dtype=torch.uint8,
+                     device="cuda")
+    with pytest.raises(kv.KVError):      # block_size 8
+        kv.paged_attn_decode_append_fp8(out, q, k_new, k_new, newb, kc8,
+                                        kc8.clone(), bt, lens, 16, 0.1, 1.0,
+                                        1.0)
+    torch.cuda.synchronize()
+    assert (kc8 == NAN_CODE).all() and (lens == 0).all()
+    kc = torch.full((4, hkv, 16, D), NAN_CODE, dtype=torch.uint8,
+                    device="cuda")
+    with pytest.raises(kv.KVError):      # scale must be > 0
+        kv.paged_attn_decode_append_fp8(out, q, k_new, k_new, newb, kc,
+                                        kc.clone(), bt, lens, 32, 0.1, 0.0,
+                                        1.0)
+    good = torch.ones(hkv, dtype=torch.float32, device="cuda")
+    ws = kv.decode_workspace(S, 4, hkv, D, 32, q.device)
+    st = kv.lib().paged_attn_decode_append_fp8_per_head(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), k_new.data_ptr(),
+        newb.data_ptr(), kc.data_ptr(), kc.data_ptr(), 4, bt.data_ptr(), 2,
+        lens.data_ptr(), 32, S, 4, hkv, D, 16, 0.1, None, good.data_ptr(),
+        ws.data_ptr(), ws.numel(), None)
+    assert st == kv.KV_EINVAL
+    torch.cuda.synchronize()
+    assert (kc == NAN_CODE).all() and (lens == 0).all()
