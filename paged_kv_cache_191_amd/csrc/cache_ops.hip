@@ -10,6 +10,7 @@
 // Caches are head-major inside a block: [blocks, Hkv, block_size, D].
 
 #include "device_common.h"
+#include "fp8_codec.h"
 
 namespace {
 

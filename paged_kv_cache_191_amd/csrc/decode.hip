@@ -64,6 +64,7 @@
 #include <stdlib.h>
 
 #include "device_common.h"
+#include "fp8_codec.h"
 
 namespace {
 
@@ -1174,8 +1175,11 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
   return KV_OK;
 }
 
-// Shared-prefix pieces: enough MFMA workgroups for two per CU, at least 256
-// keys per piece, pieces a multiple of 64 keys.
+// Shared-prefix pieces: enough MFMA workgroups for one per CU (a prefill
+// workgroup of 8 waves fills a CU), at least 256 keys per piece, pieces a
+// multiple of 64 keys. More pieces make shorter workgroups, whose pipeline
+// fill then dominates (2, 4 and 16 pieces measured slower than 8 for 256
+// members of 32 / 8 heads).
 int env_psplit_override() {
   static int cached = -2;
   if (cached == -2) {
@@ -1188,11 +1192,11 @@ int env_psplit_override() {
 void choose_psplit(int num_seqs, int hq, int hkv, int max_shared,
                    int* nsplit, int* ksplit) {
   const int ms = max_shared < 16 ? 16 : max_shared;
-  const int rowblocks = (num_seqs + 31) / 32;
+  const int rowblocks = (num_seqs + 63) / 64;  // 64 query rows each
   // prefix-pass workgroups per piece: row blocks x head blocks of 4 within
   // each KV head's group
   const int per_split = rowblocks * hkv * ((hq / hkv + 3) / 4);
-  int n = (2 * device_cus() + per_split - 1) / per_split;
+  int n = (device_cus() + per_split - 1) / per_split;
   if (env_psplit_override() > 0) n = env_psplit_override();
   const int max_n = (ms + 255) / 256;
   n = n < 1 ? 1 : (n > max_n ? max_n : n);
