@@ -106,6 +106,8 @@ struct DecodeArgs {
   float* ws_o;          // [n_chunks, 2, Hq, D] unnormalised partial outputs
   float* ws_ml;         // [n_chunks, 2, Hq, 2] (reference max, sum)
   int32_t* ws_cs;       // [S + 1] tile offsets of the sequences
+  int32_t* ws_nb;       // [S] with append: new_blocks copied to the device
+  float* ws_inv;        // [2 Hkv] fp8 with append: 1 / scale, K then V heads
   // shared prefix (all NULL / 0 for plain decode)
   const int32_t* plen;  // [S] leading tokens covered by the prefix partials
   const float* pre_o;   // [n_psplit, pre_stride, Hq, D]
@@ -286,6 +288,18 @@ __global__ __launch_bounds__(kWaves * kWave, 3) void decode_sk_kernel(
   if (blockIdx.x == 0 && chunk == 0) {
     for (int i = tid; i <= S; i += kWaves * kWave) a.ws_cs[i] = s_cs[i];
     if (tid == 0) record_clamped(a, s_clamped);
+    // With append, the merge kernel stores the token: the block ids (pinned
+    // host memory, possibly) and the fp8 reciprocals go to the workspace
+    // now, long before it runs, so that it reads them from device memory.
+    if constexpr (APPEND) {
+      for (int i = tid; i < S; i += kWaves * kWave)
+        a.ws_nb[i] = a.new_blocks[i];
+      if constexpr (KV8) {
+        for (int i = tid; i < 2 * a.hkv; i += kWaves * kWave)
+          a.ws_inv[i] = i < a.hkv ? fp8_inv(a.k_scales, a.k_inv, i)
+                                  : fp8_inv(a.v_scales, a.v_inv, i - a.hkv);
+      }
+    }
   }
   const int C = chunk_tiles(total, a.n_chunks);
   const int c0 = chunk * C;
@@ -733,9 +747,9 @@ __device__ void append_token_of(const DecodeArgs& a, int s, int lane) {
   const bool ok_pos = stored >= 0 && stored < cap;
   const int idx = ok_pos ? stored / a.block_size : 0;
   int32_t* entry = a.bt_w + (int64_t)s * a.bt_stride + idx;
-  // the block id (host memory, possibly) and the current entry, and the
-  // first rows, all in flight together
-  const int nb = a.new_blocks[s];
+  // the block id (copied to the workspace by the stream-K kernel) and the
+  // current entry, and the first rows, all in flight together
+  const int nb = a.ws_nb[s];
   const int old = ok_pos ? *entry : -1;
   auto src_of = [&](int i) {
     const bool is_v = i >= per_tensor;
@@ -744,12 +758,11 @@ __device__ void append_token_of(const DecodeArgs& a, int s, int lane) {
            r;
   };
   // 1 / scale of unit i's head (fp8 caches), as kv_append_token_fp8 takes
-  // it
+  // it (computed by the stream-K kernel)
   auto inv_of = [&](int i) -> float {
     const bool is_v = i >= per_tensor;
     const int hh = (is_v ? i - per_tensor : i) / kUnits;
-    return is_v ? fp8_inv(a.v_scales, a.v_inv, hh)
-                : fp8_inv(a.k_scales, a.k_inv, hh);
+    return a.ws_inv[(is_v ? a.hkv : 0) + hh];
   };
   // unit i (8 values) into its row: as is, or (fp8 caches) as 8 codes made
   // with inv
@@ -1034,14 +1047,18 @@ int choose_chunks(int num_kv_heads, int head_blocks) {
 }
 
 // Workspace: a 256-byte header (int32 [0] = sequences whose context was
-// clamped in the last call), then the stream-K partials and tile offsets.
+// clamped in the last call), then the stream-K partials and tile offsets,
+// and for a decode with append the step's block ids and fp8 reciprocals.
 constexpr size_t kWsHeader = 256;
 
-size_t sk_workspace_bytes(int num_seqs, int hq, int n_chunks) {
+// [header][o][ml][cs: S + 1][nb: S][inv: 2 Hkv]
+size_t sk_workspace_bytes(int num_seqs, int hq, int hkv, int n_chunks) {
   const size_t o = (size_t)n_chunks * 2 * hq * kD * sizeof(float);
   const size_t ml = (size_t)n_chunks * 2 * hq * 2 * sizeof(float);
   const size_t cs = (size_t)(num_seqs + 1) * sizeof(int32_t);
-  return kWsHeader + o + ml + cs;
+  const size_t nb = (size_t)num_seqs * sizeof(int32_t);
+  const size_t inv = (size_t)2 * hkv * sizeof(float);
+  return kWsHeader + o + ml + cs + nb + inv;
 }
 
 bool fast_path_ok(kv_dtype dtype, int head_dim, int block_size, bool paged) {
@@ -1090,7 +1107,8 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
     if ((int64_t)per_launch * a.max_ctx > INT32_MAX)
       return kvp_fail(KV_EUNSUPPORTED, "%s: more than 2^31 context tokens in "
                       "one launch", name);
-    const size_t need = sk_workspace_bytes(per_launch, a.hq, a.n_chunks);
+    const size_t need =
+        sk_workspace_bytes(per_launch, a.hq, a.hkv, a.n_chunks);
     if (!workspace || ws_bytes < need)
       return kvp_fail(KV_EINVAL, "%s: workspace of %zu bytes needed, %zu given",
                       name, need, ws_bytes);
@@ -1098,6 +1116,8 @@ kv_status run_decode(const char* name, bool paged, DecodeArgs a,
     a.ws_o = (float*)((char*)workspace + kWsHeader);
     a.ws_ml = a.ws_o + (size_t)a.n_chunks * 2 * a.hq * kD;
     a.ws_cs = (int32_t*)(a.ws_ml + (size_t)a.n_chunks * 2 * a.hq * 2);
+    a.ws_nb = a.ws_cs + per_launch + 1;
+    a.ws_inv = (float*)(a.ws_nb + per_launch);
     // Batches of more than kMaxSeqs sequences run as several launches on
     // the same stream, in order, sharing the workspace.
     for (int s0 = 0; s0 < a.num_seqs; s0 += kMaxSeqs) {
@@ -1362,7 +1382,7 @@ extern "C" size_t kv_decode_workspace_bytes(int32_t num_seqs,
   const int hb = (num_q_heads / num_kv_heads + kHeadBlk - 1) / kHeadBlk;
   const int n = choose_chunks(num_kv_heads, hb);
   const int per_launch = num_seqs < kMaxSeqs ? num_seqs : kMaxSeqs;
-  return sk_workspace_bytes(per_launch, num_q_heads, n);
+  return sk_workspace_bytes(per_launch, num_q_heads, num_kv_heads, n);
 }
 
 extern "C" kv_status paged_attn_decode(

@@ -213,11 +213,13 @@ def test_pool_create_rejects_bad_order():
 
 def test_decode_workspace_sizes():
     # a 256-byte header (the clamp count), then partials [chunks, 2, Hq,
-    # D + 2] fp32 and S + 1 token offsets
+    # D + 2] fp32, S + 1 token offsets, and for a decode with append S block
+    # ids and 2 Hkv fp8 reciprocals
     c = kv.kv_decode_chunks(56, 8)
     assert c >= 1
     n = kv.kv_decode_workspace_bytes(4, 56, 8, 128, 196608)
-    assert n == 256 + c * 2 * 56 * (128 + 2) * 4 + (4 + 1) * 4
+    assert n == 256 + c * 2 * 56 * (128 + 2) * 4 + (4 + 1) * 4 + 4 * 4 + \
+        2 * 8 * 4
     # generic path (head_dim 64): the header only
     assert kv.kv_decode_workspace_bytes(4, 56, 8, 64, 100) == 256
     assert kv.kv_decode_chunks(32, 5) < 0
