@@ -148,6 +148,21 @@ SIGNATURES = {
 _lib = None
 
 
+def load_native(path: str) -> ctypes.CDLL:
+    """dlopen a library of this package, with one HIP runtime per process.
+
+    torch carries its own libamdhip64 under the same soname as ROCm's. When
+    torch is imported first, a library loaded afterwards binds to torch's
+    runtime; loaded first, it brings in ROCm's, torch then loads its own
+    beside it, and launches through the first find no device. So torch (when
+    installed) is imported before the library."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    return ctypes.CDLL(path)
+
+
 def lib() -> ctypes.CDLL:
     """Load libkvpaged.so (raises if it has not been built)."""
     global _lib
@@ -156,7 +171,7 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is not built; run `python -c 'import "
                 f"__graft_entry__ as g; g.build()'` first")
-        handle = ctypes.CDLL(LIB_PATH)
+        handle = load_native(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)
             fn.restype = res

@@ -45,3 +45,27 @@ def test_binding_matches_header_arity():
         set(decls) ^ set(kv.SIGNATURES))
     for name, n in decls.items():
         assert len(kv.SIGNATURES[name][1]) == n, name
+
+
+def test_one_hip_runtime_per_process():
+    # loading the libraries before torch must not leave two HIP runtimes in
+    # the process (torch's and ROCm's share a soname); a fresh interpreter,
+    # so that no earlier test has imported torch already
+    import subprocess
+    import sys
+    from paged_kv_cache_191_amd import build
+    ensure_built()
+    if not os.path.exists(build.PROBE_LIB):
+        build.build()
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from paged_kv_cache_191_amd import kvpaged as kv, build\n"
+        "kv.lib(); kv.load_native(build.PROBE_LIB)\n"
+        "import torch\n"
+        "print(len({l.split()[-1] for l in open('/proc/self/maps') "
+        "if 'libamdhip64' in l}))\n" % os.path.dirname(os.path.dirname(
+            os.path.abspath(__file__))))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1", r.stdout
