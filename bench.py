@@ -62,6 +62,11 @@ served from cache. The same JSON line carries:
                   layout's figures beside it;
   paged_vs_contig_overhead - (t_paged - t_contig) / t_contig per
                   configuration (per block size for the prefill);
+  plain_read_GBps / frac_of_plain_read (in each decode record) - the rate
+                  of a plain streaming read of the same byte count on the
+                  same GPU in the same run (libkvprobe.so, the best of 1-4
+                  workgroups per CU), and the record's rate against it: the
+                  practical read ceiling, next to the published peak;
   cpu_oracle    - the fp64 oracle, single-threaded, per configuration;
   cpu_baseline  - the headline workload's entry of cpu_oracle;
   configs       - every figure of every configuration.
@@ -173,6 +178,28 @@ def decode_bytes(ctx: np.ndarray, hq: int, hkv: int, d: int, B: int,
     qo = 2 * len(ctx) * hq * d * esize
     table = int(sum(-(-int(n) // B) for n in ctx)) * 4 if paged else 0
     return kvb + qo + table + 4 * len(ctx)
+
+
+# device bytes released outside torch's allocator (demand-mapped pages)
+# since the last settle()
+_native_freed = 0
+
+
+def settle(device) -> None:
+    """Gives torch's cached device memory back to the driver, then waits
+    while the driver works through what was released since the last call.
+    Reads have measured about 5% slower for a while after large releases
+    (13 GB: about 0.2 s; 40 GB: about 1 s), so every timed function calls
+    this first: no timed region starts inside that window."""
+    global _native_freed
+    import torch
+    torch.cuda.synchronize(device)
+    peak = torch.cuda.max_memory_reserved(device)
+    torch.cuda.empty_cache()
+    freed = max(0, peak - torch.cuda.memory_reserved(device)) + _native_freed
+    _native_freed = 0
+    torch.cuda.reset_peak_memory_stats(device)
+    time.sleep(0.05 + 0.05 * freed / 1e9)
 
 
 def pool_blocks(kv, w, lengths, headroom: int = 0) -> int:
@@ -438,7 +465,9 @@ class DecodeReplica:
                 self.step_map_pages.append(n)
 
     def close(self) -> None:
+        global _native_freed
         if self.vmm:
+            _native_freed += self.vc.mapped_bytes
             self.vc.close()
 
     def cache_write(self, done=None) -> None:
@@ -488,6 +517,7 @@ def fp8_head_scales(k_dev, v_dev):
 def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
                device, shared_op: bool = False, vmm_page_tokens: int = 0,
                fp8: bool = False, fused: bool = False):
+    settle(device)
     import torch
     w = inp.workload
     new_k, new_v = new_token_kv(w, device)
@@ -629,6 +659,7 @@ def run_tiny_decode(device, launches: int = 50):
     path, latency-bound, so its time is reported without a roofline. Each
     launch is timed with events behind a GPU spin (kernel time, not launch
     latency)."""
+    settle(device)
     import torch
     from paged_kv_cache_191_amd import kvpaged as kv
     from paged_kv_cache_191_amd import workloads as W
@@ -673,6 +704,7 @@ def run_swap(w, device, n_blocks: int = 2048, reps: int = 5):
     """Swap of n_blocks blocks of the workload's pool shape (K and V) out to a
     pinned host pool and back in (kv_swap_blocks), timed with events: the
     PCIe cost of preempting sequences when the device pool is full."""
+    settle(device)
     import torch
     from paged_kv_cache_191_amd import kvpaged as kv
     shape = (n_blocks, w.num_kv_heads, w.block_size, w.head_dim)
@@ -716,6 +748,7 @@ def run_cow(w, steps: int, warmup: int, device):
     copy that block (kv_copy_blocks), the last finds it unshared and writes
     in place; the decode then shares the prefix's whole blocks. Every repetition starts from a fresh allocator with the same
     free order, so the prefix rows (written once) stay valid."""
+    settle(device)
     import torch
     from paged_kv_cache_191_amd import kvpaged as kv
     from paged_kv_cache_191_amd import workloads as W
@@ -797,6 +830,7 @@ def run_cow(w, steps: int, warmup: int, device):
 
 
 def prefill_pass(inp, layout: str, device):
+    settle(device)
     import torch
     from paged_kv_cache_191_amd import kvpaged as kv
     w = inp.workload
@@ -908,6 +942,8 @@ def prefill_pass(inp, layout: str, device):
         res["vmm_map_host_ms_per_pass"] = 1e3 * map_s[0]
         res["vmm_map_us_per_page"] = 1e6 * map_s[0] / max(1, map_pages[0])
         torch.cuda.synchronize()
+        global _native_freed
+        _native_freed += vcache.mapped_bytes
         vcache.close()
     del kc, vc, q_dev, k_dev, v_dev, out
     torch.cuda.empty_cache()
@@ -1102,6 +1138,91 @@ def decode_roofline(res: dict, kernel: str, traffic=None) -> dict:
         ms_per_launch=round(res["decode_op_ms_mean"], 4))
 
 
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_191_amd", "libkvprobe.so")
+_probe = None
+
+
+def probe_lib():
+    """libkvprobe.so: the plain streaming-read kernel (measurement only)."""
+    global _probe
+    if _probe is None:
+        import ctypes
+        from paged_kv_cache_191_amd import kvpaged as kv
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is not built: run "
+                               "__graft_entry__.build()")
+        lib = kv.load_native(PROBE_LIB)
+        lib.kvprobe_threads.restype = ctypes.c_int
+        lib.kvprobe_threads.argtypes = []
+        lib.kvprobe_stream_read.restype = ctypes.c_int
+        lib.kvprobe_stream_read.argtypes = [
+            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+            ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+        _probe = lib
+    return _probe
+
+
+def plain_read(nbytes: int, device, reps: int = 20,
+               per_cu=(1, 2, 3, 4)) -> dict:
+    """The read rate a plain streaming kernel reaches for ``nbytes`` bytes on
+    this GPU: libkvprobe's kernel (each workgroup one contiguous range, 16-B
+    non-temporal loads, 8 in flight per lane), best median over 1-4
+    workgroups per CU. Two buffers alternate, as the decode's replicas do,
+    so that no read finds its bytes in the last-level cache; they are
+    written before they are timed, as the caches are."""
+    settle(device)
+    import torch
+    lib = probe_lib()
+    nb = int(nbytes) // 16 * 16
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    sink = torch.empty(max(per_cu) * cus * lib.kvprobe_threads(),
+                       dtype=torch.int32, device=device)
+    bufs = [torch.ones(nb, dtype=torch.uint8, device=device)
+            for _ in range(2)]
+    stream = torch.cuda.current_stream(device)
+    warm = 3
+    best = None
+    for k in per_cu:
+        evs = []
+        for r in range(warm + reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.kvprobe_stream_read(
+                bufs[r % 2].data_ptr(), nb, sink.data_ptr(),
+                sink.numel() * 4, k * cus, stream.cuda_stream)
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"kvprobe_stream_read returned {rc}")
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        med = float(np.median([a.elapsed_time(b) for a, b in evs[warm:]]))
+        if best is None or med < best[0]:
+            best = (med, k)
+    del bufs, sink
+    return {"bytes": nb, "us": round(best[0] * 1e3, 3),
+            "GBps": round(nb / (best[0] * 1e-3) / 1e9, 1),
+            "workgroups_per_cu": best[1]}
+
+
+def add_read_ceilings(rl: dict, device) -> dict:
+    """Times a plain read of each decode record's algorithmic bytes and adds
+    it to the record: ``plain_read_GBps`` and the record's rate as a
+    fraction of it (``frac_of_plain_read``)."""
+    seen = {}
+    for rec in rl.values():
+        nb = rec.get("bytes_per_launch")
+        if rec.get("bound") != "hbm" or not nb:
+            continue
+        key = round(nb / 2**20)  # layouts whose bytes differ by < 1 MiB
+        if key not in seen:
+            seen[key] = plain_read(nb, device)
+        pr = seen[key]
+        rec["plain_read_GBps"] = pr["GBps"]
+        rec["frac_of_plain_read"] = round(rec["achieved"] / pr["GBps"], 4)
+    return {str(v["bytes"]): v for v in seen.values()}
+
+
 def overhead(t_paged: float, t_contig: float) -> float:
     return round(t_paged / t_contig - 1.0, 4)
 
@@ -1134,10 +1255,9 @@ def bench_decode_config(name: str, args, device) -> dict:
     runs = {}
     prefix = wd.kind == "prefix"
     if not prefix:
-        # The headline form runs first, before any other layout has
-        # allocated and freed its caches: right after the contiguous leg
-        # (4.4 GB allocated and freed), the next leg's op has measured up to
-        # 4% slower on some boxes, and one leg later it recovers.
+        # The headline form runs first. Every leg starts with settle(): a
+        # leg timed right after another one had released its caches (the
+        # contiguous leg's 4.4 GB) measured up to 4% slower.
         log(f"{name}: paged decode steps, append fused into the decode op")
         runs["paged_fused"] = run_decode(inp, True, args.steps, args.warmup,
                                          args.replicas, device, fused=True)
@@ -1232,8 +1352,13 @@ def bench_decode_config(name: str, args, device) -> dict:
     if vm and "error" not in vm:
         ovh[name + "_vs_demand_mapped"] = overhead(
             paged["decode_op_ms_mean"], vm["decode_op_ms_mean"])
+    ceilings = None
+    if not args.no_read_ceiling:
+        log(f"{name}: plain reads of the same byte counts")
+        ceilings = add_read_ceilings(rl, device)
     out = {"inp": inp, "runs": runs, "rooflines": rl, "overhead": ovh,
-           "cow": cow, "memory": memory_waste(inp, LMAX_RESERVED[name])}
+           "cow": cow, "memory": memory_waste(inp, LMAX_RESERVED[name]),
+           "read_ceiling": ceilings}
     if "paged_fp8" in runs:
         out["fp8_speedup_vs_bf16"] = round(
             paged["decode_op_ms_mean"] /
@@ -1337,6 +1462,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=4.0,
                     help="seconds of oracle time per configuration")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the plain streaming reads of each decode "
+                         "record's byte count")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (reference "
                          "kernel for hardware traffic counters)")
@@ -1419,6 +1547,8 @@ def main() -> int:
                 d["copy_on_write"] = nested_round(r["cow"])
             if "fp8_speedup_vs_bf16" in r:
                 d["fp8_speedup_vs_bf16"] = r["fp8_speedup_vs_bf16"]
+            if r["read_ceiling"]:
+                d["plain_read"] = r["read_ceiling"]
             details[name] = d
             if cpu:
                 w = r["inp"].workload

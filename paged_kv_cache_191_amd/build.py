@@ -1,7 +1,8 @@
-"""Compile the HIP kernels and host code into libkvpaged.so (gfx950).
+"""Compile the HIP kernels and host code into libkvpaged.so (gfx950), and
+the plain-read measurement kernel into libkvprobe.so.
 
 Every call recompiles. Objects go to ``_build/`` next to this file; the
-library is written next to this file so it travels with the source tree.
+libraries are written next to this file so they travel with the source tree.
 """
 import os
 import shutil
@@ -15,6 +16,9 @@ INCLUDE = os.path.join(ROOT, "include")
 SOURCES = ["host.cpp", "prefix_cache.cpp", "vcache.cpp", "cache_ops.hip",
            "decode.hip", "decode_noalloc.hip", "prefill.hip"]
 LIB = os.path.join(HERE, "libkvpaged.so")
+# measurement only (the benchmark's read ceiling), not the attention API
+PROBE_SOURCES = ["read_probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libkvprobe.so")
 ARCH = os.environ.get("KVPAGED_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,21 +45,27 @@ def _compile(src: str, obj: str, extra=()) -> None:
         sys.stderr.write("\n".join(noise) + "\n")
 
 
-def build(verbose: bool = False) -> str:
-    bdir = os.path.join(HERE, "_build")
-    os.makedirs(bdir, exist_ok=True)
-    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o")
-            for s in SOURCES]
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        list(ex.map(lambda p: _compile(*p), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in srcs]
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        list(ex.map(lambda p: _compile(*p), zip(srcs, objs)))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {PROBE_LIB}")
     return LIB
 
 
