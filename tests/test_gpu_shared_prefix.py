@@ -232,9 +232,9 @@ def _prefix_case(prefix, upto=None):
     return w, inp, nat
 
 
-def test_full_prefix_share_sampled():
+def test_full_prefix_share():
     """256 sequences sharing a 4096-token prefix (one group), own suffixes
-    U{64..1024}: sampled sequences against the oracle."""
+    U{64..1024}: every output against the oracle."""
     w, inp, nat = _prefix_case(4096)
     S = w.num_seqs
     q = inp.q.to(DEV)
@@ -248,10 +248,9 @@ def test_full_prefix_share_sampled():
     got = out.float().cpu().numpy()
     assert not np.isnan(got).any()
     orc = build_oracle(inp, w.block_size)
-    seqs = [0, 1, 127, 254, 255]
     want = O.decode_paged(inp.q.float().numpy(), orc.k_pool, orc.v_pool,
-                          orc.tables, orc.lens, scale_of(w), seqs=seqs)
-    err = max_abs(got[seqs], want[seqs])
+                          orc.tables, orc.lens, scale_of(w))
+    err = max_abs(got, want)
     print(f"prefix 4096 x 256: max-abs {err:.2e}", flush=True)
     assert err <= tolerance(w)
 
@@ -281,12 +280,17 @@ def test_after_copy_on_write_step():
         scale_of(w))
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
-    seqs = [0, 100, 254, 255]
-    ks = [torch.cat([inp.k[:4104], nk[s:s + 1]]).float().numpy()
-          for s in seqs]
-    vs = [torch.cat([inp.v[:4104], nv[s:s + 1]]).float().numpy()
-          for s in seqs]
-    want = O.decode_logical(inp.q.float().numpy()[seqs], ks, vs, scale_of(w))
-    err = max_abs(got[seqs], want)
+    # every sequence: the 4104 prefix rows, then its own new token (in
+    # chunks of 32 sequences to bound the host memory of the references)
+    qh = inp.q.float().numpy()
+    err = 0.0
+    for c0 in range(0, S, 32):
+        seqs = list(range(c0, min(S, c0 + 32)))
+        ks = [torch.cat([inp.k[:4104], nk[s:s + 1]]).float().numpy()
+              for s in seqs]
+        vs = [torch.cat([inp.v[:4104], nv[s:s + 1]]).float().numpy()
+              for s in seqs]
+        want = O.decode_logical(qh[seqs], ks, vs, scale_of(w))
+        err = max(err, max_abs(got[seqs], want))
     print(f"after CoW: max-abs {err:.2e}", flush=True)
     assert err <= tolerance(w)
