@@ -1,7 +1,7 @@
 """Host-side checks that need no GPU: argument validation of the device
 append and demand-mapped cache entry points (they return before any HIP
-call), and bench.py's algorithmic byte count, traffic records and one-GPU
-guard."""
+call), and bench.py's algorithmic byte count, traffic records, read-ceiling
+records and one-GPU guard."""
 import os
 import subprocess
 import sys
@@ -115,6 +115,43 @@ def test_traffic_records_parse():
         t = bench.recorded_traffic(w)
         assert t is None or t == vals[f"traffic_bytes_per_{unit}"]
     assert bench.recorded_traffic("no_such_workload") is None
+
+
+def test_read_ceilings_attach_to_decode_records(monkeypatch):
+    # Each HBM record with a byte count gets the plain-read rate of its byte
+    # count (layouts whose bytes differ by less than 1 MiB share one
+    # measurement); MFMA records and records without a byte count are left
+    # alone.
+    sys.path.insert(0, ROOT)
+    import bench
+    calls = []
+
+    def fake_plain_read(nbytes, device):
+        calls.append(nbytes)
+        nb = int(nbytes) // 16 * 16
+        return {"bytes": nb, "us": 100.0, "GBps": 6400.0 if nb > 5e8 else
+                6000.0, "workgroups_per_cu": 2}
+
+    monkeypatch.setattr(bench, "plain_read", fake_plain_read)
+    rl = {
+        "paged": bench.roofline_record("hbm", 5880.0, 8000.0, "GB/s",
+                                       bytes_per_launch=640109829),
+        "contig": bench.roofline_record("hbm", 5900.0, 8000.0, "GB/s",
+                                        bytes_per_launch=640070707),
+        "fp8": bench.roofline_record("hbm", 4800.0, 8000.0, "GB/s",
+                                     bytes_per_launch=320598892),
+        "copy": bench.roofline_record("hbm", 3800.0, 8000.0, "GB/s"),
+        "prefill": bench.roofline_record("mfma", 1200.0, 2500.0, "TFLOP/s"),
+    }
+    out = bench.add_read_ceilings(rl, None)
+    assert calls == [640109829, 320598892]
+    assert sorted(int(k) for k in out) == [320598880, 640109824]
+    assert rl["paged"]["plain_read_GBps"] == 6400.0
+    assert rl["contig"]["plain_read_GBps"] == 6400.0
+    assert rl["paged"]["frac_of_plain_read"] == round(5880.0 / 6400.0, 4)
+    assert rl["fp8"]["frac_of_plain_read"] == round(4800.0 / 6000.0, 4)
+    assert "plain_read_GBps" not in rl["copy"]
+    assert "plain_read_GBps" not in rl["prefill"]
 
 
 def test_bench_refuses_more_than_one_gpu():
