@@ -1460,6 +1460,9 @@ def main() -> int:
                     help="skip the paged decode over fp8 E4M3 caches")
     ap.add_argument("--no-cow", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-headline", type=float, default=10.0,
+                    help="seconds of oracle time for the headline workload "
+                         "(the cpu_baseline record)")
     ap.add_argument("--cpu-budget", type=float, default=4.0,
                     help="seconds of oracle time per configuration")
     ap.add_argument("--no-read-ceiling", action="store_true",
@@ -1559,8 +1562,9 @@ def main() -> int:
                     seqs = list(range(0, w.num_seqs, 37))
                 else:
                     seqs = list(range(w.num_seqs))
-                cpu_oracle[name] = oracle_decode_rate(r["inp"], seqs,
-                                                      args.cpu_budget)
+                budget = (args.cpu_budget_headline
+                          if name == "llama3_8b_decode" else args.cpu_budget)
+                cpu_oracle[name] = oracle_decode_rate(r["inp"], seqs, budget)
             r["inp"] = None
     log(f"all configurations done in {time.perf_counter() - t_start:.1f} s")
 
