@@ -52,7 +52,7 @@ bytes); the bytes the sequences read logically are reported beside it as
 "effective" GB/s, which can exceed the HBM peak because the shared blocks are
 served from cache. The same JSON line carries:
   roofline      - the headline decode op (HIP events around each call on its
-                  stream) against 8 TB/s, with the HBM traffic counted by
+                  stream, without the system-scope fence) against 8 TB/s, with the HBM traffic counted by
                   hardware counters when they were taken on these sources;
   rooflines     - the same record for every other measured kernel: decode
                   ops of each workload and layout, the prefill passes
@@ -103,6 +103,70 @@ def decode_steps_total(steps: int, warmup: int) -> int:
     return warmup + 2 * steps + APPEND_TIMING_STEPS
 # GPU spin before each of them (about 40 us at 2.4 GHz)
 SPIN_CYCLES = 100_000
+
+
+class HipEvent:
+    """A HIP event created with hipEventDisableSystemFence, recorded on
+    torch's current stream. A torch event's record carries a system-scope
+    fence: the caches are written back and invalidated at every record, and
+    the next kernel pays for it (1-2 us per decode step). The bench's events
+    only mark completion (a replica's pinned block-id buffer may be reused
+    once the step that reads it has run) and take timestamps, which needs no
+    fence. Calls the HIP runtime torch loaded (same soname)."""
+    _lib = None
+
+    @classmethod
+    def _hip(cls):
+        if cls._lib is None:
+            import ctypes
+            import torch  # noqa: F401  (its HIP runtime is the one resolved)
+            lib = ctypes.CDLL("libamdhip64.so.7")
+            P = ctypes.c_void_p
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P),
+                                                    ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [P, P]
+            lib.hipEventSynchronize.argtypes = [P]
+            lib.hipEventElapsedTime.argtypes = [
+                ctypes.POINTER(ctypes.c_float), P, P]
+            lib.hipEventDestroy.argtypes = [P]
+            cls._lib = lib
+        return cls._lib
+
+    @staticmethod
+    def _ok(rc: int, what: str) -> None:
+        if rc != 0:
+            raise RuntimeError(f"{what} returned {rc}")
+
+    def __init__(self, enable_timing: bool = False):
+        import ctypes
+        self._h = ctypes.c_void_p()
+        flags = 0x20000000 | (0 if enable_timing else 0x2)  # no fence; timing
+        self._ok(self._hip().hipEventCreateWithFlags(ctypes.byref(self._h),
+                                                      flags),
+                 "hipEventCreateWithFlags")
+
+    def record(self) -> None:
+        import ctypes
+        import torch
+        self._ok(self._hip().hipEventRecord(
+            self._h, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)),
+            "hipEventRecord")
+
+    def synchronize(self) -> None:
+        self._ok(self._hip().hipEventSynchronize(self._h),
+                 "hipEventSynchronize")
+
+    def elapsed_time(self, end: "HipEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        self._ok(self._hip().hipEventElapsedTime(ctypes.byref(ms), self._h,
+                                                 end._h),
+                 "hipEventElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        if self._lib is not None and getattr(self, "_h", None):
+            self._lib.hipEventDestroy(self._h)
 
 
 def log(msg: str) -> None:
@@ -376,12 +440,12 @@ class DecodeReplica:
         # The pinned block-id buffer is rewritten only after the append that
         # read it has run: `uploaded` is an event recorded after that append
         # (the decode op's start event in a step).
-        self.uploaded = torch.cuda.Event()
+        self.uploaded = HipEvent()
         self.uploaded.record()
         # the replica's own event for steps without timing events (recorded
         # again each step: the next host_append of this replica has waited
         # on it by then)
-        self.done_ev = torch.cuda.Event()
+        self.done_ev = HipEvent()
         self.scale = 1.0 / float(np.sqrt(w.head_dim))
         self._bind_launches()
         torch.cuda.synchronize()
@@ -561,7 +625,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
         logical_bytes += lb
     # The same steps again (the contexts one token per replica round
     # longer), each decode op bracketed by events: its GPU time.
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+    evs = [tuple(HipEvent(enable_timing=True) for _ in range(2))
            for _ in range(steps)]
     op_bytes = op_logical = 0
     for i in range(steps):
@@ -582,7 +646,7 @@ def run_decode(inp, paged: bool, steps: int, warmup: int, reps: int,
     for i in range(0 if fused else APPEND_TIMING_STEPS):
         r = reps_[i % reps]
         r.host_append()
-        e = tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e = tuple(HipEvent(enable_timing=True) for _ in range(2))
         torch.cuda._sleep(SPIN_CYCLES)
         e[0].record()
         r.cache_write(e[1])
@@ -684,7 +748,7 @@ def run_tiny_decode(device, launches: int = 50):
     scale = 1.0 / float(np.sqrt(w.head_dim))
     times = []
     for i in range(launches + 10):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev = [HipEvent(enable_timing=True) for _ in range(2)]
         torch.cuda._sleep(SPIN_CYCLES)
         ev[0].record()
         kv.paged_attn_decode(out, q, kc, vc, bt, ctx, int(lens.max()), scale)
@@ -721,7 +785,7 @@ def run_swap(w, device, n_blocks: int = 2048, reps: int = 5):
         np.int32)).to(device)
     t_out, t_in = [], []
     for i in range(reps + 1):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e = [HipEvent(enable_timing=True) for _ in range(3)]
         e[0].record()
         kv.kv_swap_blocks(dk, dv, hk, hv, pairs)
         e[1].record()
@@ -798,7 +862,7 @@ def run_cow(w, steps: int, warmup: int, device):
         d_slots = torch.from_numpy(slots).to(device)
         d_table = torch.from_numpy(table).to(device)
         d_lens = torch.from_numpy(lens).to(device)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev = [HipEvent(enable_timing=True) for _ in range(3)]
         # keep the GPU busy while the step is queued, so that the events
         # time the kernels and not the launch latency after the host work
         torch.cuda._sleep(SPIN_CYCLES)
@@ -900,7 +964,7 @@ def prefill_pass(inp, layout: str, device):
             ctx = torch.from_numpy(lens.copy()).to(device)
             d_table = torch.from_numpy(table).to(device)
             q = q_dev[rows_d]
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev = [HipEvent(enable_timing=True) for _ in range(3)]
             torch.cuda._sleep(SPIN_CYCLES)   # GPU busy while this is queued
             ev[0].record()
             kv.kv_reshape_and_cache(k_new, v_new, d_slots, kc, vc)
@@ -1185,13 +1249,13 @@ def plain_read(nbytes: int, device, reps: int = 20,
     for k in per_cu:
         evs = []
         for r in range(warm + reps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            e0 = HipEvent(enable_timing=True)
+            e1 = HipEvent(enable_timing=True)
+            e0.record()
             rc = lib.kvprobe_stream_read(
                 bufs[r % 2].data_ptr(), nb, sink.data_ptr(),
                 sink.numel() * 4, k * cus, stream.cuda_stream)
-            e1.record(stream)
+            e1.record()
             if rc != 0:
                 raise RuntimeError(f"kvprobe_stream_read returned {rc}")
             evs.append((e0, e1))
