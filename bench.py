@@ -165,7 +165,9 @@ class HipEvent:
         return ms.value
 
     def __del__(self):
-        if self._lib is not None and getattr(self, "_h", None):
+        # not while the interpreter shuts down: the HIP runtime may be gone
+        if (self._lib is not None and getattr(self, "_h", None) and
+                not sys.is_finalizing()):
             self._lib.hipEventDestroy(self._h)
 
 
