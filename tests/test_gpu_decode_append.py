@@ -194,6 +194,22 @@ def test_decode_append_workload_shapes(name, S, B):
              int(ctx.max()), ctx)
 
 
+def test_decode_append_many_sequences():
+    # more sequences than one launch takes (4096): the launches share the
+    # workspace, each copying its own block ids into it; short contexts,
+    # the first token of some sequences among them
+    w = W.WORKLOADS["llama3_8b_decode"].replace(
+        num_seqs=4100, num_q_heads=8, num_kv_heads=2, length_range=(1, 48),
+        name="append_many_seqs")
+    inp = W.draw(w, lambda L: H.pool_blocks_for(w, L, w.num_seqs))
+    ctx = W.context_lengths(inp).astype(np.int32)
+    assert (ctx == 1).any()
+    B = w.block_size
+    cap = H.tables_capacity(int(ctx.max()), B)
+    _compare(inp, B, cap, ctx - 1, np.ones(w.num_seqs, dtype=np.int32),
+             int(ctx.max()), ctx)
+
+
 def test_decode_append_many_steps():
     # 40 steps of 16 sequences, every one fused against the two calls on
     # their own copies (new rows drawn per step): caches, tables and lengths

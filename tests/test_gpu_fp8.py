@@ -665,6 +665,18 @@ def test_decode_append_fp8_workload_shape():
     _fused_vs_two_calls(inp, stored, ks, vs, seqs=[0, 17, 40, 63])
 
 
+def test_decode_append_fp8_many_sequences():
+    """More sequences than one launch takes (4096), per-head scales: every
+    launch copies its block ids and the reciprocal scales into the shared
+    workspace."""
+    w = _small_workload(seed=19).replace(
+        num_seqs=4100, lengths=None, length_range=(1, 48), num_q_heads=8,
+        num_kv_heads=2, name="fp8_append_many_seqs")
+    inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens, w.num_seqs))
+    stored = W.context_lengths(inp).astype(np.int32) - 1
+    _fused_vs_two_calls(inp, stored, *_head_scales(9, w.num_kv_heads))
+
+
 @pytest.mark.parametrize("hq,hkv", [(56, 8), (8, 8)])
 def test_decode_append_fp8_head_groups(hq, hkv):
     """Head groups of 7 and of 1 per KV head."""
