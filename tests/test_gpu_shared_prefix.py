@@ -154,6 +154,24 @@ def _random_groups(seed):
     return groups, B, hkv * (4, 7, 16)[seed % 3], hkv
 
 
+def test_many_sequences_two_launches():
+    """4100 sequences in 100 groups of 41, more than one launch of the
+    stream-K and merge kernels takes (4096): the launches share the
+    workspace and find the prefix partials of their own sequences."""
+    g = np.random.default_rng([4000, 99])
+    groups = [(41, 48, [int(x) for x in g.integers(0, 40, size=41)], None)
+              for _ in range(100)]
+    b = build_groups(groups, 16, 8, 2, seed=99)
+    assert len(b["lens"]) == 4100
+    scale = 1.0 / np.sqrt(128)
+    want = expect(b, scale)
+    got = run_shared(b, scale)
+    err = max_abs(got, want)
+    print(f"4100 sequences in 100 groups: max-abs {err:.2e}", flush=True)
+    assert err <= TOL
+    assert max_abs(run_plain(b, scale), want) <= TOL
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_random_groups(seed):
     """Seeded random group layouts: group count and sizes, prefix and own
