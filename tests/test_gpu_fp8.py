@@ -95,15 +95,32 @@ def _oracle_codes(inp, orc, k_scale, v_scale, seqs=None):
                  dtype=np.uint8)
     vp = kp.copy()
     ctx = W.context_lengths(inp)
-    seqs = range(len(ctx)) if seqs is None else seqs
-    for s in seqs:
-        rows = W.logical_rows(inp, s)
-        slots = O.slot_mapping(orc.tables, [s] * len(rows),
-                               list(range(len(rows))), B)
-        O.scatter_rows(kp, F.quantize(inp.k[rows].float().numpy(),
+    seqs = list(range(len(ctx)) if seqs is None else seqs)
+    per_row = w.num_kv_heads * w.head_dim
+
+    def flush(batch):
+        rows = [W.logical_rows(inp, s) for s in batch]
+        sid = [s for s, r in zip(batch, rows) for _ in range(len(r))]
+        if not sid:
+            return
+        pos = [p for r in rows for p in range(len(r))]
+        slots = O.slot_mapping(orc.tables, sid, pos, B)
+        allr = np.concatenate(rows)
+        O.scatter_rows(kp, F.quantize(inp.k[allr].float().numpy(),
                                       _inv(k_scale)), slots)
-        O.scatter_rows(vp, F.quantize(inp.v[rows].float().numpy(),
+        O.scatter_rows(vp, F.quantize(inp.v[allr].float().numpy(),
                                       _inv(v_scale)), slots)
+
+    # sequences batched into oracle calls of about 4M values (the oracle
+    # encodes each distinct product once per call)
+    batch, n = [], 0
+    for s in seqs:
+        batch.append(s)
+        n += int(ctx[s]) * per_row
+        if n >= 4 << 20:
+            flush(batch)
+            batch, n = [], 0
+    flush(batch)
     return kp, vp
 
 
@@ -280,9 +297,10 @@ def test_decode_fp8_long_context_split():
     assert np.array_equal(outs["paged"], outs["contig"])
 
 
-def test_decode_fp8_full_size_sampled():
+def test_decode_fp8_full_size():
     """Llama-3-8B-shaped decode batch (64 sequences, 512..4096 tokens), the
-    launch the benchmark times; oracle on three sampled sequences."""
+    launch the benchmark times: every code of the pool and every output
+    against the oracle (about 35 s of oracle quantisation)."""
     w = W.WORKLOADS["llama3_8b_decode"]
     _log("drawing llama3_8b_decode")
     inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens))
@@ -292,18 +310,36 @@ def test_decode_fp8_full_size_sampled():
     orc = H.build_oracle(inp, w.block_size)
     ks, vs = 0.0123, 0.0123
     kc, vc = _fill_fp8(inp, nat, ks, vs)
-    seqs = [0, int(np.argmax(ctx)), w.num_seqs - 1]
-    kp, vp = _oracle_codes(inp, orc, ks, vs, seqs=seqs)
-    # the sampled sequences' codes are the oracle's, bit for bit
+    kp, vp = _oracle_codes(inp, orc, ks, vs)
+    # every sequence's codes are the oracle's, bit for bit
     kd = kc.permute(0, 2, 1, 3).cpu().numpy()
     vd = vc.permute(0, 2, 1, 3).cpu().numpy()
-    for s in seqs:
+    for s in range(w.num_seqs):
         blocks = orc.tables[s]
         assert np.array_equal(kd[blocks], kp[blocks])
         assert np.array_equal(vd[blocks], vp[blocks])
     outs, want = _decode_fp8_both(inp, nat, orc, kc, vc, kp, vp, ks, vs,
-                                  seqs=seqs, contig=False)
-    _check(outs, want, w.name, seqs=seqs)
+                                  contig=False)
+    _check(outs, want, w.name)
+
+
+def test_decode_fp8_many_sequences():
+    """4100 sequences (two launches), contexts 0..48, per-head scales:
+    paged and contiguous fp8 caches against the oracle."""
+    w = _small_workload(seed=21).replace(
+        num_seqs=4100, lengths=None, length_range=(0, 48), num_q_heads=8,
+        num_kv_heads=2, name="fp8_many_seqs")
+    inp = W.draw(w, lambda lens: H.pool_blocks_for(w, lens, 4))
+    ctx = W.context_lengths(inp)
+    assert (ctx == 0).any()
+    cap = H.tables_capacity(int(max(ctx.max(), 1)), w.block_size)
+    nat = H.build_native(inp, w.block_size, cap)
+    orc = H.build_oracle(inp, w.block_size)
+    ks, vs = _head_scales(10, w.num_kv_heads)
+    kc, vc = _fill_fp8(inp, nat, ks, vs)
+    kp, vp = _oracle_codes(inp, orc, ks, vs)
+    outs, want = _decode_fp8_both(inp, nat, orc, kc, vc, kp, vp, ks, vs)
+    _check(outs, want, w.name)
 
 
 def test_decode_fp8_errors():
