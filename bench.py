@@ -41,9 +41,13 @@ the fp8 decode its fp8 form (kv_append_token_fp8_per_head).
 Four independent replicas of the whole batch (pools, tables, queries) rotate
 so that no step finds its K/V in the 256 MB last-level cache. Each replica's
 two device launches are marshalled once (kv.bind) and re-issued every step,
-so the host keeps ahead of the GPU. The timed steps queue nothing else; a
-second pass of as many steps brackets each decode op with HIP events for its
-GPU time.
+so the host keeps ahead of the GPU. The timed steps queue nothing else
+besides one completion event per step (the replica's pinned buffer is
+refilled only after the step that reads it); a second pass of as many steps
+brackets each decode op with HIP events for its GPU time. Every event is
+created without the system-scope fence (HipEvent), and every timed function
+first waits out the slower reads that follow large memory releases
+(settle).
 
 `value` = decode algorithmic bytes of the headline workload (K+V once per KV
 head, q, o, block-table entries, lengths) summed over the timed steps / wall
