@@ -244,9 +244,11 @@ size_t kv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * merge kernel after the attention and no separate append launch is made.
  * Arguments as in kv_append_token and paged_attn_decode; context_lens
  * holds the lengths before the token and is advanced in place; the
- * workspace is kv_decode_workspace_bytes(). A sequence whose token
- * position lies outside [0, bt_stride * block_size) is not advanced and
- * attends to its stored context only. A position inside the table whose
+ * workspace is kv_decode_workspace_bytes(). new_blocks (device or pinned
+ * host memory) is copied into the workspace by the op's first kernel; the
+ * caller may rewrite it once the op has completed on `stream`. A sequence
+ * whose token position lies outside [0, bt_stride * block_size) is not
+ * advanced and attends to its stored context only. A position inside the table whose
  * block is invalid (new_blocks[s] < 0 and an entry outside
  * [0, num_blocks)) is a caller error: the token is attended to but not
  * stored, and the length is not advanced. Shapes other than bf16,
